@@ -1,0 +1,168 @@
+"""Oracle: float64 attention of absorbed-MLA decode, per stripe, and the LSE merge.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definitions followed (no blocking, fusion or online rescaling is added):
+
+* Absorbed MLA decode is multi-query attention with one shared 576-dim latent
+  row per token: the key is the whole row [c^K (512) || k^R (64)], the value
+  is its first 512 dims, and each query head brings its own 576-dim row
+  [q^C_hat (512) || q^R (64)] (page "MLA 的 Decode Context Parallelism",
+  sections 1 and 2: the two absorption identities).
+* Scores s_p = scale * q . k_p; output o = sum_p exp(s_p) v_p / sum_p exp(s_p)
+  over the visible positions, evaluated with the maximum subtracted;
+  lse = log sum_p exp(s_p) (page "DCP", section "theory", merge identity and
+  numerical stability).
+* A query at global position t sees positions p <= t (causal mask; page "DCP",
+  mergeability table: a mask only shrinks the visible set).  The q_len queries
+  of a request sit at S-q_len, ..., S-1 (SGLang DCP docs, "DCP x speculative
+  decoding": global lengths keep causality over the whole sequence).
+* A stripe's local result is the same definition restricted to the positions
+  the rank owns: o_r is normalised inside the stripe, lse_r its log-sum-exp;
+  an empty visible set gives o_r = 0 and lse_r = -inf, i.e. zero weight
+  (page "DCP", idea two; page "PCP/DCP" section 4.1: an empty shard must act
+  as a zero-weight normalisation state).
+* Merge: m = max_r lse_r, w_r = exp(lse_r - m), o = sum w_r o_r / sum w_r,
+  lse = m + log sum w_r; with base-2 LSE the pair is 2^x / log2 (page "DCP",
+  "merge operator and numerical stability"; SGLang DCP docs, "MLA decode
+  dataflow").
+
+"Base-2 LSE" is read as log2 of the same natural-softmax partition function
+(lse_2 = lse_e * log2(e)); the attention output does not depend on the base.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LN2 = math.log(2.0)
+
+
+def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.ndarray,
+                   scale: float, v_dim: int = 512, chunk: int | None = None):
+    """Softmax attention of R query rows over n latent rows, in float64.
+
+    q      [R, D] query rows (D = 576)
+    q_pos  [R]    global position of each query (it sees kv rows with kv_pos <= q_pos)
+    kv     [n, D] latent rows; the key is the whole row, the value its first v_dim dims
+    kv_pos [n]    global position of each latent row
+    Returns o [R, v_dim] and the natural-log lse [R]; a query that sees no row
+    gets o = 0 and lse = -inf.
+
+    ``chunk`` only splits the two sums over rows into pieces (a first pass
+    finds the exact maximum, a second adds up exp(s - max) and the weighted
+    values); it does not change the formula.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    R = q.shape[0]
+    n = kv.shape[0]
+    if chunk is None or chunk <= 0:
+        chunk = max(n, 1)
+
+    def scores(lo, hi):
+        s = (kv[lo:hi] @ q.T) * scale                       # [rows, R]
+        hidden = kv_pos[lo:hi, None] > q_pos[None, :]
+        s[hidden] = -np.inf
+        return s
+
+    m = np.full(R, -np.inf)
+    for lo in range(0, n, chunk):
+        s = scores(lo, min(n, lo + chunk))
+        if s.size:
+            m = np.maximum(m, s.max(axis=0))
+    seen = np.isfinite(m)
+    m_safe = np.where(seen, m, 0.0)
+    Z = np.zeros(R)
+    acc = np.zeros((R, v_dim))
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        s = scores(lo, hi)
+        e = np.exp(s - m_safe[None, :])                      # exp(-inf) = 0 for hidden rows
+        Z += e.sum(axis=0)
+        acc += e.T @ kv[lo:hi, :v_dim]
+    o = np.zeros((R, v_dim))
+    o[seen] = acc[seen] / Z[seen, None]
+    lse = np.full(R, -np.inf)
+    lse[seen] = m[seen] + np.log(Z[seen])
+    return o, lse
+
+
+def query_positions(S: int, q_len: int) -> np.ndarray:
+    """Global positions of the q_len queries of a request with S cached tokens."""
+    return np.arange(S - q_len, S, dtype=np.int64)
+
+
+def full_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, scale: float,
+                   v_dim: int = 512, chunk: int | None = None):
+    """Unsharded attention of one request.
+
+    q_req [q_len, H, D], kv_req [S, D] (logical order, position p at row p).
+    Returns o [q_len, H, v_dim] and natural-log lse [q_len, H].
+    """
+    q_len, H, D = q_req.shape
+    qp = np.repeat(query_positions(S, q_len), H)
+    o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[:S],
+                            np.arange(S, dtype=np.int64), scale, v_dim, chunk)
+    return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
+
+
+def stripe_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, positions: np.ndarray,
+                     scale: float, v_dim: int = 512, chunk: int | None = None):
+    """Local attention of one request on one stripe.
+
+    ``positions`` are the global positions the rank owns (as handed out by
+    ``oracle.layout.stripe_positions``); only those rows of ``kv_req`` enter.
+    Returns the locally normalised o_r [q_len, H, v_dim] and lse_r [q_len, H]
+    (natural log; -inf where the stripe holds no visible row).
+    """
+    q_len, H, D = q_req.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    positions = positions[positions < S]
+    qp = np.repeat(query_positions(S, q_len), H)
+    o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[positions],
+                            positions, scale, v_dim, chunk)
+    return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
+
+
+def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray, base: str = "e"):
+    """Exact merge of per-stripe results.
+
+    o_parts [N, ..., V], lse_parts [N, ...] with lse in ``base`` ("e" or "2").
+    Stripes with lse = -inf carry zero weight.  If every stripe is empty the
+    result is o = 0 and lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    if base == "e":
+        power = np.exp
+        log = np.log
+    elif base == "2":
+        power = np.exp2
+        log = np.log2
+    else:
+        raise ValueError("base must be 'e' or '2'")
+    finite = np.isfinite(lse_parts)
+    m = np.where(finite, lse_parts, -np.inf).max(axis=0)
+    any_seen = np.isfinite(m)
+    m_safe = np.where(any_seen, m, 0.0)
+    w = np.where(finite, power(np.where(finite, lse_parts, 0.0) - m_safe[None]), 0.0)
+    wsum = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0)
+    o = np.where(any_seen[..., None], o / np.where(any_seen, wsum, 1.0)[..., None], 0.0)
+    lse = np.where(any_seen, m_safe + log(np.where(any_seen, wsum, 1.0)), -np.inf)
+    return o, lse
+
+
+def to_base(lse_e: np.ndarray, base: str) -> np.ndarray:
+    """Natural-log LSE expressed in ``base`` ("e" or "2")."""
+    lse_e = np.asarray(lse_e, dtype=np.float64)
+    if base == "e":
+        return lse_e
+    if base == "2":
+        return lse_e / LN2
+    raise ValueError("base must be 'e' or '2'")

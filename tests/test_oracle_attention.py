@@ -1,0 +1,284 @@
+"""Pins for the oracle's attention, stripe attention and LSE merge (CPU only).
+
+Each check pins the float64 oracle to something other than itself: a
+pure-Python brute force on tiny inputs, torch's scaled_dot_product_attention
+and logsumexp on the same special case (a different library routine), closed
+forms (q = 0, one dominant key), the pages' two-token counterexample, and the
+merge identity / monoid laws the pages derive.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import layout as L
+
+SCALE = 1.0 / math.sqrt(192.0)
+D = 576
+V = 512
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(rng, S, H, q_len, kv_std=0.5):
+    q = rng.standard_normal((q_len, H, D))
+    kv = rng.standard_normal((S, D)) * kv_std
+    return q, kv
+
+
+# ---- brute force ------------------------------------------------------------
+
+def brute_attention(q_row, kv, kv_pos, q_pos, scale):
+    """Definition evaluated term by term with math.fsum."""
+    vis = [i for i in range(len(kv)) if kv_pos[i] <= q_pos]
+    if not vis:
+        return [0.0] * V, -math.inf
+    s = [scale * math.fsum(float(q_row[d]) * float(kv[i][d]) for d in range(D)) for i in vis]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    Z = math.fsum(e)
+    o = [math.fsum(e[j] * float(kv[vis[j]][c]) for j in range(len(vis))) / Z for c in range(V)]
+    return o, m + math.log(Z)
+
+
+@pytest.mark.parametrize("S,q_len", [(1, 1), (5, 1), (16, 1), (9, 3), (4, 4)])
+def test_full_attention_against_brute_force(S, q_len):
+    rng = np.random.default_rng(S * 10 + q_len)
+    H = 2
+    q, kv = rand_case(rng, S, H, q_len, kv_std=1.0)
+    o, lse = A.full_attention(q, kv, S, SCALE)
+    for t in range(q_len):
+        for h in range(H):
+            bo, bl = brute_attention(q[t, h], kv, list(range(S)), S - q_len + t, SCALE)
+            assert np.allclose(o[t, h], bo, rtol=1e-12, atol=1e-13)
+            assert abs(lse[t, h] - bl) <= 1e-12 * max(1.0, abs(bl))
+
+
+@pytest.mark.parametrize("N,I", [(1, 1), (2, 1), (3, 1), (4, 1), (8, 1), (2, 2), (3, 4), (4, 2)])
+def test_stripe_attention_against_brute_force(N, I):
+    rng = np.random.default_rng(100 + N * 7 + I)
+    S, H, q_len = 13, 2, 2
+    q, kv = rand_case(rng, S, H, q_len, kv_std=1.0)
+    lists = L.stripe_positions(S, N, I)
+    for r in range(N):
+        o, lse = A.stripe_attention(q, kv, S, lists[r], SCALE)
+        for t in range(q_len):
+            for h in range(H):
+                pos = lists[r].tolist()
+                bo, bl = brute_attention(q[t, h], [kv[p] for p in pos], pos, S - q_len + t, SCALE)
+                assert np.allclose(o[t, h], bo, rtol=1e-12, atol=1e-13)
+                if math.isinf(bl):
+                    assert lse[t, h] == -math.inf
+                else:
+                    assert abs(lse[t, h] - bl) <= 1e-12 * max(1.0, abs(bl))
+
+
+# ---- library routine on a special case -----------------------------------------
+
+@pytest.mark.parametrize("S,H,q_len", [(37, 4, 1), (200, 16, 1), (64, 3, 4), (5, 8, 4)])
+def test_against_torch_sdpa_fp64(S, H, q_len):
+    rng = np.random.default_rng(S + H + q_len)
+    q, kv = rand_case(rng, S, H, q_len)
+    o, lse = A.full_attention(q, kv, S, SCALE)
+    qt = torch.from_numpy(q.reshape(q_len * H, D)).view(1, 1, q_len * H, D)
+    kt = torch.from_numpy(kv).view(1, 1, S, D)
+    vt = torch.from_numpy(np.ascontiguousarray(kv[:, :V])).view(1, 1, S, V)
+    qpos = torch.arange(S - q_len, S).repeat_interleave(H)
+    mask = torch.arange(S)[None, :] <= qpos[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask.view(1, 1, -1, S), scale=SCALE)
+    scores = (qt[0, 0] @ kt[0, 0].T) * SCALE
+    ref_lse = torch.logsumexp(scores.masked_fill(~mask, -math.inf), dim=-1)
+    assert np.allclose(o.reshape(q_len * H, V), ref[0, 0].numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse.reshape(-1), ref_lse.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---- closed forms -----------------------------------------------------------------
+
+@pytest.mark.parametrize("N,I,q_len", [(1, 1, 1), (8, 1, 1), (8, 64, 4), (4, 1, 4), (3, 2, 2)])
+def test_zero_query_gives_mean_and_log_count(N, I, q_len):
+    rng = np.random.default_rng(3)
+    S, H = 300, 2
+    _, kv = rand_case(rng, S, H, q_len)
+    q = np.zeros((q_len, H, D))
+    o, lse = A.full_attention(q, kv, S, SCALE)
+    for t in range(q_len):
+        vis = S - q_len + t + 1
+        assert np.allclose(o[t], kv[:vis, :V].mean(axis=0)[None], rtol=1e-12, atol=1e-14)
+        assert np.allclose(lse[t], math.log(vis), rtol=1e-14)
+    lists = L.stripe_positions(S, N, I)
+    for r in range(N):
+        o_r, lse_r = A.stripe_attention(q, kv, S, lists[r], SCALE)
+        for t in range(q_len):
+            mine = lists[r][lists[r] <= S - q_len + t]
+            if len(mine) == 0:
+                assert (o_r[t] == 0).all() and (lse_r[t] == -np.inf).all()
+            else:
+                assert np.allclose(o_r[t], kv[mine, :V].mean(axis=0)[None], rtol=1e-12, atol=1e-14)
+                assert np.allclose(lse_r[t], math.log(len(mine)), rtol=1e-14)
+
+
+def test_one_dominant_key_returns_its_value():
+    rng = np.random.default_rng(4)
+    S, H = 50, 3
+    _, kv = rand_case(rng, S, H, 1)
+    q = np.zeros((1, H, D))
+    for h, target in enumerate([0, 17, 49]):
+        q[0, h] = kv[target] * 400.0          # score of the target dominates by a wide margin
+    o, _ = A.full_attention(q, kv, S, SCALE)
+    for h, target in enumerate([0, 17, 49]):
+        assert np.allclose(o[0, h], kv[target, :V], atol=1e-9)
+        # the rope dims take part in the score but never in the value
+        assert o.shape[-1] == V
+
+
+def test_rope_dims_enter_the_score():
+    """Keys that differ only in the last 64 dims get different weights."""
+    S = 2
+    kv = np.zeros((S, D))
+    kv[0, 0] = 1.0
+    kv[1, 1] = 1.0
+    kv[1, 512:] = 0.5
+    q = np.zeros((1, 1, D))
+    q[0, 0, 512:] = 1.0
+    o, lse = A.full_attention(q, kv, S, SCALE)
+    s1 = SCALE * 64 * 0.5
+    w1 = math.exp(s1) / (1 + math.exp(s1))
+    assert abs(o[0, 0, 1] - w1) < 1e-14 and abs(o[0, 0, 0] - (1 - w1)) < 1e-14
+    assert abs(lse[0, 0] - math.log(1 + math.exp(s1))) < 1e-14
+
+
+# ---- the pages' counterexample ------------------------------------------------------
+
+def test_two_token_counterexample():
+    g = json.load(open(os.path.join(GOLDEN, "two_token_counterexample.json")))
+    v0, v1 = g["values"][1], g["values"][0]      # token 0 carries 0, token 1 carries 1
+    for gap in (-4.0, 0.0, 4.0):
+        kv = np.zeros((2, D))
+        kv[0, 0] = v0
+        kv[1, 0] = v1
+        # scores: s0 = 0, s1 = gap (via a rope dim that only token 1 has)
+        kv[1, 575] = 1.0
+        q = np.zeros((1, 1, D))
+        q[0, 0, 575] = gap / SCALE
+        lists = L.stripe_positions(2, 2, 1)
+        parts = [A.stripe_attention(q, kv, 2, lists[r], SCALE) for r in range(2)]
+        local = [parts[r][0][0, 0, 0] for r in range(2)]
+        assert local == g["local_outputs"][::-1]           # shard 0 holds the 0, shard 1 the 1
+        naive = 0.5 * (parts[0][0] + parts[1][0])
+        assert naive[0, 0, 0] == g["naive_mean_of_local_outputs"]
+        true = 1.0 / (1.0 + math.exp(-gap))
+        o, _ = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        assert abs(o[0, 0, 0] - true) < 1e-14
+        full, _ = A.full_attention(q, kv, 2, SCALE)
+        assert abs(full[0, 0, 0] - true) < 1e-14
+
+
+# ---- merge identity and monoid laws ------------------------------------------------
+
+CASES = [
+    # (S, H, q_len, N, I): small analogues of the five workloads plus fuzz shapes
+    (1024, 16, 1, 4, 1),
+    (512, 8, 1, 8, 1),
+    (700, 6, 1, 8, 1),
+    (3, 4, 1, 8, 1),
+    (7, 4, 1, 8, 1),
+    (1000, 4, 4, 8, 1),
+    (1000, 4, 4, 8, 64),
+    (130, 3, 2, 3, 2),
+    (200, 1, 1, 2, 1),
+]
+
+
+@pytest.mark.parametrize("S,H,q_len,N,I", CASES)
+@pytest.mark.parametrize("base", ["e", "2"])
+def test_merged_stripes_equal_full_attention(S, H, q_len, N, I, base):
+    rng = np.random.default_rng(S * 31 + N)
+    q, kv = rand_case(rng, S, H, q_len)
+    o_full, lse_full = A.full_attention(q, kv, S, SCALE)
+    lists = L.stripe_positions(S, N, I)
+    parts = [A.stripe_attention(q, kv, S, lists[r], SCALE) for r in range(N)]
+    o_parts = np.stack([p[0] for p in parts])
+    lse_parts = np.stack([A.to_base(p[1], base) for p in parts])
+    o, lse = A.lse_merge(o_parts, lse_parts, base)
+    assert np.allclose(o, o_full, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, A.to_base(lse_full, base), rtol=1e-12, atol=1e-13)
+
+
+def test_one_stripe_is_the_identity():
+    rng = np.random.default_rng(9)
+    S, H, q_len = 77, 5, 3
+    q, kv = rand_case(rng, S, H, q_len)
+    o_full, lse_full = A.full_attention(q, kv, S, SCALE)
+    o1, lse1 = A.stripe_attention(q, kv, S, L.stripe_positions(S, 1, 1)[0], SCALE)
+    assert (o1 == o_full).all() and (lse1 == lse_full).all()
+    o, lse = A.lse_merge(o1[None], lse1[None])
+    assert np.allclose(o, o1, rtol=1e-15, atol=0) and np.allclose(lse, lse1, rtol=1e-15, atol=0)
+
+
+def _merge_tree(rng, o_parts, lse_parts, base):
+    items = [(o_parts[i], lse_parts[i]) for i in range(len(o_parts))]
+    while len(items) > 1:
+        i, j = sorted(rng.choice(len(items), size=2, replace=False))
+        a, b = items[i], items[j]
+        m = A.lse_merge(np.stack([a[0], b[0]]), np.stack([a[1], b[1]]), base)
+        items = [it for k, it in enumerate(items) if k not in (i, j)] + [m]
+    return items[0]
+
+
+@pytest.mark.parametrize("base", ["e", "2"])
+def test_merge_is_order_and_tree_independent(base):
+    rng = np.random.default_rng(11)
+    N, R = 8, 20
+    o_parts = rng.standard_normal((N, R, 16))
+    lse_parts = rng.standard_normal((N, R)) * 30
+    lse_parts[2, :5] = -np.inf                            # some empty stripes
+    ref_o, ref_l = A.lse_merge(o_parts, lse_parts, base)
+    for perm in itertools.islice(itertools.permutations(range(N)), 0, 40000, 997):
+        o, l = A.lse_merge(o_parts[list(perm)], lse_parts[list(perm)], base)
+        assert np.allclose(o, ref_o, rtol=1e-12, atol=1e-13) and np.allclose(l, ref_l, rtol=1e-13)
+    for _ in range(20):
+        o, l = _merge_tree(rng, o_parts, lse_parts, base)
+        assert np.allclose(o, ref_o, rtol=1e-12, atol=1e-13) and np.allclose(l, ref_l, rtol=1e-13)
+
+
+def test_merge_base_pairing():
+    rng = np.random.default_rng(12)
+    o_parts = rng.standard_normal((5, 7, 8))
+    lse_e = rng.standard_normal((5, 7)) * 10
+    oe, le = A.lse_merge(o_parts, lse_e, "e")
+    o2, l2 = A.lse_merge(o_parts, lse_e / math.log(2), "2")
+    assert np.allclose(oe, o2, rtol=1e-13) and np.allclose(le, l2 * math.log(2), rtol=1e-13)
+    # mixing the bases (2^x weights on natural-log lse) gives wrong weights
+    o_bad, _ = A.lse_merge(o_parts, lse_e, "2")
+    assert not np.allclose(o_bad, oe, rtol=1e-3)
+
+
+def test_merge_empty_stripes_carry_zero_weight():
+    o_parts = np.array([[[1.0, 2.0]], [[np.nan, np.nan]] , [[5.0, 7.0]]])
+    o_parts[1] = 123.0                                    # junk in an empty stripe
+    lse_parts = np.array([[0.5], [-np.inf], [0.5]])
+    o, lse = A.lse_merge(o_parts, lse_parts)
+    assert np.allclose(o, [[3.0, 4.5]]) and np.allclose(lse, [0.5 + math.log(2)])
+    o, lse = A.lse_merge(o_parts[1:2], lse_parts[1:2])
+    assert (o == 0).all() and (lse == -np.inf).all()
+
+
+def test_large_lse_does_not_overflow():
+    o_parts = np.array([[[1.0]], [[3.0]]])
+    lse_parts = np.array([[1000.0], [1000.0 + math.log(3)]])
+    o, lse = A.lse_merge(o_parts, lse_parts)
+    assert np.allclose(o, [[2.5]]) and np.allclose(lse, [1000.0 + math.log(4)])
+
+
+def test_chunked_evaluation_is_the_same_sum():
+    rng = np.random.default_rng(13)
+    S, H, q_len = 1000, 4, 4
+    q, kv = rand_case(rng, S, H, q_len)
+    o1, l1 = A.full_attention(q, kv, S, SCALE)
+    o2, l2 = A.full_attention(q, kv, S, SCALE, chunk=97)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(l1, l2, rtol=1e-14)

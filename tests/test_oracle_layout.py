@@ -1,0 +1,233 @@
+"""Pins for the oracle's token striping, counts and slot mapping (CPU only).
+
+The oracle produces the striping by simulating the round-robin hand-out.  Here
+it is checked against (a) the values the pages print for their worked
+examples (tests/golden), (b) the closed forms the pages give, written out
+below from the pages, and (c) invariants the pages state.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---- closed forms from the pages (used only as pins) -----------------------
+
+def token_rr(p, N):
+    """Page "DCP", core abstraction, idea one: owner = p mod N, row = p div N."""
+    return p % N, p // N
+
+
+def block_rr(p, N, I):
+    """Page "PCP/DCP", section 6: owner = (t div B) mod P,
+    local index = (t div (B*P))*B + t mod B (P = DCP size, B = block size)."""
+    return (p // I) % N, (p // (I * N)) * I + p % I
+
+
+def block_rr_local_len(n, r, N, I):
+    """Page "PCP/DCP", section 6: local_len(n, r)."""
+    return (n // (N * I)) * I + np.clip(n % (N * I) - r * I, 0, I)
+
+
+def virtual_block(x, N, I, block_size):
+    """vLLM-Ascend CP design, section "block table": virtual block of
+    block_size*cp_size tokens, local block index, target rank and the offset
+    inside the rank's block; the local row is taken as
+    (virtual block index) * block_size + that offset."""
+    vbs = block_size * N
+    vb = x // vbs
+    off = x % vbs
+    lbi = off // I
+    rank = lbi % N
+    inner = (lbi // N) * I + off % I
+    return rank, vb * block_size + inner
+
+
+# ---- printed worked examples ------------------------------------------------
+
+def test_token_rr_worked_example():
+    g = golden("token_rr_dcp8.json")
+    lists = L.stripe_positions(64, g["N"], g["interleave"])
+    for r, prefix in g["rank_prefixes"].items():
+        assert lists[int(r)][: len(prefix)].tolist() == prefix
+
+
+def test_block_rr_worked_example():
+    g = golden("block_rr_dcp4_b4.json")
+    N, I = g["N"], g["interleave"]
+    owner, _ = L.owner_and_row_table(24, N, I)
+    for lo, hi, r in g["runs"]:
+        assert (owner[lo:hi + 1] == r).all()
+    for x, counts in g["counts_after"].items():
+        assert L.local_counts(int(x), N, I).tolist() == counts
+
+
+def test_page_expansion_worked_example():
+    g = golden("page_expansion.json")
+    P = g["page_size"]
+    rows = np.arange(P * len(g["pages"]))
+    slots = L.page_slot(np.array(g["pages"]), rows, P)
+    want = np.concatenate([np.arange(lo, hi + 1) for lo, hi in g["slot_ranges"]])
+    assert slots.tolist() == want.tolist()
+
+
+def test_rank1_extraction_worked_example():
+    g = golden("rank1_extraction.json")
+    N, r, n, P = g["N"], g["rank"], g["length"], g["page_size"]
+    pos = L.stripe_positions(n, N, 1)[r]
+    assert pos[: len(g["positions_head"])].tolist() == g["positions_head"]
+    assert pos[-1] == g["positions_last"]
+    assert len(pos) == g["tokens_received"]
+    # The prefill side is unsharded (DCP1): request position t sits at row t.
+    src = L.page_slot(np.array(g["source_pages"]), pos, P)
+    assert src.tolist() == g["source_slots"]
+    for bad in g["not_in_source_slots"]:
+        assert bad not in src.tolist()
+    # The decode side stores the received rows compactly in page 10.
+    _, row, dst = L.slot_map(pos, np.zeros_like(pos), N, 1, P, r, np.array([[g["dest_page"]]]))
+    assert row.tolist() == list(range(len(pos)))
+    lo, hi = g["dest_slot_range"]
+    assert dst.tolist() == list(range(lo, hi + 1))
+
+
+# ---- closed forms -----------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("I", [1, 2, 4, 16, 64])
+def test_simulation_equals_closed_forms(N, I):
+    S = 5000
+    owner, row = L.owner_and_row_table(S, N, I)
+    p = np.arange(S)
+    o3, r3 = block_rr(p, N, I)
+    assert (owner == o3).all() and (row == r3).all()
+    if I == 1:
+        o1, r1 = token_rr(p, N)
+        assert (owner == o1).all() and (row == r1).all()
+    for block_size in (I, 2 * I, 64 if 64 % I == 0 else I):
+        o4, r4 = virtual_block(p, N, I, block_size)
+        assert (owner == o4).all() and (row == r4).all()
+
+
+@pytest.mark.parametrize("N,I", [(1, 1), (3, 1), (8, 1), (4, 4), (8, 64), (3, 16)])
+def test_local_counts_equal_local_len(N, I):
+    for x in list(range(0, 300)) + [1000, 1333, 4097, 65535]:
+        got = L.local_counts(x, N, I)
+        want = np.array([block_rr_local_len(x, r, N, I) for r in range(N)])
+        assert (got == want).all(), (x, got, want)
+
+
+def test_owner_row_walk_matches_simulation_and_large_positions():
+    for N, I in [(1, 1), (8, 1), (8, 64), (3, 4)]:
+        owner, row = L.owner_and_row_table(4096, N, I)
+        for p in range(0, 4096, 7):
+            assert L.owner_row_walk(p, N, I) == (owner[p], row[p])
+    rng = np.random.default_rng(5)
+    for p in rng.integers(0, 1 << 40, size=200):
+        for N, I in [(8, 1), (8, 64), (5, 2)]:
+            assert L.owner_row_walk(int(p), N, I) == tuple(int(v) for v in block_rr(int(p), N, I))
+
+
+# ---- invariants the pages state ---------------------------------------------
+
+@pytest.mark.parametrize("N,I", [(1, 1), (2, 1), (8, 1), (4, 4), (8, 64), (3, 2)])
+def test_count_invariants(N, I):
+    for x in range(0, 700, 3):
+        c = L.local_counts(x, N, I)
+        assert c.sum() == x
+        # token RR: counts differ by at most one; block RR: by at most one block
+        assert c.max() - c.min() <= (1 if I == 1 else I)
+    for a, n in [(0, 0), (0, 17), (1000, 333), (5, 1), (513, 64)]:
+        assert L.interval_counts(a, n, N, I).sum() == n
+
+
+@pytest.mark.parametrize("N,I", [(1, 1), (8, 1), (8, 64), (3, 2)])
+def test_owner_row_is_a_bijection_with_compact_rows(N, I):
+    S = 2000
+    owner, row = L.owner_and_row_table(S, N, I)
+    seen = set()
+    for p in range(S):
+        key = (int(owner[p]), int(row[p]))
+        assert key not in seen
+        seen.add(key)
+    counts = L.local_counts(S, N, I)
+    for r in range(N):
+        assert sorted(row[owner == r].tolist()) == list(range(counts[r]))
+        # rows of one rank follow position order
+        assert (np.diff(row[owner == r]) == 1).all()
+
+
+def test_chunk_interval_counts():
+    """count(a+L) - count(a) with global positions, a=1000, L=333, N=8: the
+    counts come from the block-RR local_len of page "PCP/DCP" section 6."""
+    for I, want in [(1, [42, 42, 42, 42, 42, 41, 41, 41]), (64, [64, 64, 64, 64, 53, 0, 0, 24])]:
+        closed = [block_rr_local_len(1333, r, 8, I) - block_rr_local_len(1000, r, 8, I) for r in range(8)]
+        assert closed == want
+        assert L.interval_counts(1000, 333, 8, I).tolist() == want
+
+
+# ---- slot map and KV write ------------------------------------------------------
+
+def test_slot_map_against_closed_forms():
+    rng = np.random.default_rng(1)
+    for N, I, P in [(4, 1, 16), (8, 1, 64), (8, 64, 64), (3, 2, 4)]:
+        B = 3
+        cols = 40
+        tables = rng.permutation(B * cols).reshape(B, cols).astype(np.int32)
+        pos = rng.integers(0, 1500, size=400)
+        req = rng.integers(0, B, size=400)
+        for rank in [-1] + list(range(N)):
+            owner, row, slot = L.slot_map(pos, req, N, I, P, rank, tables)
+            for i in range(len(pos)):
+                o, rr = block_rr(int(pos[i]), N, I)
+                assert owner[i] == o and row[i] == rr
+                if rank >= 0 and o == rank and rr // P < cols:
+                    assert slot[i] == tables[req[i], rr // P] * P + rr % P
+                else:
+                    assert slot[i] == -1
+
+
+def test_slot_map_missing_page_gives_minus_one():
+    table = np.array([[7, -1]], dtype=np.int32)
+    _, row, slot = L.slot_map(np.array([0, 8, 16, 24, 10**6 * 8]), np.zeros(5, dtype=np.int64), 8, 1, 2, 0, table)
+    assert row.tolist() == [0, 1, 2, 3, 10**6]
+    assert slot.tolist() == [14, 15, -1, -1, -1]
+
+
+def test_kv_write_owner_filtered_and_chunked_equals_one_shot():
+    N, I, P = 8, 1, 4
+    S = 1500
+    rows = np.arange(S * 3, dtype=np.int64).reshape(S, 3)        # row p holds (3p, 3p+1, 3p+2)
+    counts = L.local_counts(S, N, I)
+    pages = -(-counts // P)
+    cols = int(pages.max())
+    for rank in range(N):
+        table = np.random.default_rng(rank).permutation(cols + 5)[:cols].reshape(1, cols).astype(np.int32)
+        pool = np.full(((cols + 5) * P, 3), -7, dtype=np.int64)
+        pos = np.arange(S)
+        req = np.zeros(S, dtype=np.int64)
+        one = L.kv_write(pool, rows, pos, req, N, I, P, rank, table)
+        chunked = pool
+        for lo, hi in [(0, 1000), (1000, 1333), (1333, S)]:
+            chunked = L.kv_write(chunked, rows[lo:hi], pos[lo:hi], req[lo:hi], N, I, P, rank, table)
+        assert (one == chunked).all()
+        # every owned position is at its slot, nothing else was touched
+        written = (one != -7).all(axis=1)
+        assert written.sum() == counts[rank]
+        mine = np.arange(S)[np.arange(S) % N == rank]
+        for j, p in enumerate(mine):
+            slot = table[0, j // P] * P + j % P
+            assert (one[slot] == rows[p]).all()
+        # the middle chunk wrote exactly its interval share
+        mid = L.kv_write(pool, rows[1000:1333], pos[1000:1333], req[1000:1333], N, I, P, rank, table)
+        assert (mid != -7).all(axis=1).sum() == L.interval_counts(1000, 333, N, I)[rank]
