@@ -1,0 +1,198 @@
+/*
+ * dcp.h -- C ABI of the MI355X (gfx950) decode-context-parallel (DCP) MLA
+ * attention library, libdcp.so.
+ *
+ * DCP stripes the shared latent KV of absorbed MLA over N ranks by token
+ * position: rank r stores the positions it owns compactly, each rank attends
+ * all H query heads to its own stripe and returns a locally normalised output
+ * with its log-sum-exp, and an exact LSE merge recombines the stripes
+ * (page "DCP" (zdszero), "core abstraction" and "theory"; SGLang DCP docs,
+ * "MLA decode dataflow").  On one GPU the N stripes are N separate pools and
+ * every rank's kernel runs at its real per-rank shape.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named as device pointers must point to device memory (or
+ *    memory the device can read/write); the caller owns all buffers.  The
+ *    library never allocates or frees memory and keeps no state between calls.
+ *  - bfloat16 data is passed as raw 16-bit storage (void*).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on `stream` and returns; nothing is synchronised.
+ *  - Return value: DCP_OK, or a negative error code.  On any error return
+ *    nothing has been enqueued.  Argument errors (DCP_EINVAL,
+ *    DCP_EUNSUPPORTED) are detected on the host before any HIP call.
+ *  - Errors that depend on device data (a page id outside the pool, a page
+ *    table with no entry for a needed row, a negative position) cannot be seen
+ *    on the host: the kernels then skip the offending row, never touch memory
+ *    outside the buffers, and store DCP_ERANGE into *status when `status` is
+ *    not NULL.  Kernels only ever store DCP_ERANGE there; the caller clears
+ *    *status to DCP_OK beforehand.
+ */
+#ifndef DCP_H
+#define DCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCP_OK 0
+#define DCP_EINVAL (-1)        /* invalid argument (NULL, negative size, bad layout) */
+#define DCP_EUNSUPPORTED (-2)  /* shape outside what the kernels are built for */
+#define DCP_EHIP (-3)          /* a HIP call or kernel launch failed */
+#define DCP_ERANGE (-4)        /* device data out of range (stored into *status) */
+
+/* Token-to-rank layout.
+ * n_stripes  N >= 1: DCP size (number of stripes / ranks).
+ * interleave I >= 1: tokens are handed out in consecutive runs of I, one run
+ *            per rank in turn (I = 1: token round robin, owner = p mod N;
+ *            page "PCP/DCP" (obnotes) sections 5 and 6; vLLM-Ascend CP design,
+ *            "block table", cp_kv_cache_interleave_size).
+ * page_size  P >= 1, with P % I == 0 (the vLLM-Ascend design requires the
+ *            block size to be a multiple of the interleave).
+ * For a global position p:
+ *   owner(p) = floor(p / I) mod N
+ *   row(p)   = floor(p / (I*N)) * I + p mod I          (compact local row)
+ *   count_r(x) = #{ p in [0, x) : owner(p) = r }
+ * and a local row j of rank r holds global position
+ *   p = floor(j / I) * I * N + r * I + j mod I. */
+typedef struct dcp_layout {
+  int32_t n_stripes;
+  int32_t interleave;
+  int32_t page_size;
+} dcp_layout;
+
+/* Human-readable name of a return code (static storage, never NULL). */
+const char* dcp_strerror(int code);
+
+/* Library ABI version (incremented when a signature changes). */
+int dcp_abi_version(void);
+
+/* dcp_slot_map -- owner, local row and physical slot of n positions.
+ * Page "DCP": ownership is a pure function of the position; page "PCP/DCP",
+ * "KV cache management": slot = page_id * page_size + offset in page, the page
+ * id coming from the request's page table.
+ *
+ * pos   [n] int64  device, global positions (>= 0).
+ * req   [n] int32  device, request index of each position, or NULL (all 0).
+ * block_table [bt_rows][bt_cols] int32 device, rank `rank`'s page table:
+ *       entry [b][k] is the page of this rank's pool holding local rows
+ *       k*P .. k*P+P-1 of request b; -1 = none.  May be NULL (no slots).
+ * owner [n] int32 out, row [n] int64 out, slot [n] int64 out: each may be NULL.
+ *       slot[i] = -1 when rank < 0, block_table is NULL, or owner != rank.
+ *       An owned position whose request or page-table column is out of range,
+ *       or whose entry is negative, also gets -1 and raises DCP_ERANGE.
+ *       A negative position gets owner = -1, row = -1, slot = -1, DCP_ERANGE.
+ * status  device int32, nullable (see conventions). */
+int dcp_slot_map(dcp_layout layout, int32_t rank,
+                 const int64_t* pos, const int32_t* req, int64_t n,
+                 const int32_t* block_table, int32_t bt_rows, int32_t bt_cols,
+                 int32_t* owner, int64_t* row, int64_t* slot,
+                 int32_t* status, void* stream);
+
+/* dcp_local_count -- every rank's share of n intervals [start, start+len).
+ * Page "DCP", idea one, and page "PCP/DCP" section 6: the share of rank r is
+ * count_r(start + len) - count_r(start) with global positions; start = 0
+ * gives the local length of a request of `len` tokens.
+ * start [n] int64 device (NULL = all 0), len [n] int64 device (>= 0),
+ * count [n][N] int64 device out.  Negative start/len: counts 0, DCP_ERANGE
+ * is not reported (no status); the caller validates lengths. */
+int dcp_local_count(dcp_layout layout, const int64_t* start, const int64_t* len,
+                    int64_t n, int64_t* count, void* stream);
+
+/* dcp_kv_write -- owner-filtered paged write of new latent rows.
+ * Page "MLA 的 Decode Context Parallelism", section 4, stage 2: each new
+ * 576-dim latent row is stored only on the rank that owns its position, at
+ * its compact slot; rows of other ranks are skipped (not read).
+ * kv_new [T][row_dim] bf16 device; row_dim % 8 == 0.
+ * pos [T] int64, req [T] int32 (NULL = all 0) device.
+ * block_table as in dcp_slot_map (required).
+ * pool [num_pages][P][row_dim] bf16 device, this rank's pool.
+ * A row whose page id is outside [0, num_pages) or whose table entry is
+ * missing is skipped and raises DCP_ERANGE. */
+int dcp_kv_write(dcp_layout layout, int32_t rank,
+                 const void* kv_new, int32_t row_dim, int64_t T,
+                 const int64_t* pos, const int32_t* req,
+                 const int32_t* block_table, int32_t bt_rows, int32_t bt_cols,
+                 void* pool, int64_t num_pages,
+                 int32_t* status, void* stream);
+
+/* Arguments of one rank's stripe attention (absorbed MLA decode).
+ * Query row i of request b, query t, head h: q[b][t][h][0..575] =
+ * [absorbed nope part (512) || rope part (64)] (page "MLA 的 DCP", section 2).
+ * The key of a cached token is its whole 576-dim latent row, the value its
+ * first v_dim = 512 dims.  The q_len queries of request b sit at global
+ * positions seq_len[b] - q_len + t and see the cached positions p <= their
+ * own (causal among drafts; SGLang DCP docs, "DCP x speculative decoding":
+ * the kernel gets the global lengths and its rank).
+ *
+ * layout, rank  rank r's stripe under `layout` (0 <= rank < N).
+ * batch, q_len, n_heads  B >= 1, q_len >= 1, H >= 1.
+ * head_dim, v_dim        must be 576 and 512 (else DCP_EUNSUPPORTED).
+ * q           [B][q_len][H][head_dim] bf16 device.
+ * pool        [num_pages][P][head_dim] bf16 device, this rank's pool.
+ * block_table [B][bt_cols] int32 device, this rank's page table.
+ * seq_len     [B] int32 device, GLOBAL context lengths (>= q_len).
+ * scale       softmax scale applied to q.k (e.g. 1/sqrt(192)).
+ * lse_base    0: lse in natural log; 1: lse in log2 (same partition function,
+ *             lse2 = lse * log2(e)); the output o does not depend on it.
+ * num_splits  KV splits per request (0 = chosen by the library).
+ * workspace, workspace_bytes  device scratch of at least the size
+ *             dcp_stripe_attn_workspace() reports for these arguments.
+ * o    [B][q_len][H][v_dim] fp32 device out: o_r, normalised inside the stripe.
+ * lse  [B][q_len][H] fp32 device out: lse_r in the chosen base.
+ *      A query with no visible row in this stripe gets o = 0, lse = -inf
+ *      (zero weight in the merge; page "PCP/DCP" section 4.1).
+ * status device int32, nullable: DCP_ERANGE when a needed page id is outside
+ *      [0, num_pages) or missing from the table (that request's output is
+ *      then unspecified, memory outside the buffers is never read). */
+typedef struct dcp_attn_args {
+  dcp_layout layout;
+  int32_t rank;
+  int32_t batch;
+  int32_t q_len;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t v_dim;
+  const void* q;
+  const void* pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t bt_cols;
+  const int32_t* seq_len;
+  float scale;
+  int32_t lse_base;
+  int32_t num_splits;
+  void* workspace;
+  size_t workspace_bytes;
+  float* o;
+  float* lse;
+  int32_t* status;
+} dcp_attn_args;
+
+/* Workspace bytes dcp_stripe_attn needs for `args` (pointers are not read). */
+int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);
+
+/* dcp_stripe_attn -- one rank's local attention over its stripe, returning
+ * (o_r, lse_r) (page "DCP", idea two; page "MLA 的 DCP", section 3). */
+int dcp_stripe_attn(const dcp_attn_args* args, void* stream);
+
+/* dcp_lse_merge -- exact merge of N stripes' partial results.
+ * Page "DCP", "merge operator and numerical stability"; SGLang DCP docs,
+ * "MLA decode dataflow": m = max_r lse_r, w_r = base^(lse_r - m),
+ * o = sum_r w_r o_r / sum_r w_r, lse = m + log_base(sum_r w_r).
+ * o_parts [N][rows][v_dim] fp32, lse_parts [N][rows] fp32 device, lse in
+ * base e (lse_base 0) or 2 (lse_base 1).  Stripes with lse = -inf carry zero
+ * weight and their o values are never used.  If every stripe of a row is
+ * empty: o = 0, lse = -inf.  o [rows][v_dim], lse [rows] fp32 device out
+ * (lse may be NULL).  v_dim % 4 == 0. */
+int dcp_lse_merge(int32_t n_stripes, int64_t rows, int32_t v_dim,
+                  const float* o_parts, const float* lse_parts, int32_t lse_base,
+                  float* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H */

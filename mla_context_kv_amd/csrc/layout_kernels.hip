@@ -1,0 +1,159 @@
+// Integer side of DCP: slot map, per-rank interval counts and the
+// owner-filtered paged KV write.
+//
+// Ownership is a pure function of the global position (page "DCP"
+// (zdszero), "core abstraction", idea one); runs of I tokens go to the ranks
+// in turn (page "PCP/DCP" (obnotes), section 6); a row's slot is its page id
+// times the page size plus its offset in the page (page "PCP/DCP", "KV cache
+// management"); a new latent row is stored only on its owner (page
+// "MLA 的 Decode Context Parallelism", section 4, stage 2).
+#include "dcp_common.h"
+
+namespace dcp {
+namespace {
+
+constexpr int kThreads = 256;
+
+int grid_for(int64_t work, int64_t per_block) {
+  int64_t g = ceil_div(work, per_block);
+  if (g < 1) g = 1;
+  if (g > 16384) g = 16384;   // grid-stride loops cover the rest
+  return static_cast<int>(g);
+}
+
+__global__ void __launch_bounds__(kThreads)
+slot_map_kernel(Layout L, int64_t P, int32_t rank, const int64_t* __restrict__ pos,
+                const int32_t* __restrict__ req, int64_t n, const int32_t* __restrict__ bt,
+                int32_t bt_rows, int32_t bt_cols, int32_t* __restrict__ owner,
+                int64_t* __restrict__ row, int64_t* __restrict__ slot, int32_t* status) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t p = pos[i];
+    if (p < 0) {
+      if (owner) owner[i] = -1;
+      if (row) row[i] = -1;
+      if (slot) slot[i] = -1;
+      flag_range(status);
+      continue;
+    }
+    const int64_t o = owner_of(L, p);
+    const int64_t r = row_of(L, p);
+    if (owner) owner[i] = (int32_t)o;
+    if (row) row[i] = r;
+    if (!slot) continue;
+    int64_t s = -1;
+    if (rank >= 0 && bt != nullptr && o == rank) {
+      const int64_t b = req ? req[i] : 0;
+      const int64_t col = r / P;
+      if (b < 0 || b >= bt_rows || col >= bt_cols) {
+        flag_range(status);
+      } else {
+        const int32_t pg = bt[b * bt_cols + col];
+        if (pg < 0) flag_range(status);
+        else s = (int64_t)pg * P + r % P;
+      }
+    }
+    slot[i] = s;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+local_count_kernel(Layout L, const int64_t* __restrict__ start, const int64_t* __restrict__ len,
+                   int64_t n, int64_t* __restrict__ count) {
+  const int64_t total = n * L.N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total; k += stride) {
+    const int64_t i = k / L.N;
+    const int64_t r = k - i * L.N;
+    const int64_t a = start ? start[i] : 0;
+    const int64_t l = len[i];
+    int64_t c = 0;
+    if (a >= 0 && l > 0) c = count_of(L, a + l, r) - count_of(L, a, r);
+    count[k] = c;
+  }
+}
+
+// One new row per group of 8 lanes; each lane copies 16-byte chunks
+// c, c+8, c+16, ... so a group moves 128 contiguous bytes per step.
+__global__ void __launch_bounds__(kThreads)
+kv_write_kernel(Layout L, int64_t P, int32_t rank, const uint4* __restrict__ kv_new,
+                int32_t chunks, int64_t T, const int64_t* __restrict__ pos,
+                const int32_t* __restrict__ req, const int32_t* __restrict__ bt,
+                int32_t bt_rows, int32_t bt_cols, uint4* __restrict__ pool, int64_t num_pages,
+                int32_t* status) {
+  const int64_t groups = (int64_t)gridDim.x * (blockDim.x / 8);
+  const int lane8 = threadIdx.x & 7;
+  for (int64_t i = (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8; i < T; i += groups) {
+    const int64_t p = pos[i];
+    if (p < 0) {
+      if (lane8 == 0) flag_range(status);
+      continue;
+    }
+    if (owner_of(L, p) != rank) continue;          // not ours: the row is not even read
+    const int64_t r = row_of(L, p);
+    const int64_t b = req ? req[i] : 0;
+    const int64_t col = r / P;
+    if (b < 0 || b >= bt_rows || col >= bt_cols) {
+      if (lane8 == 0) flag_range(status);
+      continue;
+    }
+    const int32_t pg = bt[b * bt_cols + col];
+    if (pg < 0 || pg >= num_pages) {
+      if (lane8 == 0) flag_range(status);
+      continue;
+    }
+    const int64_t slot = (int64_t)pg * P + r % P;
+    const uint4* src = kv_new + i * chunks;
+    uint4* dst = pool + slot * chunks;
+    for (int c = lane8; c < chunks; c += 8) dst[c] = src[c];
+  }
+}
+
+}  // namespace
+}  // namespace dcp
+
+using namespace dcp;
+
+extern "C" int dcp_slot_map(dcp_layout layout, int32_t rank, const int64_t* pos, const int32_t* req,
+                            int64_t n, const int32_t* block_table, int32_t bt_rows, int32_t bt_cols,
+                            int32_t* owner, int64_t* row, int64_t* slot, int32_t* status,
+                            void* stream) {
+  if (!layout_ok(layout) || n < 0) return DCP_EINVAL;
+  if (rank < -1 || rank >= layout.n_stripes) return DCP_EINVAL;
+  if (block_table && (bt_rows < 1 || bt_cols < 1)) return DCP_EINVAL;
+  if (n > 0 && pos == nullptr) return DCP_EINVAL;
+  if (n == 0) return DCP_OK;
+  hipLaunchKernelGGL(slot_map_kernel, dim3(grid_for(n, kThreads)), dim3(kThreads), 0,
+                     (hipStream_t)stream, to_layout(layout), (int64_t)layout.page_size, rank, pos,
+                     req, n, block_table, bt_rows, bt_cols, owner, row, slot, status);
+  return launch_status();
+}
+
+extern "C" int dcp_local_count(dcp_layout layout, const int64_t* start, const int64_t* len,
+                               int64_t n, int64_t* count, void* stream) {
+  if (!layout_ok(layout) || n < 0) return DCP_EINVAL;
+  if (n > 0 && (len == nullptr || count == nullptr)) return DCP_EINVAL;
+  if (n == 0) return DCP_OK;
+  hipLaunchKernelGGL(local_count_kernel, dim3(grid_for(n * layout.n_stripes, kThreads)),
+                     dim3(kThreads), 0, (hipStream_t)stream, to_layout(layout), start, len, n,
+                     count);
+  return launch_status();
+}
+
+extern "C" int dcp_kv_write(dcp_layout layout, int32_t rank, const void* kv_new, int32_t row_dim,
+                            int64_t T, const int64_t* pos, const int32_t* req,
+                            const int32_t* block_table, int32_t bt_rows, int32_t bt_cols,
+                            void* pool, int64_t num_pages, int32_t* status, void* stream) {
+  if (!layout_ok(layout) || T < 0) return DCP_EINVAL;
+  if (rank < 0 || rank >= layout.n_stripes) return DCP_EINVAL;
+  if (row_dim <= 0 || row_dim % 8 != 0) return DCP_EINVAL;
+  if (block_table == nullptr || bt_rows < 1 || bt_cols < 1 || num_pages < 1 || pool == nullptr)
+    return DCP_EINVAL;
+  if (T > 0 && (kv_new == nullptr || pos == nullptr)) return DCP_EINVAL;
+  if (T == 0) return DCP_OK;
+  hipLaunchKernelGGL(kv_write_kernel, dim3(grid_for(T, kThreads / 8)), dim3(kThreads), 0,
+                     (hipStream_t)stream, to_layout(layout), (int64_t)layout.page_size, rank,
+                     (const uint4*)kv_new, row_dim / 8, T, pos, req, block_table, bt_rows, bt_cols,
+                     (uint4*)pool, num_pages, status);
+  return launch_status();
+}

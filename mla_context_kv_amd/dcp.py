@@ -1,0 +1,270 @@
+"""Thin ctypes binding of libdcp (include/dcp.h) with the same entry-point names.
+
+Only argument marshalling happens here: shapes, dtypes, devices and
+contiguity are checked, tensors are passed as raw device pointers together
+with torch's current HIP stream, and every step of the computation runs in the
+library's kernels.  There is no fallback: if libdcp.so is missing or fails to
+load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdcp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dcp.h")
+
+DCP_OK = 0
+DCP_EINVAL = -1
+DCP_EUNSUPPORTED = -2
+DCP_EHIP = -3
+DCP_ERANGE = -4
+
+HEAD_DIM = 576
+V_DIM = 512
+
+
+class DcpError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+
+
+class dcp_layout(ctypes.Structure):
+    _fields_ = [("n_stripes", ctypes.c_int32), ("interleave", ctypes.c_int32),
+                ("page_size", ctypes.c_int32)]
+
+
+class dcp_attn_args(ctypes.Structure):
+    _fields_ = [
+        ("layout", dcp_layout),
+        ("rank", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("v_dim", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("pool", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
+        ("bt_cols", ctypes.c_int32),
+        ("seq_len", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("lse_base", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+_lib_handle: Optional[ctypes.CDLL] = None
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "dcp_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "dcp_abi_version": (ctypes.c_int, []),
+    "dcp_slot_map": (ctypes.c_int, [dcp_layout, _I32, _VP, _VP, _I64, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "dcp_local_count": (ctypes.c_int, [dcp_layout, _VP, _VP, _I64, _VP, _VP]),
+    "dcp_kv_write": (ctypes.c_int, [dcp_layout, _I32, _VP, _I32, _I64, _VP, _VP, _VP, _I32, _I32, _VP, _I64, _VP, _VP]),
+    "dcp_stripe_attn_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), ctypes.POINTER(ctypes.c_size_t)]),
+    "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
+    "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdcp (raises if it is not built or cannot be loaded)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, argt) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = argt
+        _lib_handle = h
+    return _lib_handle
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/dcp.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcp_[a-z0-9_]+)\s*\(", text)))
+
+
+def strerror(code: int) -> str:
+    return lib().dcp_strerror(int(code)).decode()
+
+
+def layout(n_stripes: int, interleave: int = 1, page_size: int = 64) -> dcp_layout:
+    return dcp_layout(int(n_stripes), int(interleave), int(page_size))
+
+
+def _check(code: int, where: str):
+    if code != DCP_OK:
+        raise DcpError(code, where)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "", device=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def dcp_slot_map(lay: dcp_layout, rank: int, pos: torch.Tensor, req: Optional[torch.Tensor] = None,
+                 block_table: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None):
+    """owner (int32), local row (int64) and slot (int64) of every position."""
+    dev = pos.device
+    n = pos.numel()
+    owner = torch.empty(n, dtype=torch.int32, device=dev)
+    row = torch.empty(n, dtype=torch.int64, device=dev)
+    slot = torch.empty(n, dtype=torch.int64, device=dev)
+    bt_rows, bt_cols = (block_table.shape if block_table is not None else (0, 0))
+    rc = lib().dcp_slot_map(lay, int(rank), _ptr(pos, torch.int64, "pos", dev),
+                            _ptr(req, torch.int32, "req", dev), n,
+                            _ptr(block_table, torch.int32, "block_table", dev), int(bt_rows), int(bt_cols),
+                            owner.data_ptr(), row.data_ptr(), slot.data_ptr(),
+                            _ptr(status, torch.int32, "status", dev), _stream(dev))
+    _check(rc, "dcp_slot_map")
+    return owner, row, slot
+
+
+def dcp_local_count(lay: dcp_layout, length: torch.Tensor, start: Optional[torch.Tensor] = None):
+    """Every rank's share of [start, start+length): int64 [n, N]."""
+    dev = length.device
+    n = length.numel()
+    count = torch.empty((n, lay.n_stripes), dtype=torch.int64, device=dev)
+    rc = lib().dcp_local_count(lay, _ptr(start, torch.int64, "start", dev),
+                               _ptr(length, torch.int64, "length", dev), n, count.data_ptr(), _stream(dev))
+    _check(rc, "dcp_local_count")
+    return count
+
+
+def dcp_kv_write(lay: dcp_layout, rank: int, kv_new: torch.Tensor, pos: torch.Tensor,
+                 req: Optional[torch.Tensor], block_table: torch.Tensor, pool: torch.Tensor,
+                 status: Optional[torch.Tensor] = None) -> None:
+    """Store the rows of kv_new that rank `rank` owns into its paged pool."""
+    dev = pool.device
+    if kv_new.dim() != 2 or pool.dim() != 3 or pool.shape[2] != kv_new.shape[1]:
+        raise ValueError("kv_new must be [T, D] and pool [pages, P, D]")
+    if pool.shape[1] != lay.page_size:
+        raise ValueError("pool page size does not match the layout")
+    rc = lib().dcp_kv_write(lay, int(rank), _ptr(kv_new, torch.bfloat16, "kv_new", dev), int(kv_new.shape[1]),
+                            int(kv_new.shape[0]), _ptr(pos, torch.int64, "pos", dev),
+                            _ptr(req, torch.int32, "req", dev), _ptr(block_table, torch.int32, "block_table", dev),
+                            int(block_table.shape[0]), int(block_table.shape[1]),
+                            _ptr(pool, torch.bfloat16, "pool", dev), int(pool.shape[0]),
+                            _ptr(status, torch.int32, "status", dev), _stream(dev))
+    _check(rc, "dcp_kv_write")
+
+
+def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits,
+               workspace, o, lse, status) -> dcp_attn_args:
+    B, q_len, H, D = q.shape
+    a = dcp_attn_args()
+    a.layout = lay
+    a.rank = int(rank)
+    a.batch, a.q_len, a.n_heads, a.head_dim, a.v_dim = int(B), int(q_len), int(H), int(D), V_DIM
+    a.num_pages = int(pool.shape[0])
+    a.bt_cols = int(block_table.shape[1])
+    a.scale = float(scale)
+    a.lse_base = int(lse_base)
+    a.num_splits = int(num_splits)
+    return a
+
+
+def dcp_stripe_attn_workspace(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Tensor,
+                              block_table: torch.Tensor, num_splits: int = 0, lse_base: int = 0) -> int:
+    """Workspace bytes dcp_stripe_attn needs for these shapes."""
+    a = _attn_args(lay, rank, q, pool, block_table, None, 1.0, lse_base, num_splits, None, None, None, None)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(nbytes)), "dcp_stripe_attn_workspace")
+    return int(nbytes.value)
+
+
+def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Tensor,
+                    block_table: torch.Tensor, seq_len: torch.Tensor, scale: float, lse_base: int = 0,
+                    num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    status: Optional[torch.Tensor] = None):
+    """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H])."""
+    dev = q.device
+    if q.dim() != 4 or pool.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("q must be [B, q_len, H, 576], pool [pages, P, 576], block_table [B, cols]")
+    B, q_len, H, D = q.shape
+    if pool.shape[1] != lay.page_size or pool.shape[2] != D:
+        raise ValueError("pool must be [pages, page_size, head_dim]")
+    if block_table.shape[0] != B or seq_len.numel() != B:
+        raise ValueError("block_table and seq_len need one row per request")
+    if o is None:
+        o = torch.empty((B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
+    if o.numel() != B * q_len * H * V_DIM or lse.numel() != B * q_len * H:
+        raise ValueError("o / lse have the wrong size")
+    a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status)
+    need = ctypes.c_size_t(0)
+    _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
+    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    a.q = _ptr(q, torch.bfloat16, "q", dev)
+    a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
+    a.block_table = _ptr(block_table, torch.int32, "block_table", dev)
+    a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
+    a.workspace = _ptr(workspace, None, "workspace", dev) if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.o = _ptr(o, torch.float32, "o", dev)
+    a.lse = _ptr(lse, torch.float32, "lse", dev)
+    a.status = _ptr(status, torch.int32, "status", dev)
+    _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
+    return o, lse
+
+
+def dcp_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, lse_base: int = 0,
+                  o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Exact merge over the leading (stripe) axis: o_parts [N, ..., V], lse_parts [N, ...]."""
+    dev = o_parts.device
+    N = o_parts.shape[0]
+    v_dim = o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    if o_parts.numel() != N * rows * v_dim or lse_parts.shape[0] != N:
+        raise ValueError("o_parts must be [N, rows..., V] matching lse_parts [N, rows...]")
+    if o is None:
+        o = torch.empty(o_parts.shape[1:], dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=dev)
+    rc = lib().dcp_lse_merge(int(N), int(rows), int(v_dim), _ptr(o_parts, torch.float32, "o_parts", dev),
+                             _ptr(lse_parts, torch.float32, "lse_parts", dev), int(lse_base),
+                             _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev),
+                             _stream(dev))
+    _check(rc, "dcp_lse_merge")
+    return o, lse

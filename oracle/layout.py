@@ -97,13 +97,24 @@ def page_slot(block_table_row: np.ndarray, local_row: np.ndarray, page_size: int
     """Physical slot of a local row: page id of its page times page size plus
     the offset inside the page.  Rows whose page entry is missing or negative
     map to -1."""
+    return page_slots(np.asarray(block_table_row)[None, :], np.zeros(np.shape(local_row), dtype=np.int64),
+                      local_row, page_size)
+
+
+def page_slots(block_table: np.ndarray, req: np.ndarray, local_row: np.ndarray, page_size: int) -> np.ndarray:
+    """page_slot for many rows at once: row i of request req[i] sits at
+    block_table[req[i], local_row[i] // page_size] * page_size + local_row[i] % page_size
+    (-1 where the request or page index is outside the table or the entry is negative)."""
+    block_table = np.asarray(block_table, dtype=np.int64)
+    req = np.asarray(req, dtype=np.int64)
     local_row = np.asarray(local_row, dtype=np.int64)
     page_idx = local_row // page_size
     offset = local_row % page_size
-    out = np.full(local_row.shape, -1, dtype=np.int64)
-    inside = page_idx < len(block_table_row)
+    rows, cols = block_table.shape
+    inside = (req >= 0) & (req < rows) & (page_idx >= 0) & (page_idx < cols)
     page = np.full(local_row.shape, -1, dtype=np.int64)
-    page[inside] = np.asarray(block_table_row, dtype=np.int64)[page_idx[inside]]
+    page[inside] = block_table[req[inside], page_idx[inside]]
+    out = np.full(local_row.shape, -1, dtype=np.int64)
     ok = page >= 0
     out[ok] = page[ok] * page_size + offset[ok]
     return out
@@ -135,8 +146,7 @@ def slot_map(pos: np.ndarray, req: np.ndarray, N: int, I: int, page_size: int,
     slot = np.full(n, -1, dtype=np.int64)
     if rank >= 0 and block_table is not None:
         mine = owner == rank
-        for i in np.nonzero(mine)[0]:
-            slot[i] = page_slot(block_table[req[i]], np.array([row[i]]), page_size)[0]
+        slot[mine] = page_slots(block_table, req[mine], row[mine], page_size)
     return owner, row, slot
 
 
@@ -151,6 +161,6 @@ def kv_write(pool: np.ndarray, kv_rows: np.ndarray, pos: np.ndarray, req: np.nda
     """
     out = pool.copy()
     _, _, slot = slot_map(pos, req, N, I, page_size, rank, block_table)
-    for i in np.nonzero(slot >= 0)[0]:
-        out[slot[i]] = kv_rows[i]
+    keep = slot >= 0
+    out[slot[keep]] = kv_rows[keep]
     return out

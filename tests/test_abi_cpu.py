@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dcp.h declares, and rejects bad arguments on the host before any HIP
+call (so nothing is enqueued)."""
+
+import ctypes
+
+import pytest
+
+from mla_context_kv_amd import dcp
+
+L = dcp.lib()
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails validation first
+
+
+def test_library_exports_every_declared_function():
+    names = dcp.header_functions()
+    assert {"dcp_slot_map", "dcp_local_count", "dcp_kv_write", "dcp_stripe_attn",
+            "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror_and_version():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(dcp.strerror(code), str) and dcp.strerror(code)
+    assert L.dcp_abi_version() >= 1
+
+
+BAD_LAYOUTS = [dcp.layout(0, 1, 64), dcp.layout(8, 0, 64), dcp.layout(8, 1, 0), dcp.layout(8, 3, 64),
+               dcp.layout(-2, 1, 64)]
+
+
+@pytest.mark.parametrize("lay", BAD_LAYOUTS)
+def test_bad_layout_is_rejected_everywhere(lay):
+    assert L.dcp_slot_map(lay, 0, FAKE, None, 4, None, 0, 0, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_local_count(lay, None, FAKE, 4, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_kv_write(lay, 0, FAKE, 576, 4, FAKE, None, FAKE, 1, 1, FAKE, 1, None, None) == dcp.DCP_EINVAL
+    a = _args(lay=lay)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+
+
+def test_slot_map_argument_errors():
+    lay = dcp.layout(8, 1, 64)
+    assert L.dcp_slot_map(lay, 8, FAKE, None, 4, None, 0, 0, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_slot_map(lay, -2, FAKE, None, 4, None, 0, 0, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_slot_map(lay, 0, None, None, 4, None, 0, 0, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_slot_map(lay, 0, FAKE, None, -1, None, 0, 0, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_slot_map(lay, 0, FAKE, None, 4, FAKE, 0, 4, FAKE, FAKE, FAKE, None, None) == dcp.DCP_EINVAL
+    # nothing to do: success without touching the device
+    assert L.dcp_slot_map(lay, 0, None, None, 0, None, 0, 0, None, None, None, None, None) == dcp.DCP_OK
+
+
+def test_local_count_argument_errors():
+    lay = dcp.layout(8, 64, 64)
+    assert L.dcp_local_count(lay, None, None, 3, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_local_count(lay, None, FAKE, 3, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_local_count(lay, None, FAKE, -3, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_local_count(lay, None, None, 0, None, None) == dcp.DCP_OK
+
+
+def test_kv_write_argument_errors():
+    lay = dcp.layout(4, 1, 16)
+    ok = dict(rank=0, kv=FAKE, row_dim=576, T=4, pos=FAKE, bt=FAKE, rows=1, cols=1, pool=FAKE, pages=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.dcp_kv_write(lay, a["rank"], a["kv"], a["row_dim"], a["T"], a["pos"], None, a["bt"],
+                              a["rows"], a["cols"], a["pool"], a["pages"], None, None)
+
+    assert call(rank=4) == dcp.DCP_EINVAL
+    assert call(rank=-1) == dcp.DCP_EINVAL
+    assert call(row_dim=570) == dcp.DCP_EINVAL
+    assert call(T=-1) == dcp.DCP_EINVAL
+    assert call(bt=None) == dcp.DCP_EINVAL
+    assert call(rows=0) == dcp.DCP_EINVAL
+    assert call(pool=None) == dcp.DCP_EINVAL
+    assert call(pages=0) == dcp.DCP_EINVAL
+    assert call(kv=None) == dcp.DCP_EINVAL
+    assert call(T=0, kv=None, pos=None) == dcp.DCP_OK
+
+
+def _args(lay=None, **kw):
+    a = dcp.dcp_attn_args()
+    a.layout = lay if lay is not None else dcp.layout(8, 1, 64)
+    a.rank, a.batch, a.q_len, a.n_heads, a.head_dim, a.v_dim = 0, 2, 1, 16, 576, 512
+    a.q = a.pool = a.block_table = a.seq_len = a.o = a.lse = 0x1000
+    a.num_pages, a.bt_cols, a.scale, a.lse_base, a.num_splits = 4, 4, 0.07, 0, 2
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("rank", 8, dcp.DCP_EINVAL), ("rank", -1, dcp.DCP_EINVAL), ("batch", 0, dcp.DCP_EINVAL),
+    ("q_len", 0, dcp.DCP_EINVAL), ("n_heads", 0, dcp.DCP_EINVAL), ("head_dim", 512, dcp.DCP_EUNSUPPORTED),
+    ("v_dim", 576, dcp.DCP_EUNSUPPORTED), ("num_pages", 0, dcp.DCP_EINVAL), ("bt_cols", 0, dcp.DCP_EINVAL),
+    ("lse_base", 2, dcp.DCP_EINVAL), ("num_splits", -1, dcp.DCP_EINVAL), ("q", None, dcp.DCP_EINVAL),
+    ("pool", None, dcp.DCP_EINVAL), ("seq_len", None, dcp.DCP_EINVAL), ("o", None, dcp.DCP_EINVAL),
+])
+def test_stripe_attn_argument_errors(field, value, code):
+    a = _args(**{field: value})
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == code
+
+
+def test_stripe_attn_workspace_size_and_missing_workspace():
+    a = _args(num_splits=3, bt_cols=100)
+    n = ctypes.c_size_t(0)
+    assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK
+    assert n.value == 3 * 2 * 16 * (512 + 1) * 4
+    a = _args(num_splits=1)
+    assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK and n.value == 0
+    assert L.dcp_stripe_attn_workspace(ctypes.byref(a), None) == dcp.DCP_EINVAL
+    # splits need a workspace: rejected before launch when none is given
+    a = _args(num_splits=3, bt_cols=100)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+
+
+def test_lse_merge_argument_errors():
+    assert L.dcp_lse_merge(0, 4, 512, FAKE, FAKE, 0, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_lse_merge(8, -1, 512, FAKE, FAKE, 0, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_lse_merge(8, 4, 510, FAKE, FAKE, 0, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_lse_merge(8, 4, 512, FAKE, FAKE, 3, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_lse_merge(8, 4, 512, None, FAKE, 0, FAKE, None, None) == dcp.DCP_EINVAL
+    assert L.dcp_lse_merge(8, 0, 512, None, None, 0, None, None, None) == dcp.DCP_OK

@@ -1,0 +1,165 @@
+"""GPU parity of the integer path: slot map, interval counts and the
+owner-filtered paged KV write, bit-exact against the oracle's simulation."""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_context_kv_amd import dcp, stripes, workloads
+from oracle import layout as OL
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)]
+
+
+def _tokens(lens):
+    pos = np.concatenate([np.arange(int(s), dtype=np.int64) for s in lens])
+    req = np.concatenate([np.full(int(s), b, dtype=np.int32) for b, s in enumerate(lens)])
+    return pos, req
+
+
+@pytest.mark.parametrize("name,I", CASES)
+def test_slot_map_bit_exact_full_size(name, I):
+    w = workloads.WORKLOADS[name]
+    dev = H.device()
+    lens = workloads.seq_lens(w)
+    N, P = w.N, w.page_size
+    print(f"slot map: {name} I={I} tokens={int(lens.sum())}", flush=True)
+    counts = H.oracle_counts(lens, N, I)
+    tables, _ = workloads.make_block_tables(w, stripes.pages_from_counts(counts, P))
+    pos, req = _tokens(lens)
+    pos_d = torch.from_numpy(pos).to(dev)
+    req_d = torch.from_numpy(req).to(dev)
+    lay = dcp.layout(N, I, P)
+    own_ref, row_ref, _ = OL.slot_map(pos, req, N, I, P, -1, None)
+    for r in range(N):
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        bt = torch.from_numpy(tables[r]).to(dev)
+        owner, row, slot = dcp.dcp_slot_map(lay, r, pos_d, req_d, bt, status)
+        torch.cuda.synchronize()
+        _, _, slot_ref = OL.slot_map(pos, req, N, I, P, r, tables[r])
+        assert (owner.cpu().numpy() == own_ref).all()
+        assert (row.cpu().numpy() == row_ref).all()
+        assert (slot.cpu().numpy() == slot_ref).all()
+        assert int(status.item()) == 0
+
+
+def test_slot_map_large_positions_and_errors():
+    dev = H.device()
+    rng = np.random.default_rng(7)
+    pos = rng.integers(0, 1 << 40, size=3000).astype(np.int64)
+    for N, I in [(8, 1), (8, 64), (5, 2), (1, 1)]:
+        lay = dcp.layout(N, I, 64)
+        owner, row, slot = dcp.dcp_slot_map(lay, -1, torch.from_numpy(pos).to(dev))
+        torch.cuda.synchronize()
+        ref = np.array([OL.owner_row_walk(int(p), N, I) for p in pos])
+        assert (owner.cpu().numpy() == ref[:, 0]).all() and (row.cpu().numpy() == ref[:, 1]).all()
+        assert (slot.cpu().numpy() == -1).all()
+    # an owned row whose page is missing from the table, and a negative position, raise DCP_ERANGE
+    lay = dcp.layout(8, 1, 2)
+    table = torch.tensor([[7, -1]], dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    p = torch.tensor([0, 8, 16, 8 * 10**6], dtype=torch.int64, device=dev)
+    _, _, slot = dcp.dcp_slot_map(lay, 0, p, torch.zeros(4, dtype=torch.int32, device=dev), table, status)
+    torch.cuda.synchronize()
+    assert slot.cpu().tolist() == [14, 15, -1, -1] and int(status.item()) == dcp.DCP_ERANGE
+    status.zero_()
+    owner, row, slot = dcp.dcp_slot_map(lay, 0, torch.tensor([-5], dtype=torch.int64, device=dev), None, None, status)
+    torch.cuda.synchronize()
+    assert owner.item() == -1 and row.item() == -1 and int(status.item()) == dcp.DCP_ERANGE
+
+
+@pytest.mark.parametrize("N,I", [(8, 1), (8, 64), (4, 1), (3, 16), (1, 1)])
+def test_local_count_bit_exact(N, I):
+    dev = H.device()
+    rng = np.random.default_rng(N * 100 + I)
+    start = np.concatenate([[0, 1000, 0, 5, 513], rng.integers(0, 70000, size=200)]).astype(np.int64)
+    length = np.concatenate([[131072, 333, 0, 1, 64], rng.integers(0, 70000, size=200)]).astype(np.int64)
+    got = dcp.dcp_local_count(dcp.layout(N, I, 64 if 64 % I == 0 else I), torch.from_numpy(length).to(dev),
+                              torch.from_numpy(start).to(dev)).cpu().numpy()
+    for i in range(len(start)):
+        assert (got[i] == OL.interval_counts(int(start[i]), int(length[i]), N, I)).all(), (start[i], length[i])
+    if (N, I) == (8, 1):
+        assert got[1].tolist() == [42, 42, 42, 42, 42, 41, 41, 41]
+    if (N, I) == (8, 64):
+        assert got[1].tolist() == [64, 64, 64, 64, 53, 0, 0, 24]
+
+
+def _rows_written(pool):
+    """Rows of a pool that are no longer the NaN fill."""
+    return ~(pool.view(torch.int16) == 0x7FC0).all(dim=-1)
+
+
+@pytest.mark.parametrize("name,I", CASES)
+def test_kv_write_places_every_owned_row(name, I):
+    w = workloads.WORKLOADS[name]
+    print(f"kv write: {name} I={I}", flush=True)
+    s = H.make_setup(w, I)
+    dev = s.q.device
+    assert int(s.status.item()) == 0
+    pos, req = _tokens(s.lens)
+    own_ref, _, _ = OL.slot_map(pos, req, w.N, I, w.page_size, -1, None)
+    src_row = np.arange(len(pos), dtype=np.int64)          # row index into s.kv
+    for r in range(w.N):
+        _, _, slot = OL.slot_map(pos, req, w.N, I, w.page_size, r, s.tables[r])
+        mine = slot >= 0
+        assert mine.sum() == (own_ref == r).sum()
+        flat = s.sp.pools[r].view(-1, workloads.ROW_DIM)
+        got = flat[torch.from_numpy(slot[mine]).to(dev)]
+        want = s.kv[torch.from_numpy(src_row[mine]).to(dev)]
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        written = _rows_written(flat)
+        assert int(written.sum().item()) == int(mine.sum())
+    del s
+    torch.cuda.empty_cache()
+
+
+def test_chunked_write_equals_one_shot_and_counts():
+    """Ragged batch: [0,1000), [1000,1333), [1333,S) in three calls."""
+    w = workloads.WORKLOADS["ragged"]
+    dev = H.device()
+    lens = workloads.seq_lens(w)
+    lay = dcp.layout(w.N, 1, w.page_size)
+    counts = H.oracle_counts(lens, w.N, 1)
+    tables, pool_pages = workloads.make_block_tables(w, stripes.pages_from_counts(counts, w.page_size))
+    kv = workloads.make_all_kv(w, lens, dev)
+    one = stripes.build_pools(lay, lens, kv, tables, pool_pages, nan_fill=True)
+    pos, req = stripes.positions_and_requests(lens, dev)
+    pools = torch.empty_like(one.pools)
+    workloads.bf16_nan_fill(pools)
+    mid_only = torch.empty_like(one.pools)
+    workloads.bf16_nan_fill(mid_only)
+    for lo, hi in [(0, 1000), (1000, 1333), (1333, 1 << 30)]:
+        sel = (pos >= lo) & (pos < hi)
+        for r in range(w.N):
+            dcp.dcp_kv_write(lay, r, kv[sel].contiguous(), pos[sel].contiguous(), req[sel].contiguous(),
+                             one.tables[r], pools[r])
+            if lo == 1000:
+                dcp.dcp_kv_write(lay, r, kv[sel].contiguous(), pos[sel].contiguous(), req[sel].contiguous(),
+                                 one.tables[r], mid_only[r])
+    torch.cuda.synchronize()
+    assert torch.equal(pools.view(torch.int16), one.pools.view(torch.int16))
+    assert int((lens >= 1333).sum()) > 0
+    per_rank = np.array([int(_rows_written(mid_only[r].view(-1, workloads.ROW_DIM)).sum().item()) for r in range(w.N)])
+    # every request contributes its share of [1000, min(S_b, 1333)); a full chunk is [42]*5 + [41]*3
+    want = sum(OL.interval_counts(1000, max(0, min(int(S), 1333) - 1000), w.N, 1) for S in lens)
+    assert (per_rank == want).all()
+
+
+def test_kv_write_out_of_range_page_is_skipped_and_flagged():
+    dev = H.device()
+    lay = dcp.layout(2, 1, 4)
+    pool = torch.zeros((3, 4, 8), dtype=torch.bfloat16, device=dev)
+    table = torch.tensor([[0, 5, 1]], dtype=torch.int32, device=dev)     # page 5 does not exist
+    kv = torch.ones((24, 8), dtype=torch.bfloat16, device=dev)
+    pos = torch.arange(24, dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dcp.dcp_kv_write(lay, 0, kv, pos, None, table, pool, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == dcp.DCP_ERANGE
+    # rank 0 owns positions 0,2,..,22 -> rows 0..11: pages 0, 5 (skipped), 1
+    assert pool[0].float().sum().item() == 32 and pool[1].float().sum().item() == 32
+    assert pool[2].float().sum().item() == 0
