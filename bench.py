@@ -1,0 +1,231 @@
+"""Decode-step benchmark of DCP stripe attention + LSE merge on one MI355X.
+
+One step = the N per-rank dcp_stripe_attn launches, each at its real per-rank
+shape (all H query heads against that rank's stripe of every request), plus
+one dcp_lse_merge of the N partials, all on one stream with the inputs already
+resident in HBM.  Default workload: the Kimi-K3-shaped decode batch
+(B=64 requests x 131072 tokens, H=96, N=8 stripes, page 64, base-2 LSE).
+
+Prints one JSON line: KV GB/s as `value`, microseconds per step, the roofline
+of the dominant kernel (the stripe attention, timed per launch with HIP events
+on its stream) and the float64 CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+ROW_BYTES = 576 * 2             # one latent row (key = whole row, value = first 512 dims)
+FLOP_PER_ROW_QUERY = 2 * 576 + 2 * 512   # QK^T + PV per (query row, visible token)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3", help="tiny | dsv3 | k3 | ragged | long")
+    ap.add_argument("--interleave", type=int, default=1)
+    ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=1)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the per-rank stripe kernels of all N stripes and the merge run on a "
+              f"single MI355X; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_context_kv_amd import dcp, stripes, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    I = args.interleave
+    N, P = w.N, w.page_size
+    lay = dcp.layout(N, I, P)
+    lens = workloads.seq_lens(w)
+    base = 1 if w.lse_base == "2" else 0
+
+    # ---- set-up (not timed): per-rank counts through the library, page tables,
+    # inputs, owner-filtered write into the N pools
+    t0 = time.perf_counter()
+    counts = dcp.dcp_local_count(lay, torch.from_numpy(lens.astype(np.int64)).to(dev)).cpu().numpy()   # [B, N]
+    tables, pool_pages = workloads.make_block_tables(w, stripes.pages_from_counts(counts, P))
+    q = workloads.make_q(w, dev)
+    kv = workloads.make_all_kv(w, lens, dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sp = stripes.build_pools(lay, lens, kv, tables, pool_pages, status=status)
+    ns = args.cpu_sample_requests
+    sample = None
+    if not args.no_cpu_baseline:
+        off = 0
+        sample = []
+        for b in range(min(ns, w.B)):
+            S = int(lens[b])
+            sample.append((q[b].double().cpu().numpy(), kv[off:off + S].double().cpu().numpy(), S))
+            off += S
+    del kv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    setup_s = time.perf_counter() - t0
+
+    M = w.q_len * w.H
+    o_parts = torch.empty((N, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((N, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # prebuilt argument blocks: the timed loop only calls into the library
+    L = dcp.lib()
+    attn_args = []
+    ws_bytes = 0
+    for r in range(N):
+        a = dcp._attn_args(lay, r, q, sp.pools[r], sp.tables[r], sp.seq_len, workloads.SCALE, base, args.splits,
+                           None, None, None, None)
+        need = ctypes.c_size_t(0)
+        assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
+        ws_bytes = max(ws_bytes, need.value)
+        attn_args.append(a)
+    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    for r, a in enumerate(attn_args):
+        a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
+        a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        a.o, a.lse, a.status = o_parts[r].data_ptr(), lse_parts[r].data_ptr(), status.data_ptr()
+    refs = [ctypes.byref(a) for a in attn_args]
+    sh = stream.cuda_stream
+    rows = w.B * M
+    merge_call = (N, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
+
+    def step(events=None):
+        for r in range(N):
+            if events is not None:
+                events[r].record(stream)
+            rc = L.dcp_stripe_attn(refs[r], sh)
+            if rc != 0:
+                raise RuntimeError(f"dcp_stripe_attn: {dcp.strerror(rc)}")
+        if events is not None:
+            events[N].record(stream)
+        rc = L.dcp_lse_merge(*merge_call)
+        if rc != 0:
+            raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
+        if events is not None:
+            events[N + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_start
+
+    per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+    merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
+    step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
+    ms_per_step = wall_s * 1e3 / args.steps
+
+    # ---- algorithmic work
+    local = counts.astype(np.int64)                                  # rows per (request, rank)
+    kv_bytes = float(lens.sum()) * ROW_BYTES
+    q_bytes = w.B * M * ROW_BYTES
+    part_bytes = w.B * M * (512 + 1) * 4                               # one stripe's (o_r, lse_r)
+    vis = np.zeros(w.B)
+    for t in range(w.q_len):
+        vis += np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
+    flops = float((vis * w.H).sum()) * FLOP_PER_ROW_QUERY
+    kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    # dominant kernel: one stripe-attention launch (its algorithmic bytes: the
+    # stripe's latent rows, the queries, and its (o_r, lse_r))
+    stripe_bytes = local.sum(axis=0) * ROW_BYTES + q_bytes + part_bytes          # per rank
+    launch_ms = per_stripe_ms.mean(axis=0)                                        # per rank
+    achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if sample is not None:
+        from oracle import attention as OA
+        from oracle import layout as OL
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        t1 = time.perf_counter()
+        sample_bytes = 0.0
+        for qb, kvb, S in sample:
+            lists = OL.stripe_positions(S, N, I)
+            parts = [OA.stripe_attention(qb, kvb, S, lists[r], workloads.SCALE, chunk=65536) for r in range(N)]
+            OA.lse_merge(np.stack([p[0] for p in parts]), np.stack([OA.to_base(p[1], w.lse_base) for p in parts]),
+                         w.lse_base)
+            sample_bytes += S * ROW_BYTES
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+               "kind": "oracle", "seconds": round(cpu_s, 3),
+               "sample": f"{len(sample)} of {w.B} requests ({int(sum(s[2] for s in sample))} tokens, {w.H} heads, "
+                         f"q_len {w.q_len}): all {N} stripe attentions + LSE merge in float64 NumPy"}
+
+    out = {
+        "metric": "us/decode-step and KV GB/s (% HBM peak) for stripe attn+merge, K3 shape, 1 GPU",
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 1),
+        "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": int(lens.max()), "H": w.H, "q_len": w.q_len, "N": N,
+                   "interleave": I, "page_size": P, "lse_base": w.lse_base, "kv_bytes": int(kv_bytes),
+                   "launches_per_step": N + 1},
+        "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
+        "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
+        "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stripe_attn_kernel (one dcp_stripe_attn launch)",
+                     "bytes_per_launch": int(stripe_bytes.mean())},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,9 +30,17 @@
 //    N = 32 query rows, K = 16 tokens): P^T comes straight from the S^T
 //    accumulator registers (no data movement), V^T is read from the
 //    token-major LDS tile with ds_read_b64_tr_b16 transpose reads.
-//  * Split-KV: each split writes (o, lse) of its chunk; a combine pass merges
-//    them with the same exact LSE merge as across stripes.
-#include "merge_impl.h"
+//  * Split-KV: each split writes (o, lse) of its chunk; the last split of a
+//    (request, row group) to finish -- found with a device-scope arrival
+//    counter that it resets afterwards -- merges them with the same exact LSE
+//    merge as across stripes, while the partials are still in L2 (all splits
+//    of a request run on one XCD).
+#include "dcp_common.h"
+
+namespace dcp {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+}  // namespace dcp
 
 namespace dcp {
 namespace attn {
@@ -84,6 +92,7 @@ struct Params {
   float* lse;
   float* ws_o;                      // split partials [splits][B][M][512], lse2 [splits][B][M]
   float* ws_lse;
+  int32_t* counters;               // [B][mgroups] split arrival counters (zero between calls)
   int32_t* status;
 };
 
@@ -228,7 +237,9 @@ stripe_attn_kernel(Params p) {
       const int s = (k * W + wave) * 64 + lane;
       const int tt = s / kRowSlots;
       const int c = s - tt * kRowSlots;
-      const bool use = tt < rows_left && c < kChunks;   // rows_left <= 32 keeps s inside the tile
+      // slots past the 32-row tile (the last instruction's tail) and pad chunks
+      // load the zero row: never a row outside the tile
+      const bool use = s < kTileSlots && tt < rows_left && c < kChunks;
       const char* src = zero;
       if (kAligned) {
         if (use && tile_base != zero) src = tile_base + tt * kRowBytes + c * 16;
@@ -350,27 +361,74 @@ stripe_attn_kernel(Params p) {
   const float l_tot = l_run + other_half(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-  if (!valid) return;
   float* orow;
   if (p.splits == 1) orow = p.o + ((int64_t)b * p.M + R) * kDV;
   else orow = p.ws_o + (((int64_t)split * p.B + b) * p.M + R) * kDV;
+  if (valid) {
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb) {
+    for (int cb = 0; cb < kColBlocks; ++cb) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float4 v;
-      v.x = oacc[cb][4 * g4 + 0] * inv;
-      v.y = oacc[cb][4 * g4 + 1] * inv;
-      v.z = oacc[cb][4 * g4 + 2] * inv;
-      v.w = oacc[cb][4 * g4 + 3] * inv;
-      *reinterpret_cast<float4*>(orow + cb * 32 + 8 * g4 + 4 * half) = v;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float4 v;
+        v.x = oacc[cb][4 * g4 + 0] * inv;
+        v.y = oacc[cb][4 * g4 + 1] * inv;
+        v.z = oacc[cb][4 * g4 + 2] * inv;
+        v.w = oacc[cb][4 * g4 + 3] * inv;
+        *reinterpret_cast<float4*>(orow + cb * 32 + 8 * g4 + 4 * half) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (half == 0) {
+      if (p.splits == 1) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
+      else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
+    }
   }
-  if (half == 0) {
-    if (p.splits == 1) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
-    else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
+  if (p.splits == 1) return;
+
+  // ---- split-KV combine, done by the last split of (request, row group) to
+  // finish: the chunks of one stripe are a disjoint partition of its rows, so
+  // their partials merge exactly like stripes do.
+  __threadfence();                       // release this split's partial
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(smem);          // the tile ring is idle now
+  int32_t* counter = p.counters + (int64_t)b * p.mgroups + mg;
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(counter, 1);
+    *flag = (prev == p.splits - 1);
   }
+  __syncthreads();
+  if (*flag == 0) return;
+  __threadfence();                       // acquire the other splits' partials
+  const float to_out = p.out_base2 ? 1.0f : kLn2;
+  for (int i = 0; i < 32; ++i) {
+    const int Rr = mg * 32 * W + wave * 32 + i;
+    if (Rr >= p.M) break;
+    const int64_t rowi = (int64_t)b * p.M + Rr;
+    const int64_t stride = (int64_t)p.B * p.M;       // between splits
+    float m = -INFINITY;
+    for (int sp = 0; sp < p.splits; ++sp) m = fmaxf(m, p.ws_lse[sp * stride + rowi]);
+    float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      for (int sp = 0; sp < p.splits; ++sp) {
+        const float x = p.ws_lse[sp * stride + rowi];
+        if (x == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(x - m);
+        wsum += w;
+        const float4* src = reinterpret_cast<const float4*>(p.ws_o + (sp * stride + rowi) * kDV);
+        const float4 v0 = src[lane];
+        const float4 v1 = src[64 + lane];
+        acc0.x += w * v0.x; acc0.y += w * v0.y; acc0.z += w * v0.z; acc0.w += w * v0.w;
+        acc1.x += w * v1.x; acc1.y += w * v1.y; acc1.z += w * v1.z; acc1.w += w * v1.w;
+      }
+    }
+    const float winv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    float4* dst = reinterpret_cast<float4*>(p.o + rowi * kDV);
+    dst[lane] = make_float4(acc0.x * winv, acc0.y * winv, acc0.z * winv, acc0.w * winv);
+    dst[64 + lane] = make_float4(acc1.x * winv, acc1.y * winv, acc1.z * winv, acc1.w * winv);
+    if (lane == 0) p.lse[rowi] = wsum > 0.f ? (m + __builtin_amdgcn_logf(wsum)) * to_out : -INFINITY;
+  }
+  if (threadIdx.x == 0) *counter = 0;    // leave the counter ready for the next call
 }
 
 struct Plan {
@@ -411,7 +469,10 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   pl->split_rows = (int)(tiles_per_split * kTile);
   pl->splits = (int)splits;
   if ((int64_t)a->batch * pl->splits * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
-  pl->ws_bytes = pl->splits > 1 ? (size_t)pl->splits * a->batch * M * (kDV + 1) * sizeof(float) : 0;
+  // partials (o, lse) of every split, then one arrival counter per (request, row group)
+  pl->ws_bytes = pl->splits > 1 ? (size_t)pl->splits * a->batch * M * (kDV + 1) * sizeof(float) +
+                                      (size_t)a->batch * pl->mgroups * sizeof(int32_t)
+                                : 0;
   return DCP_OK;
 }
 
@@ -473,6 +534,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.lse = a->lse;
   prm.ws_o = pl.splits > 1 ? (float*)a->workspace : nullptr;
   prm.ws_lse = pl.splits > 1 ? prm.ws_o + (size_t)pl.splits * a->batch * M * kDV : nullptr;
+  prm.counters = pl.splits > 1 ? (int32_t*)(prm.ws_lse + (size_t)pl.splits * a->batch * M) : nullptr;
   prm.status = a->status;
   const int64_t blocks = (int64_t)a->batch * pl.splits * pl.mgroups;
   hipStream_t s = (hipStream_t)stream;
@@ -483,7 +545,5 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
     case 3: r = launch<3>(prm, blocks, s); break;
     default: r = launch<4>(prm, blocks, s); break;
   }
-  if (r != DCP_OK || pl.splits == 1) return r;
-  return launch_lse_merge(pl.splits, (int64_t)a->batch * M, kDV, prm.ws_o, prm.ws_lse, 1,
-                          a->lse_base, a->o, a->lse, s);
+  return r;
 }

@@ -60,7 +60,7 @@ class Setup:
 
 
 def make_setup(w: workloads.Workload, interleave: int = 1, lens=None, nan_fill: bool = True,
-               spare_pages: int = 3) -> Setup:
+               spare_pages: int = 0) -> Setup:
     dev = device()
     lens = workloads.seq_lens(w) if lens is None else np.asarray(lens, dtype=np.int64)
     N, P = w.N, w.page_size
