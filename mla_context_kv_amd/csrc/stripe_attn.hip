@@ -126,7 +126,8 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
 __device__ __forceinline__ void scale_acc(f32x16& acc, float sc) {
 #define DCP_SCALE1(i) "v_accvgpr_read_b32 %[t], %[a" #i "]\n\tv_mul_f32 %[t], %[t], %[s]\n\tv_accvgpr_write_b32 %[a" #i "], %[t]\n\t"
   float t;
-  asm volatile(DCP_SCALE1(0) DCP_SCALE1(1) DCP_SCALE1(2) DCP_SCALE1(3) DCP_SCALE1(4) DCP_SCALE1(5)
+  // leading pad: the accumulators may have just been written by an MFMA
+  asm volatile("s_nop 15\n\t" DCP_SCALE1(0) DCP_SCALE1(1) DCP_SCALE1(2) DCP_SCALE1(3) DCP_SCALE1(4) DCP_SCALE1(5)
                    DCP_SCALE1(6) DCP_SCALE1(7) DCP_SCALE1(8) DCP_SCALE1(9) DCP_SCALE1(10) DCP_SCALE1(11)
                        DCP_SCALE1(12) DCP_SCALE1(13) DCP_SCALE1(14) DCP_SCALE1(15)
                : [t] "=&v"(t), [a0] "+a"(acc[0]), [a1] "+a"(acc[1]), [a2] "+a"(acc[2]),
@@ -135,22 +136,8 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float sc) {
                  [a11] "+a"(acc[11]), [a12] "+a"(acc[12]), [a13] "+a"(acc[13]), [a14] "+a"(acc[14]),
                  [a15] "+a"(acc[15])
                : [s] "v"(sc));
+  asm volatile("s_nop 7" ::: "memory");   // before an MFMA reads the rewritten accumulators
 #undef DCP_SCALE1
-}
-
-// QK^T accumulation with the accumulator pinned to VGPRs (the 256 AGPRs hold
-// the output accumulators).  Dependent MFMAs on the same accumulator may issue
-// back to back; before VALU reads the result, qk_done() pads the wait states
-// the hardware requires after an 8-pass MFMA (with margin), tied to the
-// accumulator so no read can be scheduled above it.
-__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk_done(f32x16& acc) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc));
 }
 
 // Scalar (SMEM) read of a uniform 32-bit value: keeps page-table lookups off
@@ -165,6 +152,12 @@ __device__ __forceinline__ float other_half(float v) {
   // value of lane l ^ 32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
+// (the scalar-base form: no 64-bit per-lane address arithmetic).
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
 template <int W, bool kAligned>
@@ -214,39 +207,73 @@ stripe_attn_kernel(Params p) {
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const char* zero = reinterpret_cast<const char*>(g_zero_row);
+  const int32_t* bt_row = p.bt + (int64_t)b * p.bt_cols;
 
-  // Issue this wave's DMA loads of tile `it` into its ring stage.  Slots past
-  // the tile, pad chunks, rows past the split and tiles past ntiles all load
-  // the zero row, so every wave issues exactly kLoads loads per tile and the
-  // vmcnt arithmetic holds.
-  auto load_tile = [&](int it) {
+  // ---- page table of the split, one page id per lane, 64 pages at a time
+  // (page-aligned tiles only: a tile lies inside one page)
+  int32_t pt_base = kAligned ? row_lo / p.P : 0;
+  int32_t vpt = -1;
+  auto load_page_table = [&](int32_t base) {
+    pt_base = base;
+    const int32_t pi = base + lane;
+    vpt = pi < p.bt_cols ? bt_row[pi] : -1;
+    // Consume the loaded value right here, so the wait for this load happens
+    // on this (rare) path; otherwise the compiler waits for every outstanding
+    // vector-memory operation -- all in-flight tile loads -- at each later use.
+    asm volatile("" : "+v"(vpt));
+  };
+  if (kAligned) load_page_table(pt_base);
+  // base address of tile `it` (aligned path): its page, offset inside the page
+  auto tile_base_of = [&](int it) -> const char* {
+    const int32_t J = row_lo + it * kTile;
+    const int32_t pi = J / p.P;
+    if (pi - pt_base >= 64) load_page_table(pi);    // rare: long splits cross 64 pages
+    const int32_t pg = __builtin_amdgcn_readlane(vpt, pi - pt_base);
+    if (pg < 0 || pg >= p.num_pages) {
+      if (lane == 0) flag_range(p.status);
+      return nullptr;
+    }
+    return p.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
+  };
+
+  // A tile is "fast" when it is page-aligned and all 32 rows lie in the split:
+  // its 32 rows are 36,864 contiguous bytes, so slot s of the padded LDS tile
+  // (row s / 73, chunk s % 73) takes global chunk s - s / 73 of the tile; pad
+  // chunks and slots past the tile fetch a neighbouring chunk of the same tile,
+  // which is never read from LDS.
+  auto tile_is_fast = [&](int it) -> bool {
+    return kAligned && it < ntiles && row_hi - (row_lo + it * kTile) >= kTile;
+  };
+  auto fast_offset = [&](int k) -> uint32_t {
+    const uint32_t s = (uint32_t)((k * W + wave) * 64 + lane);
+    uint32_t g = s - ((s * 57457u) >> 22);          // s - floor(s / 73), exact for s < 4096
+    g = g < (uint32_t)(kTile * kChunks - 1) ? g : (uint32_t)(kTile * kChunks - 1);
+    return g * 16u;
+  };
+  // General loads: partial tiles, tiles past ntiles, and pages smaller than a
+  // tile.  Rows outside the split, pad chunks and slots past the tile load the
+  // zero row, so no stale or unowned row ever reaches the tile.
+  auto load_tile_general = [&](int it) {
     const int stage = it % S::kStages;
     const int32_t J = row_lo + it * kTile;
     const bool live = it < ntiles;
-    const int32_t rows_left = live ? row_hi - J : 0;   // rows of this tile inside the split
-    const char* tile_base = zero;
-    if (kAligned && live) {
-      const int32_t pi = J / p.P;
-      const int32_t pg = pi < p.bt_cols ? scalar_load(p.bt + (int64_t)b * p.bt_cols + pi) : -1;
-      if (pg >= 0 && pg < p.num_pages) tile_base = p.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
-      else if (lane == 0) flag_range(p.status);
-    }
+    const int32_t rows_left = live ? row_hi - J : 0;
+    const char* tb = nullptr;
+    if (kAligned && live) tb = tile_base_of(it);
     const uint32_t lds_stage = lds0 + stage * S::kStageBytes;
 #pragma unroll 1
     for (int k = 0; k < S::kLoads; ++k) {
       const int s = (k * W + wave) * 64 + lane;
       const int tt = s / kRowSlots;
       const int c = s - tt * kRowSlots;
-      // slots past the 32-row tile (the last instruction's tail) and pad chunks
-      // load the zero row: never a row outside the tile
       const bool use = s < kTileSlots && tt < rows_left && c < kChunks;
       const char* src = zero;
       if (kAligned) {
-        if (use && tile_base != zero) src = tile_base + tt * kRowBytes + c * 16;
+        if (use && tb) src = tb + tt * kRowBytes + c * 16;
       } else if (use) {
         const int32_t j = J + tt;
         const int32_t pi = j / p.P;
-        const int32_t pg = pi < p.bt_cols ? p.bt[(int64_t)b * p.bt_cols + pi] : -1;
+        const int32_t pg = pi < p.bt_cols ? bt_row[pi] : -1;
         if (pg >= 0 && pg < p.num_pages) src = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes + c * 16;
         else flag_range(p.status);
       }
@@ -265,54 +292,75 @@ stripe_attn_kernel(Params p) {
   const int kq_off = (tau(n) * kRowSlots + half) * 16;          // + 32*ks
   const int g = lane >> 4, jl = lane & 15;
   const int v_off = ((4 * (jl >> 2) + (g >> 1)) * kRowSlots + 2 * (g & 1) + ((jl & 3) >> 1)) * 16 + (jl & 1) * 8;
+  // tile-relative token of each of this lane's S^T registers (for masking)
+  auto tok_of = [&](int i) { return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half; };
 
+  // ---- prologue: tiles 0 .. S-2 in flight, S^T of tile 0
 #pragma unroll 1
-  for (int it = 0; it < S::kStages - 1; ++it) load_tile(it);
+  for (int it = 0; it < S::kStages - 1; ++it) {
+    if (tile_is_fast(it)) {
+      const char* tb = tile_base_of(it);
+      const uint32_t lds_stage = lds0 + (it % S::kStages) * S::kStageBytes;
+      if (tb) {
+#pragma unroll 1
+        for (int k = 0; k < S::kLoads; ++k)
+          dma16_sbase(tb, fast_offset(k), lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
+      } else {
+        load_tile_general(it);
+      }
+    } else {
+      load_tile_general(it);
+    }
+  }
+  const float c2 = p.c2;
 
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
-    wait_vm_then_barrier<S::kWaitLoads>();
-    load_tile(it + S::kStages - 1);
+    // Tile it is in LDS and every wave is done with tile it-1, whose stage
+    // now receives tile it+S-1.
+    wait_vm_then_barrier<(S::kStages - 2) * S::kLoads>();
+    const int nt = it + S::kStages - 1;
+    const bool fast = tile_is_fast(nt);
+    const char* ntb = fast ? tile_base_of(nt) : nullptr;
+    if (!fast || ntb == nullptr) load_tile_general(nt);
+    const bool dma_in_pv = fast && ntb != nullptr;
+    const uint32_t nlds = lds0 + (nt % S::kStages) * S::kStageBytes;
     const char* st = smem + (it % S::kStages) * S::kStageBytes;
     const int32_t J = row_lo + it * kTile;
 
-    // S^T = K Q^T over the 576 latent dims; K fragments read two steps ahead
-    f32x16 sacc;
+    // -- S^T = K Q^T over the 576 latent dims (K fragments read 3 steps ahead)
+    f32x16 sacc = f32x16{};
     {
       const char* kb = st + kq_off;
       bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb);
       bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + 32);
+      bf16x8 a2 = *reinterpret_cast<const bf16x8*>(kb + 64);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        bf16x8 a2 = a1;
-        if (ks + 2 < kKSteps) a2 = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + 2));
-        if (ks == 0) mfma_qk_first(sacc, a0, qf[0]);
-        else mfma_qk(sacc, a0, qf[ks]);
+        bf16x8 a3 = a2;
+        if (ks + 3 < kKSteps) a3 = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + 3));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sacc, 0, 0, 0);
         a0 = a1;
         a1 = a2;
+        a2 = a3;
         __builtin_amdgcn_sched_barrier(0);
       }
-      qk_done(sacc);
     }
 
-    // online softmax (base 2); masking only on tiles that cross a limit
-    const bool full = (J + kTile) <= lim;
-    if (__builtin_amdgcn_ballot_w64(!full) == 0) {
+    // -- online softmax in base 2.  Scores are masked only on tiles that
+    // cross a row's visible limit; the row max is taken on the raw scores
+    // (the scale is positive) and each weight costs one FMA and one exp2.
+    const int32_t vis = lim - J;                       // visible rows of this tile
+    if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] *= p.c2;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half;
-        sacc[i] = (J + tok < lim) ? sacc[i] * p.c2 : -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
     }
-    float mx = sacc[0];
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = fmaxf(mx, other_half(mx));
+    for (int i = 3; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), i + 1 < 16 ? sacc[i + 1] : -INFINITY);
+    mx = fmaxf(mx, other_half(mx)) * c2;               // tile max in base-2 units
     const float m_new = fmaxf(m_run, mx);
-    const bool move = m_new > m_run + 8.0f;
+    const bool move = m_new > m_run + 8.0f;             // move the reference only on a large jump
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
 #pragma unroll
@@ -320,18 +368,19 @@ stripe_attn_kernel(Params p) {
       l_run *= alpha;
       if (move) m_run = m_new;
     }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     bf16x8 pk[2];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(sacc[i] - mref);
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, neg_m));
       psum += e;
       pk[i >> 3][i & 7] = (__bf16)e;
     }
     l_run += psum;
 
-    // O^T += V^T P^T; V^T fragments by transpose reads, one step ahead
+    // -- O^T += V^T P^T (V^T fragments by transpose reads, 3 steps ahead),
+    // with the loads of tile it+S-1 slotted under the MFMAs
     {
       const char* vb = st + v_off;
       auto vfrag = [&](int step) {
@@ -343,15 +392,24 @@ stripe_attn_kernel(Params p) {
       };
       bf16x8 v0 = vfrag(0);
       bf16x8 v1 = vfrag(1);
+      bf16x8 v2 = vfrag(2);
 #pragma unroll
       for (int step = 0; step < 2 * kColBlocks; ++step) {
-        bf16x8 v2 = v1;
-        if (step + 2 < 2 * kColBlocks) v2 = vfrag(step + 2);
+        bf16x8 v3 = v2;
+        if (step + 3 < 2 * kColBlocks) v3 = vfrag(step + 3);
         oacc[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pk[step & 1], oacc[step >> 1], 0, 0, 0);
         v0 = v1;
         v1 = v2;
+        v2 = v3;
+        if (step < S::kLoads && dma_in_pv)
+          dma16_sbase(ntb, fast_offset(step), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((step * W + wave) * 1024));
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the rest of the tile's loads when a wave issues more loads than PV steps
+#pragma unroll 1
+      for (int k = 2 * kColBlocks; k < S::kLoads; ++k)
+        if (dma_in_pv)
+          dma16_sbase(ntb, fast_offset(k), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
     }
   }
   // drain the remaining (zero-row) loads before the workgroup's LDS is released

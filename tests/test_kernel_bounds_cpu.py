@@ -80,6 +80,18 @@ def check_workload(w, I, guard_tile=True, num_splits=0):
                         continue                       # dead tiles load only the zero row
                     J = row_lo + it * TILE
                     rows_left = row_hi - J
+                    if P % TILE == 0 and rows_left >= TILE and guard_tile:
+                        # fast path: slot s takes chunk min(s - s//73, 2303) of the
+                        # 36,864 contiguous bytes of the tile's 32 rows
+                        loads, _ = shape(W)
+                        s_ = np.arange(loads * 64 * W)
+                        g = np.minimum(s_ - (s_ * 57457 >> 22), TILE * CHUNKS - 1)
+                        assert ((s_ * 57457 >> 22) == s_ // 73).all()
+                        assert g.min() >= 0 and g.max() < TILE * CHUNKS
+                        pi = J // P
+                        assert pi < cols and 0 <= tab[b, pi] < pool_pages
+                        assert J % P + TILE <= P          # the tile's rows lie inside its page
+                        continue
                     use = base_ok & (tt < rows_left)
                     if not use.any():
                         continue
