@@ -157,14 +157,23 @@ __device__ __forceinline__ float other_half(float v) {
 // 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
 // (the scalar-base form: no 64-bit per-lane address arithmetic).
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr) : "memory");
+  // the base is wave-uniform by construction; say so, so that it always lands
+  // in an SGPR pair (free when the compiler already knows)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
 }
+
+// The split combine keeps 32W rows x splits merge weights in the idle tile ring.
+constexpr int kMaxSplits = 256;
 
 template <int W, bool kAligned>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(1, 1)))
 stripe_attn_kernel(Params p) {
   using S = Shape<W>;
   __shared__ __align__(16) char smem[S::kLdsBytes];
+  static_assert(64 + 32 * W * kMaxSplits * 4 <= S::kLdsBytes, "combine weights fit in LDS");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -457,34 +466,62 @@ stripe_attn_kernel(Params p) {
   __syncthreads();
   if (*flag == 0) return;
   __threadfence();                       // acquire the other splits' partials
+  // The whole workgroup merges: first one thread per row turns the splits'
+  // lse into normalised weights (kept in LDS, idle now), then every thread
+  // merges float4 column slices with several independent loads in flight.
+  const int rows_g = min(32 * W, p.M - mg * 32 * W);
+  const int64_t stride = (int64_t)p.B * p.M;          // between splits
+  const int64_t row0 = (int64_t)b * p.M + mg * 32 * W;
+  float* wts = reinterpret_cast<float*>(smem) + 16;   // [rows_g][splits]
   const float to_out = p.out_base2 ? 1.0f : kLn2;
-  for (int i = 0; i < 32; ++i) {
-    const int Rr = mg * 32 * W + wave * 32 + i;
-    if (Rr >= p.M) break;
-    const int64_t rowi = (int64_t)b * p.M + Rr;
-    const int64_t stride = (int64_t)p.B * p.M;       // between splits
+  for (int r = threadIdx.x; r < rows_g; r += blockDim.x) {
+    const int64_t rowi = row0 + r;
     float m = -INFINITY;
     for (int sp = 0; sp < p.splits; ++sp) m = fmaxf(m, p.ws_lse[sp * stride + rowi]);
-    float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
     float wsum = 0.f;
-    if (m != -INFINITY) {
-      for (int sp = 0; sp < p.splits; ++sp) {
-        const float x = p.ws_lse[sp * stride + rowi];
-        if (x == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(x - m);
-        wsum += w;
-        const float4* src = reinterpret_cast<const float4*>(p.ws_o + (sp * stride + rowi) * kDV);
-        const float4 v0 = src[lane];
-        const float4 v1 = src[64 + lane];
-        acc0.x += w * v0.x; acc0.y += w * v0.y; acc0.z += w * v0.z; acc0.w += w * v0.w;
-        acc1.x += w * v1.x; acc1.y += w * v1.y; acc1.z += w * v1.z; acc1.w += w * v1.w;
-      }
+    for (int sp = 0; sp < p.splits; ++sp) {
+      const float x = p.ws_lse[sp * stride + rowi];
+      const float w = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m);
+      wts[r * p.splits + sp] = w;
+      wsum += w;
     }
     const float winv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    float4* dst = reinterpret_cast<float4*>(p.o + rowi * kDV);
-    dst[lane] = make_float4(acc0.x * winv, acc0.y * winv, acc0.z * winv, acc0.w * winv);
-    dst[64 + lane] = make_float4(acc1.x * winv, acc1.y * winv, acc1.z * winv, acc1.w * winv);
-    if (lane == 0) p.lse[rowi] = wsum > 0.f ? (m + __builtin_amdgcn_logf(wsum)) * to_out : -INFINITY;
+    for (int sp = 0; sp < p.splits; ++sp) wts[r * p.splits + sp] *= winv;
+    p.lse[rowi] = wsum > 0.f ? (m + __builtin_amdgcn_logf(wsum)) * to_out : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int kU = 4;                                // float4 items per thread per round
+  const int items = rows_g * (kDV / 4);
+  for (int base = threadIdx.x; base < items; base += kU * 64 * W) {
+    float4 acc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < p.splits; ++sp) {
+      float4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int idx = base + u * 64 * W;
+        const int r = idx < items ? idx / (kDV / 4) : 0;
+        const int c4 = idx < items ? idx % (kDV / 4) : 0;
+        v[u] = reinterpret_cast<const float4*>(p.ws_o + (sp * stride + row0 + r) * kDV)[c4];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int idx = base + u * 64 * W;
+        const int r = idx < items ? idx / (kDV / 4) : 0;
+        const float w = wts[r * p.splits + sp];
+        acc[u].x += w * v[u].x;
+        acc[u].y += w * v[u].y;
+        acc[u].z += w * v[u].z;
+        acc[u].w += w * v[u].w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = base + u * 64 * W;
+      if (idx < items)
+        reinterpret_cast<float4*>(p.o + (row0 + idx / (kDV / 4)) * kDV)[idx % (kDV / 4)] = acc[u];
+    }
   }
   if (threadIdx.x == 0) *counter = 0;    // leave the counter ready for the next call
 }
@@ -521,6 +558,7 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
     splits = ceil_div(cus, base);
   }
   if (splits > tiles_max) splits = tiles_max;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
   const int64_t tiles_per_split = ceil_div(tiles_max, splits);
   splits = ceil_div(tiles_max, tiles_per_split);
