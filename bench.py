@@ -109,7 +109,7 @@ def main():
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
         attn_args.append(a)
-    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     for r, a in enumerate(attn_args):
         a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()

@@ -141,11 +141,8 @@ int dcp_kv_write(dcp_layout layout, int32_t rank,
  * workspace, workspace_bytes  device scratch of at least the size
  *             dcp_stripe_attn_workspace() reports for these arguments (0 when
  *             one KV split per request is used).  It holds the splits'
- *             partial (o, lse) and, at its end, one int32 arrival counter per
- *             (request, group of up to 128 query rows).  The counters must be
- *             zero before the first call that uses this workspace (e.g.
- *             allocate it zero-filled); every call leaves them zero again, so
- *             a workspace can be reused by later calls on the same stream.
+ *             partial (o, lse), which a second kernel on the same stream
+ *             merges into o and lse; its contents need no initialisation.
  *             Calls that overlap in time must not share a workspace.
  * o    [B][q_len][H][v_dim] fp32 device out: o_r, normalised inside the stripe.
  * lse  [B][q_len][H] fp32 device out: lse_r in the chosen base.

@@ -11,7 +11,7 @@
 // their o is never read; if all parts are empty, o = 0 and lse = -inf.
 //
 // HBM-bound: per row it reads N lse values and N*v_dim floats once and
-// writes v_dim + 1 floats.  One wavefront per row, 16-byte coalesced accesses.
+// writes v_dim + 1 floats, with 16-byte coalesced accesses.
 #pragma once
 
 #include "dcp_common.h"
@@ -23,51 +23,93 @@ constexpr int kMergeRowsPerBlock = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at lse_parts[r * rows + i].
-// in_base2 / out_base2 select the base of the input and output lse.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at
+// lse_parts[r * rows + i].  in_base2 / out_base2 select the base of the input
+// and output lse.  One wavefront per row: the lanes first hold the parts' lse
+// (64 parts at a time) for the max and the weight sum, then every lane merges
+// two 16-byte column slices, with the loads of 8 parts in flight before their
+// FMAs.  Parts of weight zero (lse = -inf, or an underflowed weight) are never
+// read.
 __global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
 lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__ o_parts,
                  const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
                  float4* __restrict__ o, float* __restrict__ lse) {
-  const int64_t r0 = (int64_t)blockIdx.x * kMergeRowsPerBlock + threadIdx.x / 64;
+  const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + threadIdx.x / 64;
   const int lane = threadIdx.x & 63;
-  if (r0 >= rows) return;
+  if (row >= rows) return;
   // weights are base^(lse_r - m): the difference is taken in the input base
   // (exact for nearby values) and only then scaled into base 2 for exp2
   const float to2 = in_base2 ? 1.0f : kLog2e;
   float m = -INFINITY;
-  for (int r = 0; r < N; ++r) m = fmaxf(m, lse_parts[(int64_t)r * rows + r0]);
+  for (int r0 = 0; r0 < N; r0 += 64)
+    if (r0 + lane < N) m = fmaxf(m, lse_parts[(int64_t)(r0 + lane) * rows + row]);
+  m = wave_max(m);
   if (m == -INFINITY) {
-    for (int c = lane; c < v4; c += 64) o[r0 * v4 + c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse && lane == 0) lse[r0] = -INFINITY;
+    for (int c = lane; c < v4; c += 64) o[row * v4 + c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse && lane == 0) lse[row] = -INFINITY;
     return;
   }
   float wsum = 0.f;
-  for (int r = 0; r < N; ++r) {
-    const float x = lse_parts[(int64_t)r * rows + r0];
-    if (x == -INFINITY) continue;
-    wsum += exp2f((x - m) * to2);
+  for (int r0 = 0; r0 < N; r0 += 64) {
+    const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * rows + row] : -INFINITY;
+    wsum += x == -INFINITY ? 0.f : exp2f((x - m) * to2);
   }
+  wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
-  for (int c = lane; c < v4; c += 64) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int r = 0; r < N; ++r) {
-      const float x = lse_parts[(int64_t)r * rows + r0];
-      if (x == -INFINITY) continue;
-      const float w = exp2f((x - m) * to2) * inv;
-      const float4 v = o_parts[((int64_t)r * rows + r0) * v4 + c];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+  for (int cb = 0; cb < v4; cb += 128) {
+    const int c0 = cb + lane, c1 = cb + 64 + lane;
+    const bool in0 = c0 < v4, in1 = c1 < v4;
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    for (int r0 = 0; r0 < N; r0 += 64) {
+      const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * rows + row] : -INFINITY;
+      const float w = x == -INFINITY ? 0.f : exp2f((x - m) * to2) * inv;   // lane k: weight of part r0 + k
+      const int nr = min(64, N - r0);
+      for (int u = 0; u < nr; u += 8) {
+        float wu[8];
+        float4 v0[8], v1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          wu[k] = u + k < nr ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + k)) : 0.f;
+          v0[k] = v1[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (wu[k] != 0.f) {
+            const float4* src = o_parts + ((int64_t)(r0 + u + k) * rows + row) * v4;
+            if (in0) v0[k] = src[c0];
+            if (in1) v1[k] = src[c1];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          a0.x += wu[k] * v0[k].x;
+          a0.y += wu[k] * v0[k].y;
+          a0.z += wu[k] * v0[k].z;
+          a0.w += wu[k] * v0[k].w;
+          a1.x += wu[k] * v1[k].x;
+          a1.y += wu[k] * v1[k].y;
+          a1.z += wu[k] * v1[k].z;
+          a1.w += wu[k] * v1[k].w;
+        }
+      }
     }
-    o[r0 * v4 + c] = acc;
+    if (in0) o[row * v4 + c0] = a0;
+    if (in1) o[row * v4 + c1] = a1;
   }
   if (lse && lane == 0) {
     // lse = m + log_base(sum w), written in the output base
     const float lw2 = log2f(wsum);                          // log2 of the weight sum
     const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
-    lse[r0] = m_out + (out_base2 ? lw2 : lw2 * kLn2);
+    lse[row] = m_out + (out_base2 ? lw2 : lw2 * kLn2);
   }
 }
 

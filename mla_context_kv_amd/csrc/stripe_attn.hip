@@ -30,17 +30,13 @@
 //    N = 32 query rows, K = 16 tokens): P^T comes straight from the S^T
 //    accumulator registers (no data movement), V^T is read from the
 //    token-major LDS tile with ds_read_b64_tr_b16 transpose reads.
-//  * Split-KV: each split writes (o, lse) of its chunk; the last split of a
-//    (request, row group) to finish -- found with a device-scope arrival
-//    counter that it resets afterwards -- merges them with the same exact LSE
-//    merge as across stripes, while the partials are still in L2 (all splits
-//    of a request run on one XCD).
+//  * Split-KV: when there are fewer (request, row group) items than compute
+//    units, each request's stripe is cut into equal chunks of whole tiles; a
+//    chunk writes its (o, lse) partial to the workspace and a second launch
+//    merges the chunks with the same exact LSE merge as across stripes (the
+//    chunks are a disjoint partition of the stripe's rows).
 #include "dcp_common.h"
-
-namespace dcp {
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-}  // namespace dcp
+#include "merge_impl.h"
 
 namespace dcp {
 namespace attn {
@@ -54,6 +50,16 @@ constexpr int kTileSlots = kTile * kRowSlots;  // 2336
 constexpr int kKSteps = kD / 16;        // 36 MFMA k-steps for QK^T
 constexpr int kColBlocks = kDV / 32;    // 16 value-column blocks
 constexpr int kRowBytes = kD * 2;       // 1152
+// LDS operand prefetch depth (MFMA steps) of the QK^T and PV chains
+#ifndef DCP_QK_AHEAD
+#define DCP_QK_AHEAD 3
+#endif
+#ifndef DCP_PV_AHEAD
+#define DCP_PV_AHEAD 3
+#endif
+constexpr int kQkAhead = DCP_QK_AHEAD;
+constexpr int kPvAhead = DCP_PV_AHEAD;
+static_assert(kQkAhead >= 1 && kQkAhead <= 15 && kPvAhead >= 1 && kPvAhead <= 7, "LDS counter range");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -72,8 +78,9 @@ struct Shape {
   static_assert(kWaitLoads <= 63, "vmcnt range");
 };
 
-// A zero latent row (plus pad chunk): the source of every tile slot that holds
-// no token of this split, so padding never injects NaN or stale data.
+// A zero latent row (plus pad chunk): what a tile slot holds when its page id
+// is out of range (the call also flags DCP_ERANGE), so a bad table never
+// makes the kernel read outside the pool.
 __device__ __align__(16) uint4 g_zero_row[kRowSlots];
 
 struct Params {
@@ -92,7 +99,6 @@ struct Params {
   float* lse;
   float* ws_o;                      // split partials [splits][B][M][512], lse2 [splits][B][M]
   float* ws_lse;
-  int32_t* counters;               // [B][mgroups] split arrival counters (zero between calls)
   int32_t* status;
 };
 
@@ -118,6 +124,17 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 template <int N>
 __device__ __forceinline__ void wait_vm_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait until only the loads of the `after` most recent tiles (each kLoads
+// per wave) are in flight, then barrier.  Tiles past the split issue no loads,
+// so near the end fewer tiles are in flight and the count drops with them.
+template <int kMaxAfter, int kLoads>
+__device__ __forceinline__ void wait_tiles_then_barrier(int after) {
+  static_assert(kMaxAfter == 1 || kMaxAfter == 2, "ring depth");
+  if (after >= kMaxAfter) wait_vm_then_barrier<kMaxAfter * kLoads>();
+  else if (kMaxAfter == 2 && after == 1) wait_vm_then_barrier<kLoads>();
+  else wait_vm_then_barrier<0>();
 }
 
 // acc *= s for one 32x32 accumulator tile that lives in AGPRs: each element is
@@ -165,7 +182,7 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
 }
 
-// The split combine keeps 32W rows x splits merge weights in the idle tile ring.
+// Upper bound on KV chunks per request (each adds one partial to the workspace).
 constexpr int kMaxSplits = 256;
 
 template <int W, bool kAligned>
@@ -173,7 +190,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdg
 stripe_attn_kernel(Params p) {
   using S = Shape<W>;
   __shared__ __align__(16) char smem[S::kLdsBytes];
-  static_assert(64 + 32 * W * kMaxSplits * 4 <= S::kLdsBytes, "combine weights fit in LDS");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -259,27 +275,29 @@ stripe_attn_kernel(Params p) {
     g = g < (uint32_t)(kTile * kChunks - 1) ? g : (uint32_t)(kTile * kChunks - 1);
     return g * 16u;
   };
-  // General loads: partial tiles, tiles past ntiles, and pages smaller than a
-  // tile.  Rows outside the split, pad chunks and slots past the tile load the
-  // zero row, so no stale or unowned row ever reaches the tile.
+  // General loads (live tiles only): partial tiles and pages smaller than a
+  // tile.  A slot that holds no token of the split (rows past the split end,
+  // the pad chunk, slots past the tile) loads a chunk of the tile's first
+  // row instead: finite data that the softmax masks to weight zero (or that
+  // is never read), so no stale, unowned or NaN row reaches the MFMAs.
   auto load_tile_general = [&](int it) {
     const int stage = it % S::kStages;
     const int32_t J = row_lo + it * kTile;
-    const bool live = it < ntiles;
-    const int32_t rows_left = live ? row_hi - J : 0;
+    const int32_t rows_left = row_hi - J;          // >= 1 for a live tile
     const char* tb = nullptr;
-    if (kAligned && live) tb = tile_base_of(it);
+    if (kAligned) tb = tile_base_of(it);
     const uint32_t lds_stage = lds0 + stage * S::kStageBytes;
 #pragma unroll 1
     for (int k = 0; k < S::kLoads; ++k) {
       const int s = (k * W + wave) * 64 + lane;
-      const int tt = s / kRowSlots;
-      const int c = s - tt * kRowSlots;
-      const bool use = s < kTileSlots && tt < rows_left && c < kChunks;
+      int tt = s / kRowSlots;
+      int c = s - tt * kRowSlots;
+      if (!(s < kTileSlots && tt < rows_left)) tt = 0;
+      c = c < kChunks ? c : kChunks - 1;
       const char* src = zero;
       if (kAligned) {
-        if (use && tb) src = tb + tt * kRowBytes + c * 16;
-      } else if (use) {
+        if (tb) src = tb + tt * kRowBytes + c * 16;
+      } else {
         const int32_t j = J + tt;
         const int32_t pi = j / p.P;
         const int32_t pg = pi < p.bt_cols ? bt_row[pi] : -1;
@@ -306,7 +324,7 @@ stripe_attn_kernel(Params p) {
 
   // ---- prologue: tiles 0 .. S-2 in flight, S^T of tile 0
 #pragma unroll 1
-  for (int it = 0; it < S::kStages - 1; ++it) {
+  for (int it = 0; it < S::kStages - 1 && it < ntiles; ++it) {
     if (tile_is_fast(it)) {
       const char* tb = tile_base_of(it);
       const uint32_t lds_stage = lds0 + (it % S::kStages) * S::kStageBytes;
@@ -327,31 +345,28 @@ stripe_attn_kernel(Params p) {
   for (int it = 0; it < ntiles; ++it) {
     // Tile it is in LDS and every wave is done with tile it-1, whose stage
     // now receives tile it+S-1.
-    wait_vm_then_barrier<(S::kStages - 2) * S::kLoads>();
+    const int after = ntiles - 1 - it;                 // live tiles after this one
+    wait_tiles_then_barrier<S::kStages - 2, S::kLoads>(after);
     const int nt = it + S::kStages - 1;
     const bool fast = tile_is_fast(nt);
     const char* ntb = fast ? tile_base_of(nt) : nullptr;
-    if (!fast || ntb == nullptr) load_tile_general(nt);
+    if (nt < ntiles && (!fast || ntb == nullptr)) load_tile_general(nt);
     const bool dma_in_pv = fast && ntb != nullptr;
     const uint32_t nlds = lds0 + (nt % S::kStages) * S::kStageBytes;
     const char* st = smem + (it % S::kStages) * S::kStageBytes;
     const int32_t J = row_lo + it * kTile;
 
-    // -- S^T = K Q^T over the 576 latent dims (K fragments read 3 steps ahead)
+    // -- S^T = K Q^T over the 576 latent dims (K fragments read kQkAhead steps ahead)
     f32x16 sacc = f32x16{};
     {
       const char* kb = st + kq_off;
-      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb);
-      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + 32);
-      bf16x8 a2 = *reinterpret_cast<const bf16x8*>(kb + 64);
+      bf16x8 kf[kKSteps];
+#pragma unroll
+      for (int ks = 0; ks < kQkAhead; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + 32 * ks);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        bf16x8 a3 = a2;
-        if (ks + 3 < kKSteps) a3 = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + 3));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sacc, 0, 0, 0);
-        a0 = a1;
-        a1 = a2;
-        a2 = a3;
+        if (ks + kQkAhead < kKSteps) kf[ks + kQkAhead] = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + kQkAhead));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -388,7 +403,7 @@ stripe_attn_kernel(Params p) {
     }
     l_run += psum;
 
-    // -- O^T += V^T P^T (V^T fragments by transpose reads, 3 steps ahead),
+    // -- O^T += V^T P^T (V^T fragments by transpose reads, kPvAhead steps ahead),
     // with the loads of tile it+S-1 slotted under the MFMAs
     {
       const char* vb = st + v_off;
@@ -399,17 +414,13 @@ stripe_attn_kernel(Params p) {
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 2 * kRowSlots * 16));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8 v0 = vfrag(0);
-      bf16x8 v1 = vfrag(1);
-      bf16x8 v2 = vfrag(2);
+      bf16x8 vf[2 * kColBlocks];
+#pragma unroll
+      for (int step = 0; step < kPvAhead; ++step) vf[step] = vfrag(step);
 #pragma unroll
       for (int step = 0; step < 2 * kColBlocks; ++step) {
-        bf16x8 v3 = v2;
-        if (step + 3 < 2 * kColBlocks) v3 = vfrag(step + 3);
-        oacc[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pk[step & 1], oacc[step >> 1], 0, 0, 0);
-        v0 = v1;
-        v1 = v2;
-        v2 = v3;
+        if (step + kPvAhead < 2 * kColBlocks) vf[step + kPvAhead] = vfrag(step + kPvAhead);
+        oacc[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], pk[step & 1], oacc[step >> 1], 0, 0, 0);
         if (step < S::kLoads && dma_in_pv)
           dma16_sbase(ntb, fast_offset(step), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((step * W + wave) * 1024));
         __builtin_amdgcn_sched_barrier(0);
@@ -421,7 +432,7 @@ stripe_attn_kernel(Params p) {
           dma16_sbase(ntb, fast_offset(k), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
     }
   }
-  // drain the remaining (zero-row) loads before the workgroup's LDS is released
+  // every load has landed by now; make that explicit before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: normalise and store this row's (o, lse)
@@ -450,80 +461,6 @@ stripe_attn_kernel(Params p) {
       else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
     }
   }
-  if (p.splits == 1) return;
-
-  // ---- split-KV combine, done by the last split of (request, row group) to
-  // finish: the chunks of one stripe are a disjoint partition of its rows, so
-  // their partials merge exactly like stripes do.
-  __threadfence();                       // release this split's partial
-  __syncthreads();
-  int* flag = reinterpret_cast<int*>(smem);          // the tile ring is idle now
-  int32_t* counter = p.counters + (int64_t)b * p.mgroups + mg;
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(counter, 1);
-    *flag = (prev == p.splits - 1);
-  }
-  __syncthreads();
-  if (*flag == 0) return;
-  __threadfence();                       // acquire the other splits' partials
-  // The whole workgroup merges: first one thread per row turns the splits'
-  // lse into normalised weights (kept in LDS, idle now), then every thread
-  // merges float4 column slices with several independent loads in flight.
-  const int rows_g = min(32 * W, p.M - mg * 32 * W);
-  const int64_t stride = (int64_t)p.B * p.M;          // between splits
-  const int64_t row0 = (int64_t)b * p.M + mg * 32 * W;
-  float* wts = reinterpret_cast<float*>(smem) + 16;   // [rows_g][splits]
-  const float to_out = p.out_base2 ? 1.0f : kLn2;
-  for (int r = threadIdx.x; r < rows_g; r += blockDim.x) {
-    const int64_t rowi = row0 + r;
-    float m = -INFINITY;
-    for (int sp = 0; sp < p.splits; ++sp) m = fmaxf(m, p.ws_lse[sp * stride + rowi]);
-    float wsum = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const float x = p.ws_lse[sp * stride + rowi];
-      const float w = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m);
-      wts[r * p.splits + sp] = w;
-      wsum += w;
-    }
-    const float winv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) wts[r * p.splits + sp] *= winv;
-    p.lse[rowi] = wsum > 0.f ? (m + __builtin_amdgcn_logf(wsum)) * to_out : -INFINITY;
-  }
-  __syncthreads();
-  constexpr int kU = 4;                                // float4 items per thread per round
-  const int items = rows_g * (kDV / 4);
-  for (int base = threadIdx.x; base < items; base += kU * 64 * W) {
-    float4 acc[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < p.splits; ++sp) {
-      float4 v[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int idx = base + u * 64 * W;
-        const int r = idx < items ? idx / (kDV / 4) : 0;
-        const int c4 = idx < items ? idx % (kDV / 4) : 0;
-        v[u] = reinterpret_cast<const float4*>(p.ws_o + (sp * stride + row0 + r) * kDV)[c4];
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int idx = base + u * 64 * W;
-        const int r = idx < items ? idx / (kDV / 4) : 0;
-        const float w = wts[r * p.splits + sp];
-        acc[u].x += w * v[u].x;
-        acc[u].y += w * v[u].y;
-        acc[u].z += w * v[u].z;
-        acc[u].w += w * v[u].w;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int idx = base + u * 64 * W;
-      if (idx < items)
-        reinterpret_cast<float4*>(p.o + (row0 + idx / (kDV / 4)) * kDV)[idx % (kDV / 4)] = acc[u];
-    }
-  }
-  if (threadIdx.x == 0) *counter = 0;    // leave the counter ready for the next call
 }
 
 struct Plan {
@@ -565,10 +502,8 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   pl->split_rows = (int)(tiles_per_split * kTile);
   pl->splits = (int)splits;
   if ((int64_t)a->batch * pl->splits * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
-  // partials (o, lse) of every split, then one arrival counter per (request, row group)
-  pl->ws_bytes = pl->splits > 1 ? (size_t)pl->splits * a->batch * M * (kDV + 1) * sizeof(float) +
-                                      (size_t)a->batch * pl->mgroups * sizeof(int32_t)
-                                : 0;
+  // partials (o, lse) of every split
+  pl->ws_bytes = pl->splits > 1 ? (size_t)pl->splits * a->batch * M * (kDV + 1) * sizeof(float) : 0;
   return DCP_OK;
 }
 
@@ -630,7 +565,6 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.lse = a->lse;
   prm.ws_o = pl.splits > 1 ? (float*)a->workspace : nullptr;
   prm.ws_lse = pl.splits > 1 ? prm.ws_o + (size_t)pl.splits * a->batch * M * kDV : nullptr;
-  prm.counters = pl.splits > 1 ? (int32_t*)(prm.ws_lse + (size_t)pl.splits * a->batch * M) : nullptr;
   prm.status = a->status;
   const int64_t blocks = (int64_t)a->batch * pl.splits * pl.mgroups;
   hipStream_t s = (hipStream_t)stream;
@@ -641,5 +575,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
     case 3: r = launch<3>(prm, blocks, s); break;
     default: r = launch<4>(prm, blocks, s); break;
   }
-  return r;
+  if (r != DCP_OK || pl.splits == 1) return r;
+  // the chunks of each stripe row merge exactly like stripes (partial lse in base 2)
+  return launch_lse_merge(pl.splits, (int64_t)a->batch * M, kDV, prm.ws_o, prm.ws_lse, 1, a->lse_base, a->o, a->lse, s);
 }

@@ -235,8 +235,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     need = ctypes.c_size_t(0)
     _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
     if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
-        # zero-filled: the split arrival counters at its end must start at 0
-        workspace = torch.zeros(need.value, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
     a.q = _ptr(q, torch.bfloat16, "q", dev)
     a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
     a.block_table = _ptr(block_table, torch.int32, "block_table", dev)

@@ -2,11 +2,14 @@
 
 For every workgroup and every tile load of each full-size workload (pools
 with no spare pages, exactly as the benchmark allocates them) this checks that
-each 16-byte direct-to-LDS load reads either the zero row or a row of the
-tile's own page inside the pool, and that the epilogue's stores and the split
-combine stay inside their buffers.  It mirrors the constants and index math of
-csrc/stripe_attn.hip; a planted copy of an earlier guard (slots past the tile
-not excluded) must be caught.
+each 16-byte direct-to-LDS load reads a chunk of the tile's own page inside
+the pool, and only rows of the split (rows the pool write filled), so no
+stale or NaN row reaches the MFMAs; that the vector-memory wait at the top of
+each iteration covers exactly the loads still in flight; and that the
+epilogue's stores stay inside their buffers.  It mirrors the constants and
+index math of csrc/stripe_attn.hip; planted copies of earlier mistakes (no
+clamp of the fast path's tail slots, no substitution of rows past the split)
+must be caught.
 """
 
 import math
@@ -33,7 +36,7 @@ def plan(B, M, bt_cols, P, cus=256, num_splits=0):
     mgroups = -(-M // (32 * W))
     tiles_max = -(-(bt_cols * P) // TILE)
     splits = num_splits or -(-cus // (B * mgroups))
-    splits = max(1, min(splits, tiles_max))
+    splits = max(1, min(splits, tiles_max, 256))
     per = -(-tiles_max // splits)
     splits = -(-tiles_max // per)
     return W, mgroups, splits, per * TILE
@@ -46,18 +49,50 @@ def count_rows(x, N, I, r):
     return np.where(x <= 0, 0, (x // rnd) * I + rem)
 
 
-def slot_rows(W, guard_tile=True):
-    """(tt, c, use-mask-independent-of-rows) for every slot one wave set issues per tile."""
+def fast_chunks(W, plant=None):
+    """Global chunk (0..2303 of the tile's 36,864 contiguous bytes) each slot of a fast tile loads."""
+    loads, _ = shape(W)
+    s = np.arange(loads * 64 * W)
+    q = s * 57457 >> 22
+    assert (q == s // 73).all()                       # the kernel's division by 73
+    g = s - q
+    if plant != "no_fast_clamp":
+        g = np.minimum(g, TILE * CHUNKS - 1)
+    return g
+
+
+def general_rows_chunks(W, rows_left, plant=None):
+    """(tile row, chunk) each slot of a general (partial or unaligned) tile loads."""
     loads, _ = shape(W)
     s = np.arange(loads * 64 * W)
     tt, c = s // ROW_SLOTS, s % ROW_SLOTS
-    base_ok = c < CHUNKS
-    if guard_tile:
-        base_ok &= s < TILE_SLOTS
-    return tt, base_ok
+    if plant != "no_row_substitute":
+        tt = np.where((s < TILE_SLOTS) & (tt < rows_left), tt, 0)
+    c = np.minimum(c, CHUNKS - 1)
+    return tt, c
 
 
-def check_workload(w, I, guard_tile=True, num_splits=0):
+def check_waits(ntiles, stages):
+    """The wait before tile `it` allows exactly the loads of the live tiles issued after it."""
+    issued = list(range(min(stages - 1, ntiles)))     # prologue
+    for it in range(ntiles):
+        after = ntiles - 1 - it
+        allowed_tiles = min(stages - 2, after)
+        later = [t for t in issued if t > it]
+        assert len(later) == allowed_tiles, (ntiles, stages, it)
+        assert it in issued
+        nt = it + stages - 1
+        if nt < ntiles:
+            issued.append(nt)
+
+
+def test_wait_counts_cover_the_tail():
+    for stages in (3, 4):
+        for ntiles in range(1, 12):
+            check_waits(ntiles, stages)
+
+
+def check_workload(w, I, plant=None, num_splits=0):
     lens = workloads.seq_lens(w)
     N, P = w.N, w.page_size
     counts = H.oracle_counts(lens, N, I)
@@ -67,52 +102,34 @@ def check_workload(w, I, guard_tile=True, num_splits=0):
         tab = tables[r]
         B, cols = tab.shape
         W, mgroups, splits, split_rows = plan(B, M, cols, P, num_splits=num_splits)
-        loads, stages = shape(W)
-        tt, base_ok = slot_rows(W, guard_tile)
+        g = fast_chunks(W, plant)
         max_vis = count_rows(lens, N, I, r)
         for b in range(B):
             for sp in range(splits):
                 row_lo = sp * split_rows
                 row_hi = min(row_lo + split_rows, int(max_vis[b]))
                 ntiles = -(-(row_hi - row_lo) // TILE) if row_hi > row_lo else 0
-                for it in range(ntiles + stages - 1):
-                    if it >= ntiles:
-                        continue                       # dead tiles load only the zero row
+                for it in range(ntiles):                  # tiles past the split issue no loads
                     J = row_lo + it * TILE
                     rows_left = row_hi - J
-                    if P % TILE == 0 and rows_left >= TILE and guard_tile:
-                        # fast path: slot s takes chunk min(s - s//73, 2303) of the
-                        # 36,864 contiguous bytes of the tile's 32 rows
-                        loads, _ = shape(W)
-                        s_ = np.arange(loads * 64 * W)
-                        g = np.minimum(s_ - (s_ * 57457 >> 22), TILE * CHUNKS - 1)
-                        assert ((s_ * 57457 >> 22) == s_ // 73).all()
-                        assert g.min() >= 0 and g.max() < TILE * CHUNKS
+                    if P % TILE == 0 and rows_left >= TILE:
+                        # fast path: slot s loads chunk g[s] of the tile's 32 contiguous rows
                         pi = J // P
                         assert pi < cols and 0 <= tab[b, pi] < pool_pages
-                        assert J % P + TILE <= P          # the tile's rows lie inside its page
+                        assert J % P + TILE <= P                   # the tile lies inside its page
+                        assert g.min() >= 0 and g.max() < TILE * CHUNKS, (w.name, r, b, sp, it)
                         continue
-                    use = base_ok & (tt < rows_left)
-                    if not use.any():
-                        continue
-                    if P % TILE == 0:
-                        pi = J // P
-                        pg = tab[b, pi] if pi < cols else -1
-                        assert 0 <= pg < pool_pages, "the kernel would flag this page; tables here are valid"
-                        rows = pg * P + (J % P) + tt[use]
-                        # every row read lies in the tile's own page and inside the pool
-                        assert rows.max() < pg * P + P, (w.name, r, b, sp, it)
-                        assert rows.max() < pool_pages * P
-                    else:
-                        j = J + tt[use]
-                        pi = j // P
-                        assert (pi < cols).all()
-                        pg = tab[b, pi]
-                        assert (pg >= 0).all() and (pg < pool_pages).all()
-        # epilogue: partial / final rows and the combine stay inside their buffers
+                    tt, c = general_rows_chunks(W, rows_left, plant)
+                    j = J + tt
+                    assert (j < row_hi).all(), (w.name, r, b, sp, it, "row past the split")
+                    pi = j // P
+                    assert (pi < cols).all()
+                    pg = tab[b, pi]
+                    assert (pg >= 0).all() and (pg < pool_pages).all()
+                    assert (c < CHUNKS).all()
+        # epilogue: partial / final rows stay inside their buffers
         assert B * mgroups * 32 * W >= B * M
-        ws_floats = splits * B * M * (512 + 1)
-        assert (splits - 1) * B * M + (B - 1) * M + (M - 1) < splits * B * M <= ws_floats
+        assert (splits - 1) * B * M + (B - 1) * M + (M - 1) < splits * B * M
 
 
 @pytest.mark.parametrize("name,I", [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)])
@@ -120,13 +137,19 @@ def test_dma_loads_stay_in_the_tile_page(name, I):
     check_workload(workloads.WORKLOADS[name], I)
 
 
-def test_planted_missing_tile_guard_is_caught():
-    """Without the slot < tile guard the last load instruction of a full tile
-    reads rows 32-34 past the tile: past its page, and past the pool at the
-    pool's last page (page-aligned path; the per-row path looks every row up)."""
+def test_planted_missing_fast_clamp_is_caught():
+    """Without the clamp, the tail slots of a fast tile's last load instruction
+    read up to 221 chunks past the tile's 36,864 bytes."""
     for name in ("dsv3", "k3"):
         with pytest.raises(AssertionError):
-            check_workload(workloads.WORKLOADS[name], 1, guard_tile=False)
+            check_workload(workloads.WORKLOADS[name], 1, plant="no_fast_clamp")
+
+
+def test_planted_missing_row_substitution_is_caught():
+    """Without the substitution, a partial tile loads rows past the split's end
+    (rows the pool write never filled)."""
+    with pytest.raises(AssertionError):
+        check_workload(workloads.WORKLOADS["ragged"], 1, plant="no_row_substitute")
 
 
 def test_plan_matches_library_workspace():
@@ -142,5 +165,5 @@ def test_plan_matches_library_workspace():
         n = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
         W, mg, splits, _ = plan(B, q_len * H_, cols, P, num_splits=ns)
-        want = 0 if splits == 1 else splits * B * q_len * H_ * 513 * 4 + B * mg * 4
+        want = 0 if splits == 1 else splits * B * q_len * H_ * 513 * 4
         assert n.value == want
