@@ -13,23 +13,26 @@
 // speculative decoding": global lengths keep causality).
 //
 // How (MI355X / gfx950):
-//  * One workgroup per (request, KV split, group of up to 128 query rows);
-//    W = 1..4 wavefronts, each owning 32 query rows (heads are the N side of
-//    the MFMA tiles, so the latent tile read from LDS serves all of them).
+//  * One workgroup of 4 wavefronts (one per SIMD) per (request, KV split,
+//    group of up to 128 query rows = RB blocks of 32).  Heads are the N side
+//    of the MFMA tiles, so one latent tile in LDS serves all of them.
 //  * KV tiles of 32 tokens are streamed HBM -> LDS with 16-byte direct-to-LDS
-//    loads into a 3-4 stage ring; a tile's token rows are padded to 73
-//    16-byte chunks so that both LDS access patterns below are bank-conflict
-//    free.  The same LDS tile is the key (QK^T) and the value (PV): every KV
-//    byte is read from HBM once.
+//    loads into a 4-stage ring; a tile's token rows are padded to 73 16-byte
+//    chunks so that the LDS access patterns below are bank-conflict free.
+//    The same LDS tile is the key (QK^T) and the value (PV): every KV byte is
+//    read from HBM once.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32 query
-//    rows, K = 576 in 36 steps); Q stays in registers for the whole kernel.
-//  * Online softmax in base 2 (scale * log2(e) folded in), row max over the
-//    tile with one lane-half exchange; the reference max only moves when it
-//    grows by more than 2^8, so the O rescale is rare and still exact.
-//  * O^T += V^T P^T with the same MFMA (M = 32 value columns x 16 blocks,
-//    N = 32 query rows, K = 16 tokens): P^T comes straight from the S^T
-//    accumulator registers (no data movement), V^T is read from the
-//    token-major LDS tile with ds_read_b64_tr_b16 transpose reads.
+//    rows, K = 576 in 36 steps): wave w < RB owns query-row block w, whose Q
+//    stays in its registers for the whole kernel.
+//  * Online softmax in base 2 (scale * log2(e) folded in) by the same wave,
+//    row max over the tile with one lane-half exchange; the reference max
+//    only moves when it grows by more than 2^8, so the O rescale is rare and
+//    still exact.  P (bf16) goes to a small LDS buffer.
+//  * O^T += V^T P^T with the same MFMA (M = 32 value columns, N = 32 query
+//    rows, K = 16 tokens), split by value columns: wave w owns columns
+//    128w .. 128w+127 of every row block, so each V^T fragment (transpose
+//    read of the token-major tile) feeds RB MFMAs and the tile's values are
+//    read from LDS once per workgroup, not once per row block.
 //  * Split-KV: when there are fewer (request, row group) items than compute
 //    units, each request's stripe is cut into equal chunks of whole tiles; a
 //    chunk writes its (o, lse) partial to the workspace and a second launch
@@ -48,35 +51,61 @@ constexpr int kTile = 32;               // tokens per tile
 constexpr int kRowSlots = kChunks + 1;  // padded row: 73 chunks
 constexpr int kTileSlots = kTile * kRowSlots;  // 2336
 constexpr int kKSteps = kD / 16;        // 36 MFMA k-steps for QK^T
-constexpr int kColBlocks = kDV / 32;    // 16 value-column blocks
 constexpr int kRowBytes = kD * 2;       // 1152
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveCols = kDV / kWaves / 32;   // 4 value-column blocks of 32 per wave
+constexpr int kMaxRB = 4;               // query-row blocks of 32 per workgroup
+
+// Tile loads: instruction g fills the 64 tile slots from min(64 g, 2272), so
+// 37 instructions cover a tile and a stage is exactly one tile (the last one
+// overlaps the one before it and writes the same bytes again).  With fewer
+// than 4 query-row blocks, the wave without scores to compute issues all 37;
+// otherwise each wave issues 10 (g = 4 j + wave, repeats past 36).
+constexpr int kTileInsts = (kTileSlots + 63) / 64;   // 37
+constexpr int kLoads = 10;
+constexpr int kLastBase = kTileSlots - 64;
+static_assert(kLoads * kWaves >= kTileInsts, "tile coverage");
+constexpr int kStageBytes = kTileSlots * 16;    // 37,376
+constexpr int kStages = 4;
+// P^T rows: 4 chunks of 16 bytes, chunk kk*2 + lane half holding k-step kk;
+// chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16-byte
+// accesses of 16 consecutive rows hit disjoint banks.  With fewer than 4 row
+// blocks, P^T, the rescale factors and flags are double-buffered by tile
+// parity (one barrier per tile); with 4, one buffer (two barriers per tile).
+constexpr int kPRow = 64;
+constexpr int kPBuf = 3 * 32 * kPRow;                   // one buffer of 96 rows
+constexpr int kPOff = kStages * kStageBytes;
+constexpr int kAlphaOff = kPOff + 2 * kPBuf;            // [2][128] per-row rescale factor of a tile
+constexpr int kInvOff = kAlphaOff + 2 * kMaxRB * 32 * 4;   // per-row 1 / l at the end
+constexpr int kFlagOff = kInvOff + kMaxRB * 32 * 4;     // [2][16] one byte per row block: rescale
+constexpr int kLdsBytes = kFlagOff + 32;
+static_assert(kMaxRB * 32 * kPRow <= 2 * kPBuf, "single P^T buffer of 128 rows");
+static_assert(kLdsBytes <= 163840, "LDS budget");
+static_assert(kTileInsts <= 63, "vmcnt range");
+
 // LDS operand prefetch depth (MFMA steps) of the QK^T and PV chains
 #ifndef DCP_QK_AHEAD
 #define DCP_QK_AHEAD 3
 #endif
 #ifndef DCP_PV_AHEAD
-#define DCP_PV_AHEAD 3
+#define DCP_PV_AHEAD 4
 #endif
 constexpr int kQkAhead = DCP_QK_AHEAD;
 constexpr int kPvAhead = DCP_PV_AHEAD;
 static_assert(kQkAhead >= 1 && kQkAhead <= 15 && kPvAhead >= 1 && kPvAhead <= 7, "LDS counter range");
+// QK^T steps between two of a wave's tile loads slotted under them
+#ifndef DCP_DMA_EVERY
+#define DCP_DMA_EVERY 3
+#endif
+constexpr int kDmaEvery = DCP_DMA_EVERY;
+
+static_assert(kDmaEvery >= 1 && (kLoads - 1) * kDmaEvery < kKSteps, "loads fit under QK^T");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <int W>
-struct Shape {
-  static constexpr int kThreads = 64 * W;
-  static constexpr int kLoads = (kTileSlots + 64 * W - 1) / (64 * W);  // DMA loads / wave / tile
-  static constexpr int kStageBytes = kLoads * 64 * W * 16;
-  static constexpr int kStages = (W == 1) ? 3 : 4;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kWaitLoads = (kStages - 2) * kLoads;               // loads still in flight
-  static_assert(kLdsBytes <= 163840, "LDS budget");
-  static_assert(kWaitLoads <= 63, "vmcnt range");
-};
 
 // A zero latent row (plus pad chunk): what a tile slot holds when its page id
 // is out of range (the call also flags DCP_ERANGE), so a bad table never
@@ -86,7 +115,7 @@ __device__ __align__(16) uint4 g_zero_row[kRowSlots];
 struct Params {
   int32_t N, I, P, rank;
   int32_t B, q_len, H, M;          // M = q_len * H query rows per request
-  int32_t W, mgroups, splits, split_rows;
+  int32_t RB, mgroups, splits, split_rows;
   const __bf16* q;
   const char* pool;
   int64_t num_pages;
@@ -121,21 +150,38 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm_then_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+// 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
+// (the scalar-base form: no 64-bit per-lane address arithmetic).
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
+  // the base is wave-uniform by construction; say so, so that it always lands
+  // in an SGPR pair (free when the compiler already knows)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
 }
 
-// Wait until only the loads of the `after` most recent tiles (each kLoads
-// per wave) are in flight, then barrier.  Tiles past the split issue no loads,
-// so near the end fewer tiles are in flight and the count drops with them.
-template <int kMaxAfter, int kLoads>
+// this wave's loads older than the N most recent ones and its LDS accesses
+// are done, then barrier
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait until only the loads of the `after` most recent tiles (kPerTile per
+// wave each) are in flight, then barrier.  Tiles past the split issue no
+// loads, so near the end fewer tiles are in flight and the count drops with
+// them.  A count above the counter's range waits for a few loads more.
+template <int kPerTile>
 __device__ __forceinline__ void wait_tiles_then_barrier(int after) {
-  static_assert(kMaxAfter == 1 || kMaxAfter == 2, "ring depth");
-  if (after >= kMaxAfter) wait_vm_then_barrier<kMaxAfter * kLoads>();
-  else if (kMaxAfter == 2 && after == 1) wait_vm_then_barrier<kLoads>();
+  constexpr int kTwo = 2 * kPerTile < 63 ? 2 * kPerTile : 63;
+  if (after >= 2) wait_vm_then_barrier<kTwo>();
+  else if (after == 1) wait_vm_then_barrier<kPerTile>();
   else wait_vm_then_barrier<0>();
 }
+
+// LDS writes of this wave done, then barrier
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // acc *= s for one 32x32 accumulator tile that lives in AGPRs: each element is
 // read, scaled and written back in place through one temporary VGPR, so the
@@ -157,44 +203,36 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float sc) {
 #undef DCP_SCALE1
 }
 
-// Scalar (SMEM) read of a uniform 32-bit value: keeps page-table lookups off
-// the vector-memory counter that tracks the in-flight tile loads.
-__device__ __forceinline__ int32_t scalar_load(const int32_t* ptr) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
-}
-
 __device__ __forceinline__ float other_half(float v) {
   // value of lane l ^ 32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
-// (the scalar-base form: no 64-bit per-lane address arithmetic).
-__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
-  // the base is wave-uniform by construction; say so, so that it always lands
-  // in an SGPR pair (free when the compiler already knows)
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
-}
-
 // Upper bound on KV chunks per request (each adds one partial to the workspace).
 constexpr int kMaxSplits = 256;
 
-template <int W, bool kAligned>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(1, 1)))
+// NW = 8 (up to 3 query-row blocks): two wavefronts per SIMD with split
+// roles -- waves 0..RB-1 compute scores and softmax of one row block each,
+// wave 3 issues the tile loads, waves 4..7 accumulate PV for 128 value
+// columns each -- so one wave's softmax and LDS waits overlap the other
+// wave's MFMAs on the same SIMD; one barrier per tile, P^T double-buffered.
+// NW = 4 (4 row blocks): one wave per SIMD doing scores, softmax and PV for
+// its row block and 128 columns; two barriers per tile.
+template <int RB, bool kAligned, int NW>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 stripe_attn_kernel(Params p) {
-  using S = Shape<W>;
-  __shared__ __align__(16) char smem[S::kLdsBytes];
+  static_assert((NW == 8 && RB <= 3) || (NW == 4 && RB == 4), "wave layouts");
+  constexpr bool kWS = NW == 8;        // split roles
+  __shared__ __align__(16) char smem[kLdsBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;          // which 8-element k half of an MFMA operand
   const int n = lane & 31;             // query row (MFMA column) owned by this lane
+  const bool qk_wave = wave < RB;      // owns query-row block `wave` for QK^T and softmax
+  const bool pv_wave = kWS ? wave >= 4 : true;
+  const int cgrp = kWS ? wave - 4 : wave;   // PV wave: value columns 128*cgrp .. +127
 
   // ---- work item: XCD-aware block order (the dispatcher sends block i to XCD
   // i % 8, so consecutive logical items share an XCD and its L2)
@@ -212,25 +250,27 @@ stripe_attn_kernel(Params p) {
   int32_t row_hi = row_lo + p.split_rows;
   row_hi = row_hi < max_vis ? row_hi : max_vis;
   const int ntiles = row_hi > row_lo ? (row_hi - row_lo + kTile - 1) / kTile : 0;
+  const int row0 = mg * 32 * RB;       // first query row of this workgroup
 
-  // ---- this lane's query row and its visible limit inside the split
-  const int R = mg * 32 * W + wave * 32 + n;
-  const bool valid = R < p.M;
+  // ---- QK wave: its query row and the row's visible limit inside the split
+  const int R = row0 + wave * 32 + n;
+  const bool valid = qk_wave && R < p.M;
   const int t = valid ? R / p.H : 0;
   int32_t lim = count_rows(S_b - p.q_len + t + 1, p.N, p.I, p.rank);
   if (!valid) lim = row_hi;
   lim = lim < row_hi ? lim : row_hi;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds row n, dims
-  // 16*ks + 8*half .. +7 for every k-step
+  // 16*ks + 8*half .. +7 for every k-step (QK waves, loaded on their path)
   bf16x8 qf[kKSteps];
-  {
+  auto load_q = [&]() {
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(p.q + ((int64_t)b * p.M + (valid ? R : 0)) * kD);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = valid ? qrow[2 * ks + half] : bf16x8{};
-  }
+  };
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(smem + kFlagOff)[threadIdx.x] = 0;   // ordered by the first barrier
   const char* zero = reinterpret_cast<const char*>(g_zero_row);
   const int32_t* bt_row = p.bt + (int64_t)b * p.bt_cols;
 
@@ -261,38 +301,50 @@ stripe_attn_kernel(Params p) {
     return p.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
   };
 
+  // who issues the tile loads, and how many per tile
+  constexpr bool kLoaderWave = kWS;
+  constexpr int kMyLoads = kLoaderWave ? kTileInsts : kLoads;
+  const bool loads_here = !kLoaderWave || wave == kWaves - 1;
+  // first tile slot that this wave's load j fills
+  auto load_slot0 = [&](int j) -> int {
+    const int s0 = 64 * (kLoaderWave ? j : j * kWaves + wave);
+    return s0 < kLastBase ? s0 : kLastBase;
+  };
   // A tile is "fast" when it is page-aligned and all 32 rows lie in the split:
   // its 32 rows are 36,864 contiguous bytes, so slot s of the padded LDS tile
-  // (row s / 73, chunk s % 73) takes global chunk s - s / 73 of the tile; pad
-  // chunks and slots past the tile fetch a neighbouring chunk of the same tile,
-  // which is never read from LDS.
+  // (row s / 73, chunk s % 73) takes global chunk s - s / 73 of the tile; the
+  // pad chunks fetch a neighbouring chunk of the same tile, never read from LDS.
   auto tile_is_fast = [&](int it) -> bool {
     return kAligned && it < ntiles && row_hi - (row_lo + it * kTile) >= kTile;
   };
   auto fast_offset = [&](int k) -> uint32_t {
-    const uint32_t s = (uint32_t)((k * W + wave) * 64 + lane);
+    const uint32_t s = (uint32_t)(load_slot0(k) + lane);
     uint32_t g = s - ((s * 57457u) >> 22);          // s - floor(s / 73), exact for s < 4096
     g = g < (uint32_t)(kTile * kChunks - 1) ? g : (uint32_t)(kTile * kChunks - 1);
     return g * 16u;
   };
+  auto issue_fast = [&](const char* tb, uint32_t lds_stage, int k) {
+    dma16_sbase(tb, fast_offset(k), lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane(load_slot0(k) * 16));
+  };
   // General loads (live tiles only): partial tiles and pages smaller than a
-  // tile.  A slot that holds no token of the split (rows past the split end,
-  // the pad chunk, slots past the tile) loads a chunk of the tile's first
-  // row instead: finite data that the softmax masks to weight zero (or that
-  // is never read), so no stale, unowned or NaN row reaches the MFMAs.
+  // tile.  A slot that holds no token of the split (rows past the split end)
+  // loads a chunk of the tile's first row instead, and the pad chunk loads
+  // chunk 71 of its row: finite data that the softmax masks to weight zero
+  // (or that is never read), so no stale, unowned or NaN row reaches the MFMAs.
   auto load_tile_general = [&](int it) {
-    const int stage = it % S::kStages;
+    if (!loads_here) return;
     const int32_t J = row_lo + it * kTile;
     const int32_t rows_left = row_hi - J;          // >= 1 for a live tile
     const char* tb = nullptr;
     if (kAligned) tb = tile_base_of(it);
-    const uint32_t lds_stage = lds0 + stage * S::kStageBytes;
+    const uint32_t lds_stage = lds0 + (it % kStages) * kStageBytes;
 #pragma unroll 1
-    for (int k = 0; k < S::kLoads; ++k) {
-      const int s = (k * W + wave) * 64 + lane;
+    for (int k = 0; k < kMyLoads; ++k) {
+      const int s0 = load_slot0(k);
+      const int s = s0 + lane;
       int tt = s / kRowSlots;
       int c = s - tt * kRowSlots;
-      if (!(s < kTileSlots && tt < rows_left)) tt = 0;
+      if (tt >= rows_left) tt = 0;
       c = c < kChunks ? c : kChunks - 1;
       const char* src = zero;
       if (kAligned) {
@@ -304,167 +356,343 @@ stripe_attn_kernel(Params p) {
         if (pg >= 0 && pg < p.num_pages) src = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes + c * 16;
         else flag_range(p.status);
       }
-      dma16(src, lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
+      dma16(src, lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane(s0 * 16));
     }
   };
 
-  // ---- accumulators
-  f32x16 oacc[kColBlocks];
+  // ---- accumulators of a PV wave: its value columns of every row block
+  f32x16 oacc[RB][kWaveCols];
+  auto init_o = [&]() {
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb) oacc[cb] = f32x16{};
-  float m_run = -INFINITY;   // reference max (base-2 units) of this row
-  float l_run = 0.f;         // this lane-half's share of the softmax denominator
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < kWaveCols; ++cb) oacc[rb][cb] = f32x16{};
+  };
+  float m_run = -INFINITY;   // QK wave: reference max (base-2 units) of its row
+  float l_run = 0.f;         // QK wave: this lane-half's share of the softmax denominator
 
-  // per-lane LDS byte offsets inside a stage
+  // per-lane LDS byte offsets
   const int kq_off = (tau(n) * kRowSlots + half) * 16;          // + 32*ks
-  const int g = lane >> 4, jl = lane & 15;
-  const int v_off = ((4 * (jl >> 2) + (g >> 1)) * kRowSlots + 2 * (g & 1) + ((jl & 3) >> 1)) * 16 + (jl & 1) * 8;
+  const int g4 = lane >> 4, jl = lane & 15;
+  const int v_off = ((4 * (jl >> 2) + (g4 >> 1)) * kRowSlots + 2 * (g4 & 1) + ((jl & 3) >> 1)) * 16 + (jl & 1) * 8 +
+                    cgrp * kWaveCols * 64;                        // + cb*64, + 16 token rows per k-step
+  // P^T chunk kk*2 + half of row r (swizzled), in buffer `buf`
+  auto p_addr = [&](int buf, int r, int kk) -> char* {
+    return smem + kPOff + buf * kPBuf + r * kPRow + (((kk * 2 + half) ^ ((r >> 2) & 3)) * 16);
+  };
   // tile-relative token of each of this lane's S^T registers (for masking)
   auto tok_of = [&](int i) { return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half; };
 
-  // ---- prologue: tiles 0 .. S-2 in flight, S^T of tile 0
+  // ---- prologue: tiles 0 .. 2 in flight
+  auto issue_prologue = [&]() {
 #pragma unroll 1
-  for (int it = 0; it < S::kStages - 1 && it < ntiles; ++it) {
-    if (tile_is_fast(it)) {
-      const char* tb = tile_base_of(it);
-      const uint32_t lds_stage = lds0 + (it % S::kStages) * S::kStageBytes;
-      if (tb) {
+  for (int it = 0; it < kStages - 1 && it < ntiles; ++it) {
+    const char* tb = tile_is_fast(it) ? tile_base_of(it) : nullptr;
+    if (tb) {
+      const uint32_t lds_stage = lds0 + (it % kStages) * kStageBytes;
+      if (loads_here) {
 #pragma unroll 1
-        for (int k = 0; k < S::kLoads; ++k)
-          dma16_sbase(tb, fast_offset(k), lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
-      } else {
-        load_tile_general(it);
+        for (int k = 0; k < kMyLoads; ++k) issue_fast(tb, lds_stage, k);
       }
     } else {
       load_tile_general(it);
     }
   }
+  };
   const float c2 = p.c2;
 
-#pragma unroll 1
-  for (int it = 0; it < ntiles; ++it) {
-    // Tile it is in LDS and every wave is done with tile it-1, whose stage
-    // now receives tile it+S-1.
-    const int after = ntiles - 1 - it;                 // live tiles after this one
-    wait_tiles_then_barrier<S::kStages - 2, S::kLoads>(after);
-    const int nt = it + S::kStages - 1;
-    const bool fast = tile_is_fast(nt);
-    const char* ntb = fast ? tile_base_of(nt) : nullptr;
-    if (nt < ntiles && (!fast || ntb == nullptr)) load_tile_general(nt);
-    const bool dma_in_pv = fast && ntb != nullptr;
-    const uint32_t nlds = lds0 + (nt % S::kStages) * S::kStageBytes;
-    const char* st = smem + (it % S::kStages) * S::kStageBytes;
-    const int32_t J = row_lo + it * kTile;
-
-    // -- S^T = K Q^T over the 576 latent dims (K fragments read kQkAhead steps ahead)
-    f32x16 sacc = f32x16{};
-    {
-      const char* kb = st + kq_off;
-      bf16x8 kf[kKSteps];
+  // S^T = K Q^T of the tile in stage `st` over the 576 latent dims (K
+  // fragments read kQkAhead steps ahead); with `dma`, this wave's loads of
+  // another tile are slotted under the first MFMAs.
+  auto qk = [&](const char* st, const char* ntb, uint32_t nlds, bool dma) -> f32x16 {
+    // two accumulators (even and odd k-steps): no MFMA waits for the previous one
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const char* kb = st + kq_off;
+    bf16x8 kf[kKSteps];
 #pragma unroll
-      for (int ks = 0; ks < kQkAhead; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + 32 * ks);
+    for (int ks = 0; ks < kQkAhead; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + 32 * ks);
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + kQkAhead < kKSteps) kf[ks + kQkAhead] = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + kQkAhead));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // -- online softmax in base 2.  Scores are masked only on tiles that
-    // cross a row's visible limit; the row max is taken on the raw scores
-    // (the scale is positive) and each weight costs one FMA and one exp2.
-    const int32_t vis = lim - J;                       // visible rows of this tile
-    if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-    for (int i = 3; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), i + 1 < 16 ? sacc[i + 1] : -INFINITY);
-    mx = fmaxf(mx, other_half(mx)) * c2;               // tile max in base-2 units
-    const float m_new = fmaxf(m_run, mx);
-    const bool move = m_new > m_run + 8.0f;             // move the reference only on a large jump
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb) scale_acc(oacc[cb], alpha);
-      l_run *= alpha;
-      if (move) m_run = m_new;
-    }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    bf16x8 pk[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, neg_m));
-      psum += e;
-      pk[i >> 3][i & 7] = (__bf16)e;
-    }
-    l_run += psum;
-
-    // -- O^T += V^T P^T (V^T fragments by transpose reads, kPvAhead steps ahead),
-    // with the loads of tile it+S-1 slotted under the MFMAs
-    {
-      const char* vb = st + v_off;
-      auto vfrag = [&](int step) {
-        const int cb = step >> 1, kk = step & 1;
-        const char* a = vb + kk * (16 * kRowSlots * 16) + cb * 64;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 2 * kRowSlots * 16));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 vf[2 * kColBlocks];
-#pragma unroll
-      for (int step = 0; step < kPvAhead; ++step) vf[step] = vfrag(step);
-#pragma unroll
-      for (int step = 0; step < 2 * kColBlocks; ++step) {
-        if (step + kPvAhead < 2 * kColBlocks) vf[step + kPvAhead] = vfrag(step + kPvAhead);
-        oacc[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], pk[step & 1], oacc[step >> 1], 0, 0, 0);
-        if (step < S::kLoads && dma_in_pv)
-          dma16_sbase(ntb, fast_offset(step), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((step * W + wave) * 1024));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the rest of the tile's loads when a wave issues more loads than PV steps
-#pragma unroll 1
-      for (int k = 2 * kColBlocks; k < S::kLoads; ++k)
-        if (dma_in_pv)
-          dma16_sbase(ntb, fast_offset(k), nlds + (uint32_t)__builtin_amdgcn_readfirstlane((k * W + wave) * 1024));
-    }
-  }
-  // every load has landed by now; make that explicit before the LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // ---- epilogue: normalise and store this row's (o, lse)
-  const float l_tot = l_run + other_half(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  const float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-  float* orow;
-  if (p.splits == 1) orow = p.o + ((int64_t)b * p.M + R) * kDV;
-  else orow = p.ws_o + (((int64_t)split * p.B + b) * p.M + R) * kDV;
-  if (valid) {
-#pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float4 v;
-        v.x = oacc[cb][4 * g4 + 0] * inv;
-        v.y = oacc[cb][4 * g4 + 1] * inv;
-        v.z = oacc[cb][4 * g4 + 2] * inv;
-        v.w = oacc[cb][4 * g4 + 3] * inv;
-        *reinterpret_cast<float4*>(orow + cb * 32 + 8 * g4 + 4 * half) = v;
-      }
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kQkAhead < kKSteps) kf[ks + kQkAhead] = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + kQkAhead));
+      acc[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc[ks & 1], 0, 0, 0);
+      if (dma && ks % kDmaEvery == 0 && ks / kDmaEvery < kLoads) issue_fast(ntb, nlds, ks / kDmaEvery);
       __builtin_amdgcn_sched_barrier(0);
     }
+    return acc[0] + acc[1];
+  };
+
+  // Online softmax of one tile in base 2 (QK waves), in kParts pieces so that
+  // it can run between the MFMAs of the previous tile's PV.  Scores are masked
+  // only on tiles that cross a row's visible limit; the row max is taken on
+  // the raw scores (the scale is positive); each weight costs one FMA and one
+  // exp2.  The pieces publish the row block's rescale flag and factors (when
+  // the reference max moves); P^T stays in registers until the next tile.
+  constexpr int kParts = 11;
+  f32x16 sacc;
+  int32_t vis = 0;
+  float mx = 0.f, neg_m = 0.f, psum = 0.f;
+  bf16x8 pk[2];
+  int sbuf = 0;                       // buffer of the factors and flags the pieces publish
+  auto softmax_part = [&](int part) {
+    if (part == 0) {
+      if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
+      }
+      mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[4], sacc[5]), fmaxf(sacc[6], sacc[7])));
+    } else if (part == 1) {
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[8], sacc[9]), fmaxf(sacc[10], sacc[11])));
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[12], sacc[13]), fmaxf(sacc[14], sacc[15])));
+      mx = fmaxf(mx, other_half(mx)) * c2;               // tile max in base-2 units
+      const float m_new = fmaxf(m_run, mx);
+      const bool move = m_new > m_run + 8.0f;             // move the reference only on a large jump
+      const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
+      if (any_move) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        if (half == 0) reinterpret_cast<float*>(smem + kAlphaOff)[sbuf * kMaxRB * 32 + wave * 32 + n] = alpha;
+        l_run *= alpha;
+        if (move) m_run = m_new;
+      }
+      if (lane == 0) reinterpret_cast<uint8_t*>(smem + kFlagOff)[sbuf * 16 + wave] = any_move ? 1 : 0;
+      neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+      psum = 0.f;
+    } else if (part < kParts - 1) {
+      const int i0 = 2 * (part - 2);
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, neg_m));
+        psum += e;
+        pk[i >> 3][i & 7] = (__bf16)e;
+      }
+    } else {
+      l_run += psum;
+    }
+  };
+  // P^T of this row block: k-step kk of lane half h at byte kk*32 + h*16
+  auto write_p = [&](int buf) {
+    *reinterpret_cast<bf16x8*>(p_addr(buf, wave * 32 + n, 0)) = pk[0];
+    *reinterpret_cast<bf16x8*>(p_addr(buf, wave * 32 + n, 1)) = pk[1];
+  };
+
+  // Rescale this wave's columns of the row blocks whose reference moved.
+  auto rescale = [&](int buf) {
+    const uint32_t flags = *reinterpret_cast<const uint32_t*>(smem + kFlagOff + buf * 16);
+    const uint32_t fu = __builtin_amdgcn_readfirstlane(flags);
+    if (fu != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if ((fu >> (8 * rb)) & 0xff) {
+          const float alpha = reinterpret_cast<const float*>(smem + kAlphaOff)[buf * kMaxRB * 32 + rb * 32 + n];
+#pragma unroll
+          for (int cb = 0; cb < kWaveCols; ++cb) {
+            if constexpr (kWS) oacc[rb][cb] *= alpha;     // accumulators in VGPRs
+            else scale_acc(oacc[rb][cb], alpha);
+          }
+        }
+      }
+    }
+  };
+
+  // O^T += V^T P^T for the tile in stage `st`: this wave's 4 column blocks x
+  // RB row blocks x 2 k-steps, V^T fragments by transpose reads (kPvAhead
+  // ahead), P^T fragments of a k-step read half a k-step ahead; with `sm`,
+  // the next tile's softmax pieces run between the MFMAs.
+  auto pv = [&](const char* st, bool sm, int pbuf) {
+    const char* vb = st + v_off;
+    bf16x8 pf[RB][2];
+    auto read_p = [&](int kk) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) pf[rb][kk] = *reinterpret_cast<const bf16x8*>(p_addr(pbuf, rb * 32 + n, kk));
+    };
+    read_p(0);
+    constexpr int kFrags = 2 * kWaveCols;             // (k-step, column block) pairs
+    auto vfrag = [&](int f) {
+      const int kk = f / kWaveCols, cb = f % kWaveCols;
+      const char* a = vb + kk * (16 * kRowSlots * 16) + cb * 64;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 2 * kRowSlots * 16));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // (4 row blocks leave room for a shallower prefetch only)
+    constexpr int kAhead = RB >= 4 ? 2 : kPvAhead;
+    bf16x8 vf[kFrags];
+#pragma unroll
+    for (int f = 0; f < kAhead && f < kFrags; ++f) vf[f] = vfrag(f);
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) {
+      if (f + kAhead < kFrags) vf[f + kAhead] = vfrag(f + kAhead);
+      if (f == kWaveCols / 2) read_p(1);
+      const int kk = f / kWaveCols, cb = f % kWaveCols;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pf[rb][kk], oacc[rb][cb], 0, 0, 0);
+        const int step = f * RB + rb;
+        if (sm && step < kParts) softmax_part(step);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the pieces left when there are fewer MFMAs than pieces
+#pragma unroll
+    for (int part = kFrags * RB; part < kParts; ++part)
+      if (sm) softmax_part(part);
+  };
+
+  // next tile's loads: the general path now, the fast path returned for the caller
+  auto start_tile_loads = [&](int nt, const char*& ntb, uint32_t& nlds) -> bool {
+    const bool fast = tile_is_fast(nt);
+    ntb = fast ? tile_base_of(nt) : nullptr;
+    if (nt < ntiles && (!fast || ntb == nullptr)) load_tile_general(nt);
+    nlds = lds0 + (nt % kStages) * kStageBytes;
+    return fast && ntb != nullptr;
+  };
+
+  if constexpr (kWS) {
+    // ---- split roles.  Every role passes the same barriers: one before the
+    // loop (tile 0 landed) and one per tile (A: tile it+1 landed, every wave
+    // done with tile it-1, P^T and factors of tile it visible).
+    if (qk_wave) {
+      load_q();
+      if (ntiles > 0) {
+        wait_tiles_then_barrier<kMyLoads>(0);
+        sacc = qk(smem, nullptr, 0, false);
+        vis = lim - row_lo;
+        sbuf = 0;
+#pragma unroll
+        for (int part = 0; part < kParts; ++part) softmax_part(part);
+        write_p(0);
+#pragma unroll 1
+        for (int it = 0; it < ntiles; ++it) {
+          wait_tiles_then_barrier<kMyLoads>(0);
+          if (it + 1 < ntiles) {
+            sacc = qk(smem + ((it + 1) % kStages) * kStageBytes, nullptr, 0, false);
+            vis = lim - (row_lo + (it + 1) * kTile);
+            sbuf = (it + 1) & 1;
+#pragma unroll
+            for (int part = 0; part < kParts; ++part) softmax_part(part);
+            write_p((it + 1) & 1);
+          }
+        }
+      }
+    } else if (pv_wave) {
+      init_o();
+      if (ntiles > 0) {
+        wait_tiles_then_barrier<kMyLoads>(0);
+#pragma unroll 1
+        for (int it = 0; it < ntiles; ++it) {
+          wait_tiles_then_barrier<kMyLoads>(0);
+          rescale(it & 1);
+          pv(smem + (it % kStages) * kStageBytes, false, it & 1);
+        }
+      }
+    } else {
+      // the loader (and, with fewer than 3 row blocks, idle waves)
+      issue_prologue();
+      if (ntiles > 0) {
+        wait_tiles_then_barrier<kMyLoads>(ntiles - 1 < 2 ? ntiles - 1 : 2);
+#pragma unroll 1
+        for (int it = 0; it < ntiles; ++it) {
+          wait_tiles_then_barrier<kMyLoads>(it + 2 < ntiles ? 1 : 0);
+          const char* ntb;
+          uint32_t nlds;
+          if (start_tile_loads(it + kStages - 1, ntb, nlds) && loads_here) {
+#pragma unroll
+            for (int k = 0; k < kMyLoads; ++k) issue_fast(ntb, nlds, k);
+          }
+        }
+      }
+    }
+  } else {
+    // ---- one wave per SIMD, every wave in every role
+    load_q();
+    init_o();
+    issue_prologue();
+    // tile 0: its scores and P^T (nothing to overlap yet)
+    if (ntiles > 0) {
+      wait_tiles_then_barrier<kMyLoads>(ntiles - 1 < 2 ? ntiles - 1 : 2);
+      sacc = qk(smem, nullptr, 0, false);
+      vis = lim - row_lo;
+#pragma unroll
+      for (int part = 0; part < kParts; ++part) softmax_part(part);
+    }
+    // steady state: iteration it computes PV of tile it and the scores and
+    // softmax of tile it+1, while tile it+3 streams in (into the stage of
+    // tile it-1) and tile it+2 is still landing
+#pragma unroll 1
+    for (int it = 0; it < ntiles; ++it) {
+      const bool has_next = it + 1 < ntiles;
+      // (A) tile it+1 is in LDS and every wave is done with tile it-1 (its
+      // stage and P^T)
+      wait_tiles_then_barrier<kMyLoads>(it + 2 < ntiles ? 1 : 0);
+      const char* ntb;
+      uint32_t nlds;
+      const bool dma_fast = start_tile_loads(it + kStages - 1, ntb, nlds);
+      if (dma_fast && !has_next) {
+#pragma unroll
+        for (int k = 0; k < kMyLoads; ++k) issue_fast(ntb, nlds, k);
+      }
+      write_p(0);                                      // P^T of tile it
+      rescale(0);
+      if (has_next) {
+        // this wave's loads of tile it+3 go under its QK^T MFMAs
+        sacc = qk(smem + ((it + 1) % kStages) * kStageBytes, ntb, nlds, dma_fast);
+        vis = lim - (row_lo + (it + 1) * kTile);
+      }
+      // (B) P^T of tile it is visible and every wave holds its factors: the
+      // softmax of tile it+1 may publish its own
+      lds_barrier();
+      // PV of tile it, with the softmax of tile it+1 between its MFMAs
+      sbuf = 0;
+      pv(smem + (it % kStages) * kStageBytes, has_next, 0);
+    }
+  }
+  // every load has landed by now; make that explicit before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: QK waves publish 1 / l of their rows and store lse; every
+  // wave normalises and stores its columns
+  float* const inv_lds = reinterpret_cast<float*>(smem + kInvOff);
+  if (qk_wave) {
+    const float l_tot = l_run + other_half(l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     if (half == 0) {
-      if (p.splits == 1) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
-      else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
+      inv_lds[wave * 32 + n] = inv;
+      if (valid) {
+        if (p.splits == 1) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
+        else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
+      }
+    }
+  }
+  lds_barrier();
+  if (!pv_wave) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int Rr = row0 + rb * 32 + n;
+    if (Rr >= p.M) continue;
+    const float inv = inv_lds[rb * 32 + n];
+    float* orow;
+    if (p.splits == 1) orow = p.o + ((int64_t)b * p.M + Rr) * kDV;
+    else orow = p.ws_o + (((int64_t)split * p.B + b) * p.M + Rr) * kDV;
+    orow += cgrp * kWaveCols * 32;
+#pragma unroll
+    for (int cb = 0; cb < kWaveCols; ++cb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 v;
+        v.x = oacc[rb][cb][4 * q4 + 0] * inv;
+        v.y = oacc[rb][cb][4 * q4 + 1] * inv;
+        v.z = oacc[rb][cb][4 * q4 + 2] * inv;
+        v.w = oacc[rb][cb][4 * q4 + 3] * inv;
+        *reinterpret_cast<float4*>(orow + cb * 32 + 8 * q4 + 4 * half) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 struct Plan {
-  int W, mgroups, splits, split_rows;
+  int RB, mgroups, splits, split_rows;
   size_t ws_bytes;
 };
 
@@ -481,8 +709,8 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   const int64_t max_rows = (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
   if ((int64_t)a->layout.n_stripes * a->layout.interleave > 0x7fffffff) return DCP_EUNSUPPORTED;
-  pl->W = M <= 32 ? 1 : (M <= 64 ? 2 : (M <= 96 ? 3 : 4));
-  pl->mgroups = (int)ceil_div(M, 32 * pl->W);
+  pl->RB = M <= 32 ? 1 : (M <= 64 ? 2 : (M <= 96 ? 3 : 4));
+  pl->mgroups = (int)ceil_div(M, 32 * pl->RB);
   const int64_t tiles_max = ceil_div(max_rows, kTile);
   int64_t splits = a->num_splits;
   if (splits == 0) {
@@ -507,12 +735,13 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   return DCP_OK;
 }
 
-template <int W>
+template <int RB>
 int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
+  constexpr int NW = RB == 4 ? 4 : 8;
   if (prm.P % kTile == 0)
-    hipLaunchKernelGGL((stripe_attn_kernel<W, true>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, prm);
   else
-    hipLaunchKernelGGL((stripe_attn_kernel<W, false>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, prm);
   return launch_status();
 }
 
@@ -549,7 +778,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.q_len = a->q_len;
   prm.H = a->n_heads;
   prm.M = (int32_t)M;
-  prm.W = pl.W;
+  prm.RB = pl.RB;
   prm.mgroups = pl.mgroups;
   prm.splits = pl.splits;
   prm.split_rows = pl.split_rows;
@@ -569,7 +798,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   const int64_t blocks = (int64_t)a->batch * pl.splits * pl.mgroups;
   hipStream_t s = (hipStream_t)stream;
   int r;
-  switch (pl.W) {
+  switch (pl.RB) {
     case 1: r = launch<1>(prm, blocks, s); break;
     case 2: r = launch<2>(prm, blocks, s); break;
     case 3: r = launch<3>(prm, blocks, s); break;

@@ -23,16 +23,36 @@ import gpu_helpers as H
 
 TILE, ROW_SLOTS, CHUNKS = 32, 73, 72
 TILE_SLOTS = TILE * ROW_SLOTS
+WAVES, LOADS, STAGES = 4, 10, 4
+LAST_BASE = TILE_SLOTS - 64
 
 
-def shape(W):
-    loads = -(-TILE_SLOTS // (64 * W))
-    stages = 3 if W == 1 else 4
-    return loads, stages
+TILE_INSTS = -(-TILE_SLOTS // 64)                 # 37
+
+
+def load_slots(loader_wave=False):
+    """Tile slot of every lane of every load instruction of the workgroup.  With a
+    loader wave (fewer than 4 query-row blocks) it issues instructions g = 0..36;
+    otherwise wave w's load k is g = 4k + w.  Instruction g fills the 64 slots
+    from min(64 g, 2272)."""
+    if loader_wave:
+        g = np.arange(TILE_INSTS)
+    else:
+        g = (np.arange(LOADS)[:, None] * WAVES + np.arange(WAVES)[None, :]).reshape(-1)
+    s0 = np.minimum(64 * g, LAST_BASE)
+    return (s0[:, None] + np.arange(64)[None, :]).reshape(-1), s0
+
+
+@pytest.mark.parametrize("loader_wave", [False, True])
+def test_loads_cover_every_slot_of_one_stage(loader_wave):
+    s, s0 = load_slots(loader_wave)
+    assert s.min() == 0 and s.max() == TILE_SLOTS - 1            # never past the stage
+    assert set(s.tolist()) == set(range(TILE_SLOTS))             # every slot written
+    assert len(s0) <= 63                                         # one tile fits the load counter
 
 
 def plan(B, M, bt_cols, P, cus=256, num_splits=0):
-    W = 1 if M <= 32 else 2 if M <= 64 else 3 if M <= 96 else 4
+    W = 1 if M <= 32 else 2 if M <= 64 else 3 if M <= 96 else 4     # query-row blocks of 32
     mgroups = -(-M // (32 * W))
     tiles_max = -(-(bt_cols * P) // TILE)
     splits = num_splits or -(-cus // (B * mgroups))
@@ -49,10 +69,9 @@ def count_rows(x, N, I, r):
     return np.where(x <= 0, 0, (x // rnd) * I + rem)
 
 
-def fast_chunks(W, plant=None):
+def fast_chunks(plant=None, loader_wave=False):
     """Global chunk (0..2303 of the tile's 36,864 contiguous bytes) each slot of a fast tile loads."""
-    loads, _ = shape(W)
-    s = np.arange(loads * 64 * W)
+    s, _ = load_slots(loader_wave)
     q = s * 57457 >> 22
     assert (q == s // 73).all()                       # the kernel's division by 73
     g = s - q
@@ -61,35 +80,47 @@ def fast_chunks(W, plant=None):
     return g
 
 
-def general_rows_chunks(W, rows_left, plant=None):
+def general_rows_chunks(rows_left, plant=None, loader_wave=False):
     """(tile row, chunk) each slot of a general (partial or unaligned) tile loads."""
-    loads, _ = shape(W)
-    s = np.arange(loads * 64 * W)
+    s, _ = load_slots(loader_wave)
     tt, c = s // ROW_SLOTS, s % ROW_SLOTS
     if plant != "no_row_substitute":
-        tt = np.where((s < TILE_SLOTS) & (tt < rows_left), tt, 0)
+        tt = np.where(tt < rows_left, tt, 0)
     c = np.minimum(c, CHUNKS - 1)
     return tt, c
 
 
 def check_waits(ntiles, stages):
-    """The wait before tile `it` allows exactly the loads of the live tiles issued after it."""
+    """Each wait allows exactly the loads of the live tiles issued after the tile it
+    waits for: tile 0 before the loop, then tile it+1 at the top of iteration it
+    (whose PV uses tile it and whose QK^T uses tile it+1); tile it+3 is issued
+    after that wait, into the stage of tile it-1."""
     issued = list(range(min(stages - 1, ntiles)))     # prologue
+
+    def wait_for(tile, allowed_tiles):
+        later = [t for t in issued if t > tile]
+        assert tile in issued
+        assert len(later) == allowed_tiles, (ntiles, tile, later, allowed_tiles)
+
+    if ntiles:
+        wait_for(0, min(2, ntiles - 1))
     for it in range(ntiles):
-        after = ntiles - 1 - it
-        allowed_tiles = min(stages - 2, after)
-        later = [t for t in issued if t > it]
-        assert len(later) == allowed_tiles, (ntiles, stages, it)
-        assert it in issued
+        if it + 1 < ntiles:
+            wait_for(it + 1, 1 if it + 2 < ntiles else 0)
+        else:
+            assert [t for t in issued if t > it] == []
         nt = it + stages - 1
         if nt < ntiles:
+            assert (nt - (it - 1)) % stages == 0            # reuses the stage of tile it-1
             issued.append(nt)
+        # stages in use during iteration it: it (PV), it+1 (QK^T), it+2 and it+3 landing
+        live = [t for t in issued if it <= t <= it + 3]
+        assert len(live) <= stages
 
 
 def test_wait_counts_cover_the_tail():
-    for stages in (3, 4):
-        for ntiles in range(1, 12):
-            check_waits(ntiles, stages)
+    for ntiles in range(1, 12):
+        check_waits(ntiles, STAGES)
 
 
 def check_workload(w, I, plant=None, num_splits=0):
@@ -102,7 +133,8 @@ def check_workload(w, I, plant=None, num_splits=0):
         tab = tables[r]
         B, cols = tab.shape
         W, mgroups, splits, split_rows = plan(B, M, cols, P, num_splits=num_splits)
-        g = fast_chunks(W, plant)
+        loader = W < WAVES
+        g = fast_chunks(plant, loader)
         max_vis = count_rows(lens, N, I, r)
         for b in range(B):
             for sp in range(splits):
@@ -119,7 +151,7 @@ def check_workload(w, I, plant=None, num_splits=0):
                         assert J % P + TILE <= P                   # the tile lies inside its page
                         assert g.min() >= 0 and g.max() < TILE * CHUNKS, (w.name, r, b, sp, it)
                         continue
-                    tt, c = general_rows_chunks(W, rows_left, plant)
+                    tt, c = general_rows_chunks(rows_left, plant, loader)
                     j = J + tt
                     assert (j < row_hi).all(), (w.name, r, b, sp, it, "row past the split")
                     pi = j // P
@@ -138,8 +170,8 @@ def test_dma_loads_stay_in_the_tile_page(name, I):
 
 
 def test_planted_missing_fast_clamp_is_caught():
-    """Without the clamp, the tail slots of a fast tile's last load instruction
-    read up to 221 chunks past the tile's 36,864 bytes."""
+    """Without the clamp, the pad slot of the tile's last row maps to the
+    chunk just past the tile's 36,864 bytes."""
     for name in ("dsv3", "k3"):
         with pytest.raises(AssertionError):
             check_workload(workloads.WORKLOADS[name], 1, plant="no_fast_clamp")
