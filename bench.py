@@ -42,8 +42,35 @@ def parse():
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-requests", type=int, default=1)
+    ap.add_argument("--cpu-sample-requests", type=int, default=64,
+                    help="requests of the workload the CPU oracle is timed on (bounded sample)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (the reference "
+                         "kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes of one dcp_stripe_attn call from the committed counter record,
+    or None when there is none for this workload or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            line = next(l for l in f if l.strip().startswith("traffic-record "))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line.strip()[len("traffic-record "):])
+    if rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return int(rec["bytes_per_call"]) if h.hexdigest() == rec["sha256"] else None
 
 
 def main():
@@ -80,11 +107,13 @@ def main():
     ns = args.cpu_sample_requests
     sample = None
     if not args.no_cpu_baseline:
+        # host copies (bf16) of the sampled requests' inputs; widened to float64
+        # one request at a time, outside the oracle's timed calls
         off = 0
         sample = []
         for b in range(min(ns, w.B)):
             S = int(lens[b])
-            sample.append((q[b].double().cpu().numpy(), kv[off:off + S].double().cpu().numpy(), S))
+            sample.append((q[b].cpu(), kv[off:off + S].cpu(), S))
             off += S
     del kv
     torch.cuda.synchronize()
@@ -149,6 +178,17 @@ def main():
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
 
+    if args.copy_calibration_mib > 0:
+        # one plain elementwise pass of known size (reads n bytes, writes n
+        # bytes) after the timed region: hardware byte counters of the
+        # attention kernel are scaled by what they read for this kernel
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
     merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
     step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
@@ -180,15 +220,17 @@ def main():
             threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
         except Exception:
             threads = os.cpu_count() or 1
-        t1 = time.perf_counter()
+        cpu_s = 0.0
         sample_bytes = 0.0
-        for qb, kvb, S in sample:
+        for qt, kvt, S in sample:
+            qb, kvb = qt.double().numpy(), kvt.double().numpy()
+            t1 = time.perf_counter()
             lists = OL.stripe_positions(S, N, I)
             parts = [OA.stripe_attention(qb, kvb, S, lists[r], workloads.SCALE, chunk=65536) for r in range(N)]
             OA.lse_merge(np.stack([p[0] for p in parts]), np.stack([OA.to_base(p[1], w.lse_base) for p in parts]),
                          w.lse_base)
+            cpu_s += time.perf_counter() - t1
             sample_bytes += S * ROW_BYTES
-        cpu_s = time.perf_counter() - t1
         cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
                "kind": "oracle", "seconds": round(cpu_s, 3),
                "sample": f"{len(sample)} of {w.B} requests ({int(sum(s[2] for s in sample))} tokens, {w.H} heads, "
@@ -218,8 +260,8 @@ def main():
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "stripe_attn_kernel (one dcp_stripe_attn launch)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "one dcp_stripe_attn call: stripe_attn_kernel + its split combine",
                      "bytes_per_launch": int(stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
