@@ -37,7 +37,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="k3", help="tiny | dsv3 | k3 | ragged | long")
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")

@@ -46,7 +46,13 @@ __global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
 lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__ o_parts,
                  const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
                  float4* __restrict__ o, float* __restrict__ lse) {
-  const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + threadIdx.x / 64;
+  // XCD-aware order: the dispatcher sends block i to XCD i % 8, so giving
+  // each XCD a contiguous range of rows keeps a request's rows on one XCD --
+  // the one whose L2 holds the split partials the attention kernel (same
+  // mapping) just wrote for it.
+  int64_t bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   // weights are base^(lse_r - m): the difference is taken in the input base

@@ -147,18 +147,20 @@ __device__ __forceinline__ int32_t count_rows(int32_t x, int32_t N, int32_t I, i
 __device__ __forceinline__ int tau(int m) { return 16 * (m >> 4) + 4 * (m & 3) + ((m >> 2) & 3); }
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
 
 // 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
-// (the scalar-base form: no 64-bit per-lane address arithmetic).
+// (the scalar-base form: no 64-bit per-lane address arithmetic).  The KV
+// stream is read once, so the load is marked non-temporal: it does not push
+// the split partials and outputs out of L2 and the memory-side cache.
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
   // the base is wave-uniform by construction; say so, so that it always lands
   // in an SGPR pair (free when the compiler already knows)
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(bu), "{m0}"(lds_addr) : "memory");
 }
 
 // this wave's loads older than the N most recent ones and its LDS accesses
@@ -551,7 +553,10 @@ stripe_attn_kernel(Params p) {
     // ---- split roles.  Every role passes the same barriers: one before the
     // loop (tile 0 landed) and one per tile (A: tile it+1 landed, every wave
     // done with tile it-1, P^T and factors of tile it visible).
+    // Issue priority: the loader first (its loads keep HBM busy), then the
+    // score/softmax waves (they produce P, the PV waves' input), then PV.
     if (qk_wave) {
+      __builtin_amdgcn_s_setprio(2);
       load_q();
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(0);
@@ -587,6 +592,7 @@ stripe_attn_kernel(Params p) {
       }
     } else {
       // the loader (and, with fewer than 3 row blocks, idle waves)
+      __builtin_amdgcn_s_setprio(3);
       issue_prologue();
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(ntiles - 1 < 2 ? ntiles - 1 : 2);
