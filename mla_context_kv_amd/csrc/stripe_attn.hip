@@ -82,6 +82,11 @@ constexpr int kFlagOff = kInvOff + kMaxRB * 32 * 4;     // [2][16] one byte per 
 constexpr int kLdsBytes = kFlagOff + 32;
 static_assert(kMaxRB * 32 * kPRow <= 2 * kPBuf, "single P^T buffer of 128 rows");
 static_assert(kLdsBytes <= 163840, "LDS budget");
+// epilogue staging: per PV wave one block of 32 rows x 128 columns (fp32),
+// rows padded by 16 bytes, inside the tile ring
+constexpr int kEpiPitch = kDV / kWaves + 4;            // floats per staged row
+constexpr int kEpiWaveBytes = 32 * kEpiPitch * 4;      // 16,896
+static_assert(kWaves * kEpiWaveBytes <= kStages * kStageBytes, "epilogue staging fits in the ring");
 static_assert(kTileInsts <= 63, "vmcnt range");
 
 // LDS operand prefetch depth (MFMA steps) of the QK^T and PV chains
@@ -181,6 +186,9 @@ __device__ __forceinline__ void wait_tiles_then_barrier(int after) {
   else if (after == 1) wait_vm_then_barrier<kPerTile>();
   else wait_vm_then_barrier<0>();
 }
+
+// this wave's LDS accesses are done
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // LDS writes of this wave done, then barrier
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -471,6 +479,36 @@ stripe_attn_kernel(Params p) {
       l_run += psum;
     }
   };
+  // Softmax of one whole tile (split-role waves).  After the split's first
+  // tile every row that sees any token has a finite reference within 2^8 of
+  // its running max, so the tile is first weighted against the current
+  // reference: when no lane's sum of weights exceeds 2^8 (every weight is
+  // non-negative, so then none does) the reference need not move and the
+  // tile max is never computed.  Otherwise -- an overflow, a larger max, or
+  // just many large weights -- the exact pieces above recompute it.
+  auto softmax_tile = [&](bool first) {
+    if (!first) {
+      if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
+      }
+      neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+      psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, neg_m));
+        psum += e;
+        pk[i >> 3][i & 7] = (__bf16)e;
+      }
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.0f)) == 0) {   // (also catches inf)
+        if (lane == 0) reinterpret_cast<uint8_t*>(smem + kFlagOff)[sbuf * 16 + wave] = 0;
+        l_run += psum;
+        return;
+      }
+    }
+#pragma unroll
+    for (int part = 0; part < kParts; ++part) softmax_part(part);
+  };
   // P^T of this row block: k-step kk of lane half h at byte kk*32 + h*16
   auto write_p = [&](int buf) {
     *reinterpret_cast<bf16x8*>(p_addr(buf, wave * 32 + n, 0)) = pk[0];
@@ -563,8 +601,7 @@ stripe_attn_kernel(Params p) {
         sacc = qk(smem, nullptr, 0, false);
         vis = lim - row_lo;
         sbuf = 0;
-#pragma unroll
-        for (int part = 0; part < kParts; ++part) softmax_part(part);
+        softmax_tile(true);
         write_p(0);
 #pragma unroll 1
         for (int it = 0; it < ntiles; ++it) {
@@ -573,8 +610,7 @@ stripe_attn_kernel(Params p) {
             sacc = qk(smem + ((it + 1) % kStages) * kStageBytes, nullptr, 0, false);
             vis = lim - (row_lo + (it + 1) * kTile);
             sbuf = (it + 1) & 1;
-#pragma unroll
-            for (int part = 0; part < kParts; ++part) softmax_part(part);
+            softmax_tile(false);
             write_p((it + 1) & 1);
           }
         }
@@ -593,7 +629,22 @@ stripe_attn_kernel(Params p) {
     } else {
       // the loader (and, with fewer than 3 row blocks, idle waves)
       __builtin_amdgcn_s_setprio(3);
-      issue_prologue();
+      // the per-lane byte offsets of a fast tile's loads are the same for
+      // every tile: computed once, kept in registers
+      uint32_t foff[kMyLoads];
+#pragma unroll
+      for (int k = 0; k < kMyLoads; ++k) foff[k] = fast_offset(k);
+      auto issue_fast_tile = [&](const char* tb, uint32_t lds_stage) {
+        if (!loads_here) return;
+#pragma unroll
+        for (int k = 0; k < kMyLoads; ++k) dma16_sbase(tb, foff[k], lds_stage + (uint32_t)(load_slot0(k) * 16));
+      };
+#pragma unroll 1
+      for (int it = 0; it < kStages - 1 && it < ntiles; ++it) {
+        const char* tb = tile_is_fast(it) ? tile_base_of(it) : nullptr;
+        if (tb) issue_fast_tile(tb, lds0 + (it % kStages) * kStageBytes);
+        else load_tile_general(it);
+      }
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(ntiles - 1 < 2 ? ntiles - 1 : 2);
 #pragma unroll 1
@@ -601,10 +652,7 @@ stripe_attn_kernel(Params p) {
           wait_tiles_then_barrier<kMyLoads>(it + 2 < ntiles ? 1 : 0);
           const char* ntb;
           uint32_t nlds;
-          if (start_tile_loads(it + kStages - 1, ntb, nlds) && loads_here) {
-#pragma unroll
-            for (int k = 0; k < kMyLoads; ++k) issue_fast(ntb, nlds, k);
-          }
+          if (start_tile_loads(it + kStages - 1, ntb, nlds)) issue_fast_tile(ntb, nlds);
         }
       }
     }
@@ -672,27 +720,62 @@ stripe_attn_kernel(Params p) {
   }
   lds_barrier();
   if (!pv_wave) return;
+  float* out_base;
+  if (p.splits == 1) out_base = p.o + (int64_t)b * p.M * kDV;
+  else out_base = p.ws_o + ((int64_t)split * p.B + b) * p.M * kDV;
+  out_base += cgrp * kWaveCols * 32;
+  if constexpr (kWS) {
+    // Normalise and store this wave's 128 columns of each row block.  The
+    // accumulator layout gives a lane 16-byte pieces of 4 different 128-byte
+    // lines per row; staging the block through this wave's own slice of the
+    // (now idle) tile ring turns the stores into 512-byte row segments.
+    float* const stage = reinterpret_cast<float*>(smem + cgrp * kEpiWaveBytes);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int Rr = row0 + rb * 32 + n;
-    if (Rr >= p.M) continue;
-    const float inv = inv_lds[rb * 32 + n];
-    float* orow;
-    if (p.splits == 1) orow = p.o + ((int64_t)b * p.M + Rr) * kDV;
-    else orow = p.ws_o + (((int64_t)split * p.B + b) * p.M + Rr) * kDV;
-    orow += cgrp * kWaveCols * 32;
+    for (int rb = 0; rb < RB; ++rb) {
+      const float inv = inv_lds[rb * 32 + n];
 #pragma unroll
-    for (int cb = 0; cb < kWaveCols; ++cb) {
+      for (int cb = 0; cb < kWaveCols; ++cb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float4 v;
-        v.x = oacc[rb][cb][4 * q4 + 0] * inv;
-        v.y = oacc[rb][cb][4 * q4 + 1] * inv;
-        v.z = oacc[rb][cb][4 * q4 + 2] * inv;
-        v.w = oacc[rb][cb][4 * q4 + 3] * inv;
-        *reinterpret_cast<float4*>(orow + cb * 32 + 8 * q4 + 4 * half) = v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float4 v;
+          v.x = oacc[rb][cb][4 * q4 + 0] * inv;
+          v.y = oacc[rb][cb][4 * q4 + 1] * inv;
+          v.z = oacc[rb][cb][4 * q4 + 2] * inv;
+          v.w = oacc[rb][cb][4 * q4 + 3] * inv;
+          *reinterpret_cast<float4*>(stage + n * kEpiPitch + cb * 32 + 8 * q4 + 4 * half) = v;
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
+      lds_wait();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 2 * i + half;
+        const float4 v = *reinterpret_cast<const float4*>(stage + r * kEpiPitch + 4 * n);
+        const int Rr = row0 + rb * 32 + r;
+        if (Rr < p.M) *reinterpret_cast<float4*>(out_base + (int64_t)Rr * kDV + 4 * n) = v;
+      }
+      lds_wait();   // the next block overwrites the slice
+    }
+  } else {
+    // (accumulators in AGPRs, no registers to spare: stored as they lie)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int Rr = row0 + rb * 32 + n;
+      if (Rr >= p.M) continue;
+      const float inv = inv_lds[rb * 32 + n];
+      float* const orow = out_base + (int64_t)Rr * kDV;
+#pragma unroll
+      for (int cb = 0; cb < kWaveCols; ++cb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float4 v;
+          v.x = oacc[rb][cb][4 * q4 + 0] * inv;
+          v.y = oacc[rb][cb][4 * q4 + 1] * inv;
+          v.z = oacc[rb][cb][4 * q4 + 2] * inv;
+          v.w = oacc[rb][cb][4 * q4 + 3] * inv;
+          *reinterpret_cast<float4*>(orow + cb * 32 + 8 * q4 + 4 * half) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
