@@ -52,27 +52,25 @@ constexpr int kRowSlots = kChunks + 1;  // padded row: 73 chunks
 constexpr int kTileSlots = kTile * kRowSlots;  // 2336
 constexpr int kKSteps = kD / 16;        // 36 MFMA k-steps for QK^T
 constexpr int kRowBytes = kD * 2;       // 1152
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;               // PV waves, one per SIMD
+constexpr int kNW = 8;                  // wavefronts per workgroup
+constexpr int kLoaderWaveId = 3;
 constexpr int kWaveCols = kDV / kWaves / 32;   // 4 value-column blocks of 32 per wave
-constexpr int kMaxRB = 4;               // query-row blocks of 32 per workgroup
+constexpr int kMaxRB = 3;               // query-row blocks of 32 per workgroup
 
 // Tile loads: instruction g fills the 64 tile slots from min(64 g, 2272), so
-// 37 instructions cover a tile and a stage is exactly one tile (the last one
-// overlaps the one before it and writes the same bytes again).  With fewer
-// than 4 query-row blocks, the wave without scores to compute issues all 37;
-// otherwise each wave issues 10 (g = 4 j + wave, repeats past 36).
+// the loader wave's 37 instructions cover a tile and a stage is exactly one
+// tile (the last one overlaps the one before it and writes the same bytes
+// again).
 constexpr int kTileInsts = (kTileSlots + 63) / 64;   // 37
-constexpr int kLoads = 10;
 constexpr int kLastBase = kTileSlots - 64;
-static_assert(kLoads * kWaves >= kTileInsts, "tile coverage");
 constexpr int kStageBytes = kTileSlots * 16;    // 37,376
 constexpr int kStages = 4;
 // P^T rows: 4 chunks of 16 bytes, chunk kk*2 + lane half holding k-step kk;
 // chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16-byte
-// accesses of 16 consecutive rows hit disjoint banks.  With fewer than 4 row
-// blocks, P^T, the rescale factors and flags are double-buffered by tile
-// parity (one barrier per tile); with 4, one buffer (two barriers per tile).
+// accesses of 16 consecutive rows hit disjoint banks.  P^T, the rescale
+// factors and flags are double-buffered by tile parity (one barrier per
+// tile).
 constexpr int kPRow = 64;
 constexpr int kPBuf = 3 * 32 * kPRow;                   // one buffer of 96 rows
 constexpr int kPOff = kStages * kStageBytes;
@@ -80,7 +78,7 @@ constexpr int kAlphaOff = kPOff + 2 * kPBuf;            // [2][128] per-row resc
 constexpr int kInvOff = kAlphaOff + 2 * kMaxRB * 32 * 4;   // per-row 1 / l at the end
 constexpr int kFlagOff = kInvOff + kMaxRB * 32 * 4;     // [2][16] one byte per row block: rescale
 constexpr int kLdsBytes = kFlagOff + 32;
-static_assert(kMaxRB * 32 * kPRow <= 2 * kPBuf, "single P^T buffer of 128 rows");
+static_assert(kMaxRB * 32 * kPRow <= kPBuf, "one P^T buffer holds every row");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 // epilogue staging: per PV wave one block of 32 rows x 128 columns (fp32),
 // rows padded by 16 bytes, inside the tile ring
@@ -99,13 +97,6 @@ static_assert(kTileInsts <= 63, "vmcnt range");
 constexpr int kQkAhead = DCP_QK_AHEAD;
 constexpr int kPvAhead = DCP_PV_AHEAD;
 static_assert(kQkAhead >= 1 && kQkAhead <= 15 && kPvAhead >= 1 && kPvAhead <= 7, "LDS counter range");
-// QK^T steps between two of a wave's tile loads slotted under them
-#ifndef DCP_DMA_EVERY
-#define DCP_DMA_EVERY 3
-#endif
-constexpr int kDmaEvery = DCP_DMA_EVERY;
-
-static_assert(kDmaEvery >= 1 && (kLoads - 1) * kDmaEvery < kKSteps, "loads fit under QK^T");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -193,26 +184,6 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // LDS writes of this wave done, then barrier
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// acc *= s for one 32x32 accumulator tile that lives in AGPRs: each element is
-// read, scaled and written back in place through one temporary VGPR, so the
-// rare rescale never needs a second copy of the accumulators.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float sc) {
-#define DCP_SCALE1(i) "v_accvgpr_read_b32 %[t], %[a" #i "]\n\tv_mul_f32 %[t], %[t], %[s]\n\tv_accvgpr_write_b32 %[a" #i "], %[t]\n\t"
-  float t;
-  // leading pad: the accumulators may have just been written by an MFMA
-  asm volatile("s_nop 15\n\t" DCP_SCALE1(0) DCP_SCALE1(1) DCP_SCALE1(2) DCP_SCALE1(3) DCP_SCALE1(4) DCP_SCALE1(5)
-                   DCP_SCALE1(6) DCP_SCALE1(7) DCP_SCALE1(8) DCP_SCALE1(9) DCP_SCALE1(10) DCP_SCALE1(11)
-                       DCP_SCALE1(12) DCP_SCALE1(13) DCP_SCALE1(14) DCP_SCALE1(15)
-               : [t] "=&v"(t), [a0] "+a"(acc[0]), [a1] "+a"(acc[1]), [a2] "+a"(acc[2]),
-                 [a3] "+a"(acc[3]), [a4] "+a"(acc[4]), [a5] "+a"(acc[5]), [a6] "+a"(acc[6]),
-                 [a7] "+a"(acc[7]), [a8] "+a"(acc[8]), [a9] "+a"(acc[9]), [a10] "+a"(acc[10]),
-                 [a11] "+a"(acc[11]), [a12] "+a"(acc[12]), [a13] "+a"(acc[13]), [a14] "+a"(acc[14]),
-                 [a15] "+a"(acc[15])
-               : [s] "v"(sc));
-  asm volatile("s_nop 7" ::: "memory");   // before an MFMA reads the rewritten accumulators
-#undef DCP_SCALE1
-}
-
 __device__ __forceinline__ float other_half(float v) {
   // value of lane l ^ 32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -222,18 +193,15 @@ __device__ __forceinline__ float other_half(float v) {
 // Upper bound on KV chunks per request (each adds one partial to the workspace).
 constexpr int kMaxSplits = 256;
 
-// NW = 8 (up to 3 query-row blocks): two wavefronts per SIMD with split
-// roles -- waves 0..RB-1 compute scores and softmax of one row block each,
-// wave 3 issues the tile loads, waves 4..7 accumulate PV for 128 value
-// columns each -- so one wave's softmax and LDS waits overlap the other
-// wave's MFMAs on the same SIMD; one barrier per tile, P^T double-buffered.
-// NW = 4 (4 row blocks): one wave per SIMD doing scores, softmax and PV for
-// its row block and 128 columns; two barriers per tile.
-template <int RB, bool kAligned, int NW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// Eight wavefronts, two per SIMD, with split roles: waves 0..RB-1 compute
+// the scores and softmax of one block of 32 query rows each, wave 3 issues
+// the tile loads, waves 4..7 accumulate PV for 128 value columns each -- so
+// one wave's softmax and LDS waits overlap the other wave's MFMAs on the
+// same SIMD; one barrier per tile, P^T double-buffered.
+template <int RB, bool kAligned>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * kNW, 64 * kNW), amdgpu_waves_per_eu(2, 2)))
 stripe_attn_kernel(Params p) {
-  static_assert((NW == 8 && RB <= 3) || (NW == 4 && RB == 4), "wave layouts");
-  constexpr bool kWS = NW == 8;        // split roles
+  static_assert(RB >= 1 && RB <= kMaxRB, "query-row blocks");
   __shared__ __align__(16) char smem[kLdsBytes];
 
   const int lane = threadIdx.x & 63;
@@ -241,8 +209,8 @@ stripe_attn_kernel(Params p) {
   const int half = lane >> 5;          // which 8-element k half of an MFMA operand
   const int n = lane & 31;             // query row (MFMA column) owned by this lane
   const bool qk_wave = wave < RB;      // owns query-row block `wave` for QK^T and softmax
-  const bool pv_wave = kWS ? wave >= 4 : true;
-  const int cgrp = kWS ? wave - 4 : wave;   // PV wave: value columns 128*cgrp .. +127
+  const bool pv_wave = wave >= 4;
+  const int cgrp = wave - 4;           // PV wave: value columns 128*cgrp .. +127
 
   // ---- work item: XCD-aware block order (the dispatcher sends block i to XCD
   // i % 8, so consecutive logical items share an XCD and its L2)
@@ -311,13 +279,12 @@ stripe_attn_kernel(Params p) {
     return p.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
   };
 
-  // who issues the tile loads, and how many per tile
-  constexpr bool kLoaderWave = kWS;
-  constexpr int kMyLoads = kLoaderWave ? kTileInsts : kLoads;
-  const bool loads_here = !kLoaderWave || wave == kWaves - 1;
-  // first tile slot that this wave's load j fills
+  // the loader wave issues all 37 loads of a tile
+  constexpr int kMyLoads = kTileInsts;
+  const bool loads_here = wave == kLoaderWaveId;
+  // first tile slot that load j fills
   auto load_slot0 = [&](int j) -> int {
-    const int s0 = 64 * (kLoaderWave ? j : j * kWaves + wave);
+    const int s0 = 64 * j;
     return s0 < kLastBase ? s0 : kLastBase;
   };
   // A tile is "fast" when it is page-aligned and all 32 rows lie in the split:
@@ -332,9 +299,6 @@ stripe_attn_kernel(Params p) {
     uint32_t g = s - ((s * 57457u) >> 22);          // s - floor(s / 73), exact for s < 4096
     g = g < (uint32_t)(kTile * kChunks - 1) ? g : (uint32_t)(kTile * kChunks - 1);
     return g * 16u;
-  };
-  auto issue_fast = [&](const char* tb, uint32_t lds_stage, int k) {
-    dma16_sbase(tb, fast_offset(k), lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane(load_slot0(k) * 16));
   };
   // General loads (live tiles only): partial tiles and pages smaller than a
   // tile.  A slot that holds no token of the split (rows past the split end)
@@ -393,28 +357,11 @@ stripe_attn_kernel(Params p) {
   // tile-relative token of each of this lane's S^T registers (for masking)
   auto tok_of = [&](int i) { return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half; };
 
-  // ---- prologue: tiles 0 .. 2 in flight
-  auto issue_prologue = [&]() {
-#pragma unroll 1
-  for (int it = 0; it < kStages - 1 && it < ntiles; ++it) {
-    const char* tb = tile_is_fast(it) ? tile_base_of(it) : nullptr;
-    if (tb) {
-      const uint32_t lds_stage = lds0 + (it % kStages) * kStageBytes;
-      if (loads_here) {
-#pragma unroll 1
-        for (int k = 0; k < kMyLoads; ++k) issue_fast(tb, lds_stage, k);
-      }
-    } else {
-      load_tile_general(it);
-    }
-  }
-  };
   const float c2 = p.c2;
 
   // S^T = K Q^T of the tile in stage `st` over the 576 latent dims (K
-  // fragments read kQkAhead steps ahead); with `dma`, this wave's loads of
-  // another tile are slotted under the first MFMAs.
-  auto qk = [&](const char* st, const char* ntb, uint32_t nlds, bool dma) -> f32x16 {
+  // fragments read kQkAhead steps ahead).
+  auto qk = [&](const char* st) -> f32x16 {
     // two accumulators (even and odd k-steps): no MFMA waits for the previous one
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     const char* kb = st + kq_off;
@@ -425,14 +372,13 @@ stripe_attn_kernel(Params p) {
     for (int ks = 0; ks < kKSteps; ++ks) {
       if (ks + kQkAhead < kKSteps) kf[ks + kQkAhead] = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + kQkAhead));
       acc[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc[ks & 1], 0, 0, 0);
-      if (dma && ks % kDmaEvery == 0 && ks / kDmaEvery < kLoads) issue_fast(ntb, nlds, ks / kDmaEvery);
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc[0] + acc[1];
   };
 
-  // Online softmax of one tile in base 2 (QK waves), in kParts pieces so that
-  // it can run between the MFMAs of the previous tile's PV.  Scores are masked
+  // Online softmax of one tile in base 2 (QK waves), in kParts pieces.
+  // Scores are masked
   // only on tiles that cross a row's visible limit; the row max is taken on
   // the raw scores (the scale is positive); each weight costs one FMA and one
   // exp2.  The pieces publish the row block's rescale flag and factors (when
@@ -525,10 +471,7 @@ stripe_attn_kernel(Params p) {
         if ((fu >> (8 * rb)) & 0xff) {
           const float alpha = reinterpret_cast<const float*>(smem + kAlphaOff)[buf * kMaxRB * 32 + rb * 32 + n];
 #pragma unroll
-          for (int cb = 0; cb < kWaveCols; ++cb) {
-            if constexpr (kWS) oacc[rb][cb] *= alpha;     // accumulators in VGPRs
-            else scale_acc(oacc[rb][cb], alpha);
-          }
+          for (int cb = 0; cb < kWaveCols; ++cb) oacc[rb][cb] *= alpha;
         }
       }
     }
@@ -536,9 +479,8 @@ stripe_attn_kernel(Params p) {
 
   // O^T += V^T P^T for the tile in stage `st`: this wave's 4 column blocks x
   // RB row blocks x 2 k-steps, V^T fragments by transpose reads (kPvAhead
-  // ahead), P^T fragments of a k-step read half a k-step ahead; with `sm`,
-  // the next tile's softmax pieces run between the MFMAs.
-  auto pv = [&](const char* st, bool sm, int pbuf) {
+  // ahead), P^T fragments of a k-step read half a k-step ahead.
+  auto pv = [&](const char* st, int pbuf) {
     const char* vb = st + v_off;
     bf16x8 pf[RB][2];
     auto read_p = [&](int kk) {
@@ -554,8 +496,7 @@ stripe_attn_kernel(Params p) {
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 2 * kRowSlots * 16));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // (4 row blocks leave room for a shallower prefetch only)
-    constexpr int kAhead = RB >= 4 ? 2 : kPvAhead;
+    constexpr int kAhead = kPvAhead;
     bf16x8 vf[kFrags];
 #pragma unroll
     for (int f = 0; f < kAhead && f < kFrags; ++f) vf[f] = vfrag(f);
@@ -567,15 +508,9 @@ stripe_attn_kernel(Params p) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pf[rb][kk], oacc[rb][cb], 0, 0, 0);
-        const int step = f * RB + rb;
-        if (sm && step < kParts) softmax_part(step);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the pieces left when there are fewer MFMAs than pieces
-#pragma unroll
-    for (int part = kFrags * RB; part < kParts; ++part)
-      if (sm) softmax_part(part);
   };
 
   // next tile's loads: the general path now, the fast path returned for the caller
@@ -587,7 +522,7 @@ stripe_attn_kernel(Params p) {
     return fast && ntb != nullptr;
   };
 
-  if constexpr (kWS) {
+  {
     // ---- split roles.  Every role passes the same barriers: one before the
     // loop (tile 0 landed) and one per tile (A: tile it+1 landed, every wave
     // done with tile it-1, P^T and factors of tile it visible).
@@ -598,7 +533,7 @@ stripe_attn_kernel(Params p) {
       load_q();
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(0);
-        sacc = qk(smem, nullptr, 0, false);
+        sacc = qk(smem);
         vis = lim - row_lo;
         sbuf = 0;
         softmax_tile(true);
@@ -607,7 +542,7 @@ stripe_attn_kernel(Params p) {
         for (int it = 0; it < ntiles; ++it) {
           wait_tiles_then_barrier<kMyLoads>(0);
           if (it + 1 < ntiles) {
-            sacc = qk(smem + ((it + 1) % kStages) * kStageBytes, nullptr, 0, false);
+            sacc = qk(smem + ((it + 1) % kStages) * kStageBytes);
             vis = lim - (row_lo + (it + 1) * kTile);
             sbuf = (it + 1) & 1;
             softmax_tile(false);
@@ -623,7 +558,7 @@ stripe_attn_kernel(Params p) {
         for (int it = 0; it < ntiles; ++it) {
           wait_tiles_then_barrier<kMyLoads>(0);
           rescale(it & 1);
-          pv(smem + (it % kStages) * kStageBytes, false, it & 1);
+          pv(smem + (it % kStages) * kStageBytes, it & 1);
         }
       }
     } else {
@@ -656,49 +591,6 @@ stripe_attn_kernel(Params p) {
         }
       }
     }
-  } else {
-    // ---- one wave per SIMD, every wave in every role
-    load_q();
-    init_o();
-    issue_prologue();
-    // tile 0: its scores and P^T (nothing to overlap yet)
-    if (ntiles > 0) {
-      wait_tiles_then_barrier<kMyLoads>(ntiles - 1 < 2 ? ntiles - 1 : 2);
-      sacc = qk(smem, nullptr, 0, false);
-      vis = lim - row_lo;
-#pragma unroll
-      for (int part = 0; part < kParts; ++part) softmax_part(part);
-    }
-    // steady state: iteration it computes PV of tile it and the scores and
-    // softmax of tile it+1, while tile it+3 streams in (into the stage of
-    // tile it-1) and tile it+2 is still landing
-#pragma unroll 1
-    for (int it = 0; it < ntiles; ++it) {
-      const bool has_next = it + 1 < ntiles;
-      // (A) tile it+1 is in LDS and every wave is done with tile it-1 (its
-      // stage and P^T)
-      wait_tiles_then_barrier<kMyLoads>(it + 2 < ntiles ? 1 : 0);
-      const char* ntb;
-      uint32_t nlds;
-      const bool dma_fast = start_tile_loads(it + kStages - 1, ntb, nlds);
-      if (dma_fast && !has_next) {
-#pragma unroll
-        for (int k = 0; k < kMyLoads; ++k) issue_fast(ntb, nlds, k);
-      }
-      write_p(0);                                      // P^T of tile it
-      rescale(0);
-      if (has_next) {
-        // this wave's loads of tile it+3 go under its QK^T MFMAs
-        sacc = qk(smem + ((it + 1) % kStages) * kStageBytes, ntb, nlds, dma_fast);
-        vis = lim - (row_lo + (it + 1) * kTile);
-      }
-      // (B) P^T of tile it is visible and every wave holds its factors: the
-      // softmax of tile it+1 may publish its own
-      lds_barrier();
-      // PV of tile it, with the softmax of tile it+1 between its MFMAs
-      sbuf = 0;
-      pv(smem + (it % kStages) * kStageBytes, has_next, 0);
-    }
   }
   // every load has landed by now; make that explicit before the LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -724,7 +616,7 @@ stripe_attn_kernel(Params p) {
   if (p.splits == 1) out_base = p.o + (int64_t)b * p.M * kDV;
   else out_base = p.ws_o + ((int64_t)split * p.B + b) * p.M * kDV;
   out_base += cgrp * kWaveCols * 32;
-  if constexpr (kWS) {
+  {
     // Normalise and store this wave's 128 columns of each row block.  The
     // accumulator layout gives a lane 16-byte pieces of 4 different 128-byte
     // lines per row; staging the block through this wave's own slice of the
@@ -755,28 +647,6 @@ stripe_attn_kernel(Params p) {
       }
       lds_wait();   // the next block overwrites the slice
     }
-  } else {
-    // (accumulators in AGPRs, no registers to spare: stored as they lie)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int Rr = row0 + rb * 32 + n;
-      if (Rr >= p.M) continue;
-      const float inv = inv_lds[rb * 32 + n];
-      float* const orow = out_base + (int64_t)Rr * kDV;
-#pragma unroll
-      for (int cb = 0; cb < kWaveCols; ++cb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float4 v;
-          v.x = oacc[rb][cb][4 * q4 + 0] * inv;
-          v.y = oacc[rb][cb][4 * q4 + 1] * inv;
-          v.z = oacc[rb][cb][4 * q4 + 2] * inv;
-          v.w = oacc[rb][cb][4 * q4 + 3] * inv;
-          *reinterpret_cast<float4*>(orow + cb * 32 + 8 * q4 + 4 * half) = v;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
   }
 }
 
@@ -798,7 +668,17 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   const int64_t max_rows = (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
   if ((int64_t)a->layout.n_stripes * a->layout.interleave > 0x7fffffff) return DCP_EUNSUPPORTED;
-  pl->RB = M <= 32 ? 1 : (M <= 64 ? 2 : (M <= 96 ? 3 : 4));
+  // query rows per workgroup: up to 3 blocks of 32; above 96 rows the rows
+  // are cut into groups (the workgroups of one group run side by side on
+  // one XCD and share each KV tile through its L2), with the block count
+  // that pads the fewest rows
+  if (M <= 32 * kMaxRB) {
+    pl->RB = (int)ceil_div(M, 32);
+  } else {
+    pl->RB = kMaxRB;
+    for (int rb = kMaxRB - 1; rb >= 1; --rb)
+      if (ceil_div(M, 32 * rb) * 32 * rb < ceil_div(M, 32 * pl->RB) * 32 * pl->RB) pl->RB = rb;
+  }
   pl->mgroups = (int)ceil_div(M, 32 * pl->RB);
   const int64_t tiles_max = ceil_div(max_rows, kTile);
   int64_t splits = a->num_splits;
@@ -808,8 +688,10 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
+    // one workgroup per compute unit, all in one round: a grid slightly
+    // larger than the CU count would run its last few workgroups alone
     const int64_t base = (int64_t)a->batch * pl->mgroups;
-    splits = ceil_div(cus, base);
+    splits = base < cus ? cus / base : 1;
   }
   if (splits > tiles_max) splits = tiles_max;
   if (splits > kMaxSplits) splits = kMaxSplits;
@@ -826,11 +708,10 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
 
 template <int RB>
 int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
-  constexpr int NW = RB == 4 ? 4 : 8;
   if (prm.P % kTile == 0)
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, true>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   else
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, false>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   return launch_status();
 }
 
@@ -890,8 +771,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   switch (pl.RB) {
     case 1: r = launch<1>(prm, blocks, s); break;
     case 2: r = launch<2>(prm, blocks, s); break;
-    case 3: r = launch<3>(prm, blocks, s); break;
-    default: r = launch<4>(prm, blocks, s); break;
+    default: r = launch<3>(prm, blocks, s); break;
   }
   if (r != DCP_OK || pl.splits == 1) return r;
   // the chunks of each stripe row merge exactly like stripes (partial lse in base 2)

@@ -23,39 +23,40 @@ import gpu_helpers as H
 
 TILE, ROW_SLOTS, CHUNKS = 32, 73, 72
 TILE_SLOTS = TILE * ROW_SLOTS
-WAVES, LOADS, STAGES = 4, 10, 4
+STAGES, MAX_RB = 4, 3
 LAST_BASE = TILE_SLOTS - 64
 
 
 TILE_INSTS = -(-TILE_SLOTS // 64)                 # 37
 
 
-def load_slots(loader_wave=False):
-    """Tile slot of every lane of every load instruction of the workgroup.  With a
-    loader wave (fewer than 4 query-row blocks) it issues instructions g = 0..36;
-    otherwise wave w's load k is g = 4k + w.  Instruction g fills the 64 slots
-    from min(64 g, 2272)."""
-    if loader_wave:
-        g = np.arange(TILE_INSTS)
-    else:
-        g = (np.arange(LOADS)[:, None] * WAVES + np.arange(WAVES)[None, :]).reshape(-1)
+def load_slots():
+    """Tile slot of every lane of every load instruction of the workgroup: the
+    loader wave issues instructions g = 0..36, instruction g filling the 64
+    slots from min(64 g, 2272)."""
+    g = np.arange(TILE_INSTS)
     s0 = np.minimum(64 * g, LAST_BASE)
     return (s0[:, None] + np.arange(64)[None, :]).reshape(-1), s0
 
 
-@pytest.mark.parametrize("loader_wave", [False, True])
-def test_loads_cover_every_slot_of_one_stage(loader_wave):
-    s, s0 = load_slots(loader_wave)
+def test_loads_cover_every_slot_of_one_stage():
+    s, s0 = load_slots()
     assert s.min() == 0 and s.max() == TILE_SLOTS - 1            # never past the stage
     assert set(s.tolist()) == set(range(TILE_SLOTS))             # every slot written
     assert len(s0) <= 63                                         # one tile fits the load counter
 
 
 def plan(B, M, bt_cols, P, cus=256, num_splits=0):
-    W = 1 if M <= 32 else 2 if M <= 64 else 3 if M <= 96 else 4     # query-row blocks of 32
+    # query-row blocks of 32 per workgroup: up to 3; above 96 rows, the count
+    # that pads the fewest rows when the rows are cut into groups
+    if M <= 32 * MAX_RB:
+        W = -(-M // 32)
+    else:
+        W = min(range(MAX_RB, 0, -1), key=lambda rb: (-(-M // (32 * rb)) * 32 * rb, -rb))
     mgroups = -(-M // (32 * W))
     tiles_max = -(-(bt_cols * P) // TILE)
-    splits = num_splits or -(-cus // (B * mgroups))
+    base = B * mgroups
+    splits = num_splits or (cus // base if base < cus else 1)
     splits = max(1, min(splits, tiles_max, 256))
     per = -(-tiles_max // splits)
     splits = -(-tiles_max // per)
@@ -69,9 +70,9 @@ def count_rows(x, N, I, r):
     return np.where(x <= 0, 0, (x // rnd) * I + rem)
 
 
-def fast_chunks(plant=None, loader_wave=False):
+def fast_chunks(plant=None):
     """Global chunk (0..2303 of the tile's 36,864 contiguous bytes) each slot of a fast tile loads."""
-    s, _ = load_slots(loader_wave)
+    s, _ = load_slots()
     q = s * 57457 >> 22
     assert (q == s // 73).all()                       # the kernel's division by 73
     g = s - q
@@ -80,9 +81,9 @@ def fast_chunks(plant=None, loader_wave=False):
     return g
 
 
-def general_rows_chunks(rows_left, plant=None, loader_wave=False):
+def general_rows_chunks(rows_left, plant=None):
     """(tile row, chunk) each slot of a general (partial or unaligned) tile loads."""
-    s, _ = load_slots(loader_wave)
+    s, _ = load_slots()
     tt, c = s // ROW_SLOTS, s % ROW_SLOTS
     if plant != "no_row_substitute":
         tt = np.where(tt < rows_left, tt, 0)
@@ -133,8 +134,7 @@ def check_workload(w, I, plant=None, num_splits=0):
         tab = tables[r]
         B, cols = tab.shape
         W, mgroups, splits, split_rows = plan(B, M, cols, P, num_splits=num_splits)
-        loader = W < WAVES
-        g = fast_chunks(plant, loader)
+        g = fast_chunks(plant)
         max_vis = count_rows(lens, N, I, r)
         for b in range(B):
             for sp in range(splits):
@@ -151,7 +151,7 @@ def check_workload(w, I, plant=None, num_splits=0):
                         assert J % P + TILE <= P                   # the tile lies inside its page
                         assert g.min() >= 0 and g.max() < TILE * CHUNKS, (w.name, r, b, sp, it)
                         continue
-                    tt, c = general_rows_chunks(rows_left, plant, loader)
+                    tt, c = general_rows_chunks(rows_left, plant)
                     j = J + tt
                     assert (j < row_hi).all(), (w.name, r, b, sp, it, "row past the split")
                     pi = j // P
