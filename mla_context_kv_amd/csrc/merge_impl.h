@@ -35,41 +35,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at
-// lse_parts[r * rows + i].  in_base2 / out_base2 select the base of the input
-// and output lse.  One wavefront per row: the lanes first hold the parts' lse
+// Merge of one row by one wavefront.  Part r of the row: o at
+// o_parts[r * stride * v4 ...], lse at lse_parts[r * stride]; the result goes
+// to o_row[0 .. v4) and *lse_out (when not NULL).  in_base2 / out_base2
+// select the base of the input and output lse.  The lanes first hold the parts' lse
 // (64 parts at a time) for the max and the weight sum, then every lane merges
 // two 16-byte column slices, with the loads of 8 parts in flight before their
 // FMAs.  Parts of weight zero (lse = -inf, or an underflowed weight) are never
 // read.
-__global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
-lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__ o_parts,
-                 const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
-                 float4* __restrict__ o, float* __restrict__ lse) {
-  // XCD-aware order: the dispatcher sends block i to XCD i % 8, so giving
-  // each XCD a contiguous range of rows keeps a request's rows on one XCD --
-  // the one whose L2 holds the split partials the attention kernel (same
-  // mapping) just wrote for it.
-  int64_t bid = blockIdx.x;
-  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-  const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
+__device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t v4,
+                                              const float4* __restrict__ o_parts,
+                                              const float* __restrict__ lse_parts, int32_t in_base2,
+                                              int32_t out_base2, float4* __restrict__ o_row,
+                                              float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
   // weights are base^(lse_r - m): the difference is taken in the input base
   // (exact for nearby values) and only then scaled into base 2 for exp2
   const float to2 = in_base2 ? 1.0f : kLog2e;
   float m = -INFINITY;
   for (int r0 = 0; r0 < N; r0 += 64)
-    if (r0 + lane < N) m = fmaxf(m, lse_parts[(int64_t)(r0 + lane) * rows + row]);
+    if (r0 + lane < N) m = fmaxf(m, lse_parts[(int64_t)(r0 + lane) * stride]);
   m = wave_max(m);
   if (m == -INFINITY) {
-    for (int c = lane; c < v4; c += 64) o[row * v4 + c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse && lane == 0) lse[row] = -INFINITY;
+    for (int c = lane; c < v4; c += 64) o_row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse_out && lane == 0) *lse_out = -INFINITY;
     return;
   }
   float wsum = 0.f;
   for (int r0 = 0; r0 < N; r0 += 64) {
-    const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * rows + row] : -INFINITY;
+    const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * stride] : -INFINITY;
     wsum += x == -INFINITY ? 0.f : exp2f((x - m) * to2);
   }
   wsum = wave_sum(wsum);
@@ -79,7 +73,7 @@ lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__
     const bool in0 = c0 < v4, in1 = c1 < v4;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
     for (int r0 = 0; r0 < N; r0 += 64) {
-      const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * rows + row] : -INFINITY;
+      const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * stride] : -INFINITY;
       const float w = x == -INFINITY ? 0.f : exp2f((x - m) * to2) * inv;   // lane k: weight of part r0 + k
       const int nr = min(64, N - r0);
       for (int u = 0; u < nr; u += 8) {
@@ -90,7 +84,7 @@ lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__
           wu[k] = u + k < nr ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + k)) : 0.f;
           v0[k] = v1[k] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (wu[k] != 0.f) {
-            const float4* src = o_parts + ((int64_t)(r0 + u + k) * rows + row) * v4;
+            const float4* src = o_parts + (int64_t)(r0 + u + k) * stride * v4;
             if (in0) v0[k] = src[c0];
             if (in1) v1[k] = src[c1];
           }
@@ -108,15 +102,31 @@ lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__
         }
       }
     }
-    if (in0) o[row * v4 + c0] = a0;
-    if (in1) o[row * v4 + c1] = a1;
+    if (in0) o_row[c0] = a0;
+    if (in1) o_row[c1] = a1;
   }
-  if (lse && lane == 0) {
+  if (lse_out && lane == 0) {
     // lse = m + log_base(sum w), written in the output base
     const float lw2 = log2f(wsum);                          // log2 of the weight sum
     const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
-    lse[row] = m_out + (out_base2 ? lw2 : lw2 * kLn2);
+    *lse_out = m_out + (out_base2 ? lw2 : lw2 * kLn2);
   }
+}
+
+// Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at
+// lse_parts[r * rows + i].  XCD-aware order: the dispatcher sends block i to
+// XCD i % 8, so giving each XCD a contiguous range of rows keeps a request's
+// rows on one XCD.
+__global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
+lse_merge_kernel(int32_t N, int64_t rows, int32_t v4, const float4* __restrict__ o_parts,
+                 const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
+                 float4* __restrict__ o, float* __restrict__ lse) {
+  int64_t bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
+  if (row >= rows) return;
+  merge_one_row(N, rows, v4, o_parts + row * v4, lse_parts + row, in_base2, out_base2, o + row * v4,
+                lse ? lse + row : nullptr);
 }
 
 inline int launch_lse_merge(int32_t N, int64_t rows, int32_t v_dim, const float* o_parts,

@@ -13,31 +13,34 @@
 // speculative decoding": global lengths keep causality).
 //
 // How (MI355X / gfx950):
-//  * One workgroup of 4 wavefronts (one per SIMD) per (request, KV split,
-//    group of up to 128 query rows = RB blocks of 32).  Heads are the N side
-//    of the MFMA tiles, so one latent tile in LDS serves all of them.
+//  * One workgroup of 8 wavefronts (two per SIMD) per (chunk of a request's
+//    rows, group of up to 96 query rows = RB blocks of 32).  Heads are the N
+//    side of the MFMA tiles, so one latent tile in LDS serves all of them.
+//    Waves 0..RB-1 compute scores and softmax of one row block each, wave 3
+//    issues the tile loads, waves 4..7 accumulate PV for 128 value columns.
 //  * KV tiles of 32 tokens are streamed HBM -> LDS with 16-byte direct-to-LDS
-//    loads into a 4-stage ring; a tile's token rows are padded to 73 16-byte
-//    chunks so that the LDS access patterns below are bank-conflict free.
-//    The same LDS tile is the key (QK^T) and the value (PV): every KV byte is
-//    read from HBM once.
+//    loads into a 4-stage ring (two tiles in flight while one is scored and
+//    the previous one accumulated); a tile's token rows are padded to 73
+//    16-byte chunks so that the LDS access patterns below are bank-conflict
+//    free.  The same LDS tile is the key (QK^T) and the value (PV): every KV
+//    byte is read from HBM once.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32 query
-//    rows, K = 576 in 36 steps): wave w < RB owns query-row block w, whose Q
+//    rows, K = 576 in 36 steps): score wave w owns query-row block w, whose Q
 //    stays in its registers for the whole kernel.
-//  * Online softmax in base 2 (scale * log2(e) folded in) by the same wave,
-//    row max over the tile with one lane-half exchange; the reference max
-//    only moves when it grows by more than 2^8, so the O rescale is rare and
-//    still exact.  P (bf16) goes to a small LDS buffer.
+//  * Online softmax in base 2 (scale * log2(e) folded in) by the same wave;
+//    the reference max only moves when it grows by more than 2^8, so the O
+//    rescale is rare and still exact, and a tile whose weights all stay below
+//    2^8 never computes its max.  P (bf16) goes to a small LDS buffer.
 //  * O^T += V^T P^T with the same MFMA (M = 32 value columns, N = 32 query
-//    rows, K = 16 tokens), split by value columns: wave w owns columns
-//    128w .. 128w+127 of every row block, so each V^T fragment (transpose
-//    read of the token-major tile) feeds RB MFMAs and the tile's values are
-//    read from LDS once per workgroup, not once per row block.
-//  * Split-KV: when there are fewer (request, row group) items than compute
-//    units, each request's stripe is cut into equal chunks of whole tiles; a
-//    chunk writes its (o, lse) partial to the workspace and a second launch
-//    merges the chunks with the same exact LSE merge as across stripes (the
-//    chunks are a disjoint partition of the stripe's rows).
+//    rows, K = 16 tokens), split by value columns, so each V^T fragment
+//    (transpose read of the token-major tile) feeds RB MFMAs and the tile's
+//    values are read from LDS once per workgroup, not once per row block.
+//  * Work list: every request's rows are cut into chunks of whole tiles,
+//    balanced over the batch so that the grid is one round of workgroups
+//    (ragged lengths included).  A request's only chunk writes (o_r, lse_r)
+//    itself; otherwise each chunk writes an (o, lse) partial and a second
+//    launch merges a request's chunks with the same exact LSE merge as across
+//    stripes (the chunks are a disjoint partition of the stripe's rows).
 #include "dcp_common.h"
 #include "merge_impl.h"
 
@@ -111,7 +114,10 @@ __device__ __align__(16) uint4 g_zero_row[kRowSlots];
 struct Params {
   int32_t N, I, P, rank;
   int32_t B, q_len, H, M;          // M = q_len * H query rows per request
-  int32_t RB, mgroups, splits, split_rows;
+  int32_t RB, mgroups;
+  int32_t slots;                    // chunk slots of the workspace (grid = slots * mgroups)
+  int32_t forced_splits;            // > 0: that many chunks per request; 0: balanced chunks
+  int32_t target_chunks;            // balanced: at most this many chunks (when >= B)
   const __bf16* q;
   const char* pool;
   int64_t num_pages;
@@ -120,10 +126,11 @@ struct Params {
   const int32_t* seq_len;
   float c2;                         // scale * log2(e)
   int32_t out_base2;
-  float* o;                         // final outputs (splits == 1)
+  float* o;                         // final outputs (requests cut into one chunk)
   float* lse;
-  float* ws_o;                      // split partials [splits][B][M][512], lse2 [splits][B][M]
+  float* ws_o;                      // chunk partials [slots][M][512], lse2 [slots][M]
   float* ws_lse;
+  int32_t* table;                   // chunks per request [B], first chunk of each request [B]
   int32_t* status;
 };
 
@@ -134,6 +141,124 @@ __device__ __forceinline__ int32_t count_rows(int32_t x, int32_t N, int32_t I, i
   int32_t rem = x % round - r * I;
   rem = rem < 0 ? 0 : (rem > I ? I : rem);
   return (x / round) * I + rem;
+}
+
+__device__ __forceinline__ int32_t wave_sum_i(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max_i(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
+  return v;
+}
+__device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Work list of one stripe call.  Request b's local rows (what its last query
+// sees) make tiles_b tiles of 32; the request is cut into n_b >= 1 chunks of
+// cs_b = ceil(tiles_b / n_b) tiles (an empty request gets one empty chunk,
+// which writes its zero output).  With forced_splits = s: n_b = number of
+// chunks of ceil(tiles_b / s) tiles.  Otherwise the chunks are balanced over
+// the whole batch: n_b = ceil(tiles_b / C) for the smallest of a few
+// candidate chunk lengths C that keeps the total under target_chunks (the
+// last candidate, ceil(total / (target - B)), always does).  Chunks are
+// numbered request by request; chunk c is this workgroup's (every wave finds
+// it with wave-wide scans; the workgroup of chunk 0 also writes the table the
+// chunk combine reads).
+struct WorkItem {
+  int32_t b, k, n, cs, rows;        // request, chunk of it, its chunks, chunk length (tiles), rows
+  bool live;
+};
+
+__device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
+  const int lane = threadIdx.x & 63;
+  // local rows and tiles of request b; the first 256 requests' are loaded
+  // once (all loads in flight together) and kept in registers
+  constexpr int kCached = 4;
+  int32_t rows_c[kCached];
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) {
+    const int32_t b = 64 * j + lane;
+    rows_c[j] = b < p.B ? p.seq_len[b] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) rows_c[j] = count_rows(rows_c[j], p.N, p.I, p.rank);
+  auto rows_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
+    const int32_t b = b0 + lane;
+    if (b0 < 64 * kCached) {
+      int32_t r = rows_c[0];
+#pragma unroll
+      for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? rows_c[j] : r;
+      return r;
+    }
+    return b < p.B ? count_rows(p.seq_len[b], p.N, p.I, p.rank) : 0;
+  };
+  int32_t C = 1;
+  if (p.forced_splits == 0) {
+    int32_t total = 0, maxt = 0;
+    for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
+      const int32_t t = cdiv(rows_of(b0), 32);
+      total += t;
+      maxt = max(maxt, t);
+    }
+    total = wave_sum_i(total);
+    maxt = max(wave_max_i(maxt), 1);
+    auto chunks_for = [&](int32_t len) -> int32_t {
+      int32_t nc = 0;
+      for (int32_t b0 = 0; b0 < p.B; b0 += 64)
+        nc += b0 + lane < p.B ? max(cdiv(cdiv(rows_of(b0), 32), len), 1) : 0;
+      return wave_sum_i(nc);
+    };
+    const int32_t target = p.target_chunks;
+    if (target <= p.B) {
+      C = maxt;                                    // one chunk per request
+    } else {
+      C = max(cdiv(total, target), 1);
+      const int32_t T0 = chunks_for(C);
+      if (T0 > target) {
+        const int32_t C1 = cdiv(C * T0, target);
+        C = chunks_for(C1) <= target ? C1 : max(cdiv(total, target - p.B), 1);
+      }
+    }
+  }
+  WorkItem w{0, 0, 0, 0, 0, false};
+  int32_t carry = 0;
+  for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
+    const int32_t b = b0 + lane;
+    const int32_t rows = rows_of(b0);
+    const int32_t t = cdiv(rows, 32);
+    int32_t nb = 0;
+    if (b < p.B) {
+      if (p.forced_splits > 0) nb = t > 0 ? cdiv(t, cdiv(t, p.forced_splits)) : 1;
+      else nb = max(cdiv(t, C), 1);
+    }
+    int32_t x = nb;                                // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    const int32_t incl = carry + x, excl = incl - nb;
+    if (write_table && b < p.B) {
+      p.table[b] = nb;
+      p.table[p.B + b] = excl;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(b < p.B && excl <= c && c < incl);
+    if (hit != 0 && !w.live) {
+      const int l = __builtin_ctzll(hit);
+      w.live = true;
+      w.b = b0 + l;
+      w.k = c - __builtin_amdgcn_readlane(excl, l);
+      w.n = __builtin_amdgcn_readlane(nb, l);
+      w.rows = __builtin_amdgcn_readlane(rows, l);
+      const int32_t tl = __builtin_amdgcn_readlane(t, l);
+      w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
+      if (!write_table) break;
+    }
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return w;
 }
 
 // MFMA row m of the QK^T A operand <-> token of the tile.  Within each group
@@ -190,8 +315,6 @@ __device__ __forceinline__ float other_half(float v) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// Upper bound on KV chunks per request (each adds one partial to the workspace).
-constexpr int kMaxSplits = 256;
 
 // Eight wavefronts, two per SIMD, with split roles: waves 0..RB-1 compute
 // the scores and softmax of one block of 32 query rows each, wave 3 issues
@@ -218,14 +341,16 @@ stripe_attn_kernel(Params p) {
   const int G = gridDim.x;
   if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
   const int mg = id % p.mgroups;
-  const int rest = id / p.mgroups;
-  const int split = rest % p.splits;
-  const int b = rest / p.splits;
+  const int32_t chunk = id / p.mgroups;
+  const WorkItem wi = find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
+  if (!wi.live) return;                // past the last chunk (the same in every wave)
+  const int b = wi.b;
+  const bool direct = wi.n == 1;       // the request's only chunk writes the output itself
 
   const int32_t S_b = p.seq_len[b];
-  const int32_t max_vis = count_rows(S_b, p.N, p.I, p.rank);   // rows the last query sees
-  const int32_t row_lo = split * p.split_rows;
-  int32_t row_hi = row_lo + p.split_rows;
+  const int32_t max_vis = wi.rows;     // rows the last query sees
+  const int32_t row_lo = wi.k * wi.cs * kTile;
+  int32_t row_hi = row_lo + wi.cs * kTile;
   row_hi = row_hi < max_vis ? row_hi : max_vis;
   const int ntiles = row_hi > row_lo ? (row_hi - row_lo + kTile - 1) / kTile : 0;
   const int row0 = mg * 32 * RB;       // first query row of this workgroup
@@ -605,16 +730,16 @@ stripe_attn_kernel(Params p) {
     if (half == 0) {
       inv_lds[wave * 32 + n] = inv;
       if (valid) {
-        if (p.splits == 1) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
-        else p.ws_lse[((int64_t)split * p.B + b) * p.M + R] = lse2;
+        if (direct) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
+        else p.ws_lse[(int64_t)chunk * p.M + R] = lse2;
       }
     }
   }
   lds_barrier();
   if (!pv_wave) return;
   float* out_base;
-  if (p.splits == 1) out_base = p.o + (int64_t)b * p.M * kDV;
-  else out_base = p.ws_o + ((int64_t)split * p.B + b) * p.M * kDV;
+  if (direct) out_base = p.o + (int64_t)b * p.M * kDV;
+  else out_base = p.ws_o + (int64_t)chunk * p.M * kDV;
   out_base += cgrp * kWaveCols * 32;
   {
     // Normalise and store this wave's 128 columns of each row block.  The
@@ -651,8 +776,11 @@ stripe_attn_kernel(Params p) {
 }
 
 struct Plan {
-  int RB, mgroups, splits, split_rows;
-  size_t ws_bytes;
+  int RB, mgroups;
+  int64_t slots;           // chunk slots; the grid has slots * mgroups workgroups
+  int32_t forced, target;  // Params::forced_splits, Params::target_chunks
+  bool combine;            // some request may have several chunks
+  size_t ws_bytes, table_off;
 };
 
 int make_plan(const dcp_attn_args* a, Plan* pl) {
@@ -681,29 +809,54 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   }
   pl->mgroups = (int)ceil_div(M, 32 * pl->RB);
   const int64_t tiles_max = ceil_div(max_rows, kTile);
-  int64_t splits = a->num_splits;
-  if (splits == 0) {
+  if (a->num_splits > 0) {
+    // a fixed number of chunks per request
+    pl->forced = (int32_t)(a->num_splits < tiles_max ? a->num_splits : tiles_max);
+    pl->target = 0;
+    pl->slots = (int64_t)a->batch * pl->forced;
+  } else {
+    // balanced chunks: one workgroup per compute unit, all in one round
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    // one workgroup per compute unit, all in one round: a grid slightly
-    // larger than the CU count would run its last few workgroups alone
-    const int64_t base = (int64_t)a->batch * pl->mgroups;
-    splits = base < cus ? cus / base : 1;
+    pl->forced = 0;
+    pl->target = cus / pl->mgroups > 1 ? cus / pl->mgroups : 1;
+    pl->slots = pl->target > a->batch ? pl->target : a->batch;
   }
-  if (splits > tiles_max) splits = tiles_max;
-  if (splits > kMaxSplits) splits = kMaxSplits;
-  if (splits < 1) splits = 1;
-  const int64_t tiles_per_split = ceil_div(tiles_max, splits);
-  splits = ceil_div(tiles_max, tiles_per_split);
-  pl->split_rows = (int)(tiles_per_split * kTile);
-  pl->splits = (int)splits;
-  if ((int64_t)a->batch * pl->splits * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
-  // partials (o, lse) of every split
-  pl->ws_bytes = pl->splits > 1 ? (size_t)pl->splits * a->batch * M * (kDV + 1) * sizeof(float) : 0;
+  if (pl->slots * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
+  pl->combine = pl->forced != 1;
+  // chunk partials (o, base-2 lse) and the chunk table
+  if (pl->combine) {
+    const size_t part = (size_t)pl->slots * M * (kDV + 1) * sizeof(float);
+    pl->table_off = (part + 255) & ~(size_t)255;
+    pl->ws_bytes = pl->table_off + (size_t)2 * a->batch * sizeof(int32_t);
+  } else {
+    pl->table_off = 0;
+    pl->ws_bytes = 0;
+  }
   return DCP_OK;
+}
+
+// Merge of each request's chunks (one wavefront per output row): requests cut
+// into one chunk were written by the attention kernel itself and are left
+// alone; the chunks partition the request's rows, so their partials merge
+// exactly like stripes (base-2 partial lse).
+__global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
+chunk_combine_kernel(int32_t B, int32_t M, int32_t v4, const int32_t* __restrict__ table,
+                     const float4* __restrict__ ws_o, const float* __restrict__ ws_lse, int32_t out_base2,
+                     float4* __restrict__ o, float* __restrict__ lse) {
+  int64_t bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
+  if (row >= (int64_t)B * M) return;
+  const int32_t b = (int32_t)(row / M), m = (int32_t)(row % M);
+  const int32_t n = table[b];
+  if (n <= 1) return;
+  const int64_t c0 = table[B + b];
+  merge_one_row(n, M, v4, ws_o + (c0 * M + m) * v4, ws_lse + c0 * M + m, 1, out_base2, o + row * v4,
+                lse + row);
 }
 
 template <int RB>
@@ -750,8 +903,9 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.M = (int32_t)M;
   prm.RB = pl.RB;
   prm.mgroups = pl.mgroups;
-  prm.splits = pl.splits;
-  prm.split_rows = pl.split_rows;
+  prm.slots = (int32_t)pl.slots;
+  prm.forced_splits = pl.forced;
+  prm.target_chunks = pl.target;
   prm.q = (const __bf16*)a->q;
   prm.pool = (const char*)a->pool;
   prm.num_pages = a->num_pages;
@@ -762,10 +916,11 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.out_base2 = a->lse_base;
   prm.o = a->o;
   prm.lse = a->lse;
-  prm.ws_o = pl.splits > 1 ? (float*)a->workspace : nullptr;
-  prm.ws_lse = pl.splits > 1 ? prm.ws_o + (size_t)pl.splits * a->batch * M * kDV : nullptr;
+  prm.ws_o = pl.combine ? (float*)a->workspace : nullptr;
+  prm.ws_lse = pl.combine ? prm.ws_o + (size_t)pl.slots * M * kDV : nullptr;
+  prm.table = pl.combine ? (int32_t*)((char*)a->workspace + pl.table_off) : nullptr;
   prm.status = a->status;
-  const int64_t blocks = (int64_t)a->batch * pl.splits * pl.mgroups;
+  const int64_t blocks = pl.slots * pl.mgroups;
   hipStream_t s = (hipStream_t)stream;
   int r;
   switch (pl.RB) {
@@ -773,7 +928,10 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
     case 2: r = launch<2>(prm, blocks, s); break;
     default: r = launch<3>(prm, blocks, s); break;
   }
-  if (r != DCP_OK || pl.splits == 1) return r;
-  // the chunks of each stripe row merge exactly like stripes (partial lse in base 2)
-  return launch_lse_merge(pl.splits, (int64_t)a->batch * M, kDV, prm.ws_o, prm.ws_lse, 1, a->lse_base, a->o, a->lse, s);
+  if (r != DCP_OK || !pl.combine) return r;
+  const int64_t rows = (int64_t)a->batch * M;
+  hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)ceil_div(rows, kMergeRowsPerBlock)),
+                     dim3(64 * kMergeRowsPerBlock), 0, s, a->batch, (int32_t)M, kDV / 4, prm.table,
+                     (const float4*)prm.ws_o, prm.ws_lse, a->lse_base, (float4*)a->o, a->lse);
+  return launch_status();
 }

@@ -106,7 +106,8 @@ def test_stripe_attn_workspace_size_and_missing_workspace():
     a = _args(num_splits=3, bt_cols=100)
     n = ctypes.c_size_t(0)
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK
-    assert n.value == 3 * 2 * 16 * (512 + 1) * 4                   # (o, lse) partial of every split
+    part = 3 * 2 * 16 * (512 + 1) * 4                               # (o, lse) partial of every chunk slot
+    assert n.value == -(-part // 256) * 256 + 2 * 2 * 4              # + the chunk table (count, first)
     a = _args(num_splits=1)
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK and n.value == 0
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), None) == dcp.DCP_EINVAL

@@ -55,12 +55,77 @@ def plan(B, M, bt_cols, P, cus=256, num_splits=0):
         W = min(range(MAX_RB, 0, -1), key=lambda rb: (-(-M // (32 * rb)) * 32 * rb, -rb))
     mgroups = -(-M // (32 * W))
     tiles_max = -(-(bt_cols * P) // TILE)
-    base = B * mgroups
-    splits = num_splits or (cus // base if base < cus else 1)
-    splits = max(1, min(splits, tiles_max, 256))
-    per = -(-tiles_max // splits)
-    splits = -(-tiles_max // per)
-    return W, mgroups, splits, per * TILE
+    if num_splits > 0:
+        forced = min(num_splits, tiles_max)
+        target = 0
+        slots = B * forced
+    else:
+        forced = 0
+        target = max(cus // mgroups, 1)
+        slots = max(target, B)
+    return W, mgroups, slots, forced, target
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def work_list(tiles, forced, target):
+    """The kernel's chunks in chunk order: (request, chunk of it, its chunk
+    count, chunk length in tiles).  Every request gets at least one chunk."""
+    B = len(tiles)
+    if forced > 0:
+        n = [cdiv(t, cdiv(t, forced)) if t > 0 else 1 for t in tiles]
+    else:
+        total, maxt = int(sum(tiles)), max(int(max(tiles)), 1)
+        chunks_for = lambda C: sum(max(cdiv(t, C), 1) for t in tiles)
+        if target <= B:
+            C = maxt
+        else:
+            C = max(cdiv(total, target), 1)
+            T0 = chunks_for(C)
+            if T0 > target:
+                C1 = cdiv(C * T0, target)
+                C = C1 if chunks_for(C1) <= target else max(cdiv(total, target - B), 1)
+        n = [max(cdiv(t, C), 1) for t in tiles]
+    out = []
+    for b, t in enumerate(tiles):
+        cs = cdiv(t, n[b]) if t > 0 else 0
+        out += [(b, k, n[b], cs) for k in range(n[b])]
+    return out
+
+
+def test_work_list_fits_the_grid_and_partitions_every_request():
+    """Over random batches (uniform, log-uniform, empty, huge) the chunks never
+    outnumber the grid's slots and tile each request exactly once, and the
+    balanced list keeps the longest chunk within twice the mean."""
+    rng = np.random.default_rng(5)
+    for trial in range(400):
+        B = int(rng.integers(1, 300))
+        kind = trial % 4
+        if kind == 0:
+            tiles = np.full(B, int(rng.integers(0, 600)))
+        elif kind == 1:
+            tiles = np.rint(np.exp(rng.uniform(0, np.log(2048), B))).astype(int)
+        elif kind == 2:
+            tiles = rng.integers(0, 4, B)
+        else:
+            tiles = rng.integers(0, 40000, B)
+        for mgroups in (1, 2, 4):
+            for ns in (0, 1, 3, 8):
+                forced = min(ns, 10 ** 6) if ns else 0
+                target = 0 if ns else max(256 // mgroups, 1)
+                slots = B * forced if ns else max(target, B)
+                wl = work_list(list(tiles), forced, target)
+                assert len(wl) <= slots
+                for b in range(B):
+                    mine = [(k, n, cs) for (bb, k, n, cs) in wl if bb == b]
+                    assert [k for k, _, _ in mine] == list(range(len(mine))) and mine[0][1] == len(mine)
+                    cs = mine[0][2]
+                    covered = sum(max(0, min((k + 1) * cs, tiles[b]) - k * cs) for k, _, _ in mine)
+                    assert covered == tiles[b] and (len(mine) - 1) * cs < max(tiles[b], 1)
+                if not ns and tiles.sum() > 0 and target > B:
+                    assert max(cs for (_, _, _, cs) in wl) <= 2 * cdiv(int(tiles.sum()), target - B) + 1
 
 
 def count_rows(x, N, I, r):
@@ -133,13 +198,15 @@ def check_workload(w, I, plant=None, num_splits=0):
     for r in range(N):
         tab = tables[r]
         B, cols = tab.shape
-        W, mgroups, splits, split_rows = plan(B, M, cols, P, num_splits=num_splits)
+        W, mgroups, slots, forced, target = plan(B, M, cols, P, num_splits=num_splits)
         g = fast_chunks(plant)
         max_vis = count_rows(lens, N, I, r)
-        for b in range(B):
-            for sp in range(splits):
-                row_lo = sp * split_rows
-                row_hi = min(row_lo + split_rows, int(max_vis[b]))
+        wl = work_list([cdiv(int(v), TILE) for v in max_vis], forced, target)
+        assert len(wl) <= slots                        # every chunk has a workgroup
+        for (b, sp, nchunks, cs) in wl:
+            if True:
+                row_lo = sp * cs * TILE
+                row_hi = min(row_lo + cs * TILE, int(max_vis[b]))
                 ntiles = -(-(row_hi - row_lo) // TILE) if row_hi > row_lo else 0
                 for it in range(ntiles):                  # tiles past the split issue no loads
                     J = row_lo + it * TILE
@@ -160,8 +227,8 @@ def check_workload(w, I, plant=None, num_splits=0):
                     assert (pg >= 0).all() and (pg < pool_pages).all()
                     assert (c < CHUNKS).all()
         # epilogue: partial / final rows stay inside their buffers
-        assert B * mgroups * 32 * W >= B * M
-        assert (splits - 1) * B * M + (B - 1) * M + (M - 1) < splits * B * M
+        assert mgroups * 32 * W >= M
+        assert (slots - 1) * M + (M - 1) < slots * M
 
 
 @pytest.mark.parametrize("name,I", [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)])
@@ -196,6 +263,7 @@ def test_plan_matches_library_workspace():
         a.num_pages, a.bt_cols, a.num_splits = 10, cols, ns
         n = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
-        W, mg, splits, _ = plan(B, q_len * H_, cols, P, num_splits=ns)
-        want = 0 if splits == 1 else splits * B * q_len * H_ * 513 * 4
+        W, mg, slots, forced, target = plan(B, q_len * H_, cols, P, num_splits=ns)
+        part = slots * q_len * H_ * 513 * 4
+        want = 0 if forced == 1 else cdiv(part, 256) * 256 + 2 * B * 4
         assert n.value == want
