@@ -137,13 +137,18 @@ int dcp_kv_write(dcp_layout layout, int32_t rank,
  * scale       softmax scale applied to q.k (e.g. 1/sqrt(192)).
  * lse_base    0: lse in natural log; 1: lse in log2 (same partition function,
  *             lse2 = lse * log2(e)); the output o does not depend on it.
- * num_splits  KV splits per request (0 = chosen by the library).
+ * num_splits  0: the library cuts every request's local rows into chunks
+ *             of whole 32-token tiles balanced over the whole batch (ragged
+ *             lengths included), one workgroup per chunk; k > 0: each
+ *             request into k chunks of equal length (fewer when it is
+ *             shorter than k tiles).
  * workspace, workspace_bytes  device scratch of at least the size
- *             dcp_stripe_attn_workspace() reports for these arguments (0 when
- *             one KV split per request is used).  It holds the splits'
- *             partial (o, lse), which a second kernel on the same stream
- *             merges into o and lse; its contents need no initialisation.
- *             Calls that overlap in time must not share a workspace.
+ *             dcp_stripe_attn_workspace() reports for these arguments (0 only
+ *             for num_splits = 1).  It holds each chunk's partial (o, lse)
+ *             and the chunk table; a second kernel on the same stream merges
+ *             the chunks of every request that has more than one.  Its
+ *             contents need no initialisation.  Calls that overlap in time
+ *             must not share a workspace.
  * o    [B][q_len][H][v_dim] fp32 device out: o_r, normalised inside the stripe.
  * lse  [B][q_len][H] fp32 device out: lse_r in the chosen base.
  *      A query with no visible row in this stripe gets o = 0, lse = -inf
