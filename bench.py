@@ -261,7 +261,7 @@ def main():
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "one dcp_stripe_attn call: stripe_attn_kernel + its split combine",
+                     "kernel": "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine",
                      "bytes_per_launch": int(stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
