@@ -551,29 +551,26 @@ stripe_attn_kernel(Params p) {
     }
   };
   // Softmax of one whole tile (split-role waves).  After the split's first
-  // tile every row that sees any token has a finite reference within 2^8 of
-  // its running max, so the tile is first weighted against the current
+  // tile every row that sees the whole tile has a finite reference within 2^8
+  // of its running max, so such a tile is first weighted against the current
   // reference: when no lane's sum of weights exceeds 2^8 (every weight is
   // non-negative, so then none does) the reference need not move and the
-  // tile max is never computed.  Otherwise -- an overflow, a larger max, or
-  // just many large weights -- the exact pieces above recompute it.
+  // tile max is never computed.  Otherwise -- an overflow, a larger max, many
+  // large weights, or a tile that crosses some row's visible limit -- the
+  // exact pieces above recompute it.
   auto softmax_tile = [&](bool first) {
-    if (!first) {
-      if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
+    if (!first && __builtin_amdgcn_ballot_w64(vis < kTile) == 0) {
+      const float nm = -m_run;
+      float e[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
-      }
-      neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-      psum = 0.f;
+      for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, nm));
+      const float s = (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+                      (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
+      if (__builtin_amdgcn_ballot_w64(!(s <= 256.0f)) == 0) {   // (also catches inf)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, neg_m));
-        psum += e;
-        pk[i >> 3][i & 7] = (__bf16)e;
-      }
-      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.0f)) == 0) {   // (also catches inf)
+        for (int i = 0; i < 16; ++i) pk[i >> 3][i & 7] = (__bf16)e[i];
         if (lane == 0) reinterpret_cast<uint8_t*>(smem + kFlagOff)[sbuf * 16 + wave] = 0;
-        l_run += psum;
+        l_run += s;
         return;
       }
     }
