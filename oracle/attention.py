@@ -29,6 +29,16 @@ Definitions followed (no blocking, fusion or online rescaling is added):
 
 "Base-2 LSE" is read as log2 of the same natural-softmax partition function
 (lse_2 = lse_e * log2(e)); the attention output does not depend on the base.
+
+Variants that keep the merge exact (page "DCP", "conditions for merging and
+where they fail": a mask only shrinks the visible set, a sink or position bias
+is one extra logit term in one shard, an elementwise logit transform couples
+no positions):
+
+* sliding window W: a query at t sees p with t - W < p <= t;
+* logit softcap c: each scaled score s becomes c * tanh(s / c);
+* attention sink: one extra logit sigma per query row with value zero, i.e.
+  exp(sigma) joins the denominator; in a sharded run exactly one shard adds it.
 """
 
 from __future__ import annotations
@@ -41,15 +51,19 @@ LN2 = math.log(2.0)
 
 
 def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.ndarray,
-                   scale: float, v_dim: int = 512, chunk: int | None = None):
+                   scale: float, v_dim: int = 512, chunk: int | None = None,
+                   window: int = 0, softcap: float = 0.0, sink=None):
     """Softmax attention of R query rows over n latent rows, in float64.
 
     q      [R, D] query rows (D = 576)
     q_pos  [R]    global position of each query (it sees kv rows with kv_pos <= q_pos)
     kv     [n, D] latent rows; the key is the whole row, the value its first v_dim dims
     kv_pos [n]    global position of each latent row
+    window > 0    also hides rows with kv_pos <= q_pos - window
+    softcap > 0   replaces each scaled score s by softcap * tanh(s / softcap)
+    sink   [R]    natural-log logit of an extra zero-valued term per row (None: none)
     Returns o [R, v_dim] and the natural-log lse [R]; a query that sees no row
-    gets o = 0 and lse = -inf.
+    (and has no sink) gets o = 0 and lse = -inf.
 
     ``chunk`` only splits the two sums over rows into pieces (a first pass
     finds the exact maximum, a second adds up exp(s - max) and the weighted
@@ -66,7 +80,11 @@ def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.
 
     def scores(lo, hi):
         s = (kv[lo:hi] @ q.T) * scale                       # [rows, R]
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
         hidden = kv_pos[lo:hi, None] > q_pos[None, :]
+        if window > 0:
+            hidden |= kv_pos[lo:hi, None] <= q_pos[None, :] - window
         s[hidden] = -np.inf
         return s
 
@@ -75,6 +93,9 @@ def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.
         s = scores(lo, min(n, lo + chunk))
         if s.size:
             m = np.maximum(m, s.max(axis=0))
+    if sink is not None:
+        sink = np.asarray(sink, dtype=np.float64).reshape(R)
+        m = np.maximum(m, sink)
     seen = np.isfinite(m)
     m_safe = np.where(seen, m, 0.0)
     Z = np.zeros(R)
@@ -85,6 +106,8 @@ def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.
         e = np.exp(s - m_safe[None, :])                      # exp(-inf) = 0 for hidden rows
         Z += e.sum(axis=0)
         acc += e.T @ kv[lo:hi, :v_dim]
+    if sink is not None:
+        Z += np.exp(sink - m_safe)                           # exp(-inf) = 0: no sink on that row
     o = np.zeros((R, v_dim))
     o[seen] = acc[seen] / Z[seen, None]
     lse = np.full(R, -np.inf)
@@ -97,35 +120,49 @@ def query_positions(S: int, q_len: int) -> np.ndarray:
     return np.arange(S - q_len, S, dtype=np.int64)
 
 
+def _row_sinks(sinks, q_len: int, H: int):
+    """Per-head sink logits [H] as one value per query row (t, h), or None."""
+    if sinks is None:
+        return None
+    return np.tile(np.asarray(sinks, dtype=np.float64).reshape(H), q_len)
+
+
 def full_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, scale: float,
-                   v_dim: int = 512, chunk: int | None = None):
+                   v_dim: int = 512, chunk: int | None = None,
+                   window: int = 0, softcap: float = 0.0, sinks=None):
     """Unsharded attention of one request.
 
     q_req [q_len, H, D], kv_req [S, D] (logical order, position p at row p).
+    window / softcap as in ``attention_rows``; sinks [H] per-head sink logits.
     Returns o [q_len, H, v_dim] and natural-log lse [q_len, H].
     """
     q_len, H, D = q_req.shape
     qp = np.repeat(query_positions(S, q_len), H)
     o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[:S],
-                            np.arange(S, dtype=np.int64), scale, v_dim, chunk)
+                            np.arange(S, dtype=np.int64), scale, v_dim, chunk,
+                            window, softcap, _row_sinks(sinks, q_len, H))
     return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
 
 
 def stripe_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, positions: np.ndarray,
-                     scale: float, v_dim: int = 512, chunk: int | None = None):
+                     scale: float, v_dim: int = 512, chunk: int | None = None,
+                     window: int = 0, softcap: float = 0.0, sinks=None):
     """Local attention of one request on one stripe.
 
     ``positions`` are the global positions the rank owns (as handed out by
     ``oracle.layout.stripe_positions``); only those rows of ``kv_req`` enter.
+    window / softcap as in ``attention_rows``; ``sinks`` [H] is given to the
+    one stripe that carries the sink term.
     Returns the locally normalised o_r [q_len, H, v_dim] and lse_r [q_len, H]
-    (natural log; -inf where the stripe holds no visible row).
+    (natural log; -inf where the stripe holds no visible row and no sink).
     """
     q_len, H, D = q_req.shape
     positions = np.asarray(positions, dtype=np.int64)
     positions = positions[positions < S]
     qp = np.repeat(query_positions(S, q_len), H)
     o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[positions],
-                            positions, scale, v_dim, chunk)
+                            positions, scale, v_dim, chunk,
+                            window, softcap, _row_sinks(sinks, q_len, H))
     return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
 
 

@@ -282,3 +282,178 @@ def test_chunked_evaluation_is_the_same_sum():
     o1, l1 = A.full_attention(q, kv, S, SCALE)
     o2, l2 = A.full_attention(q, kv, S, SCALE, chunk=97)
     assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(l1, l2, rtol=1e-14)
+
+
+# ---- mergeable variants: sliding window, logit softcap, attention sink ------
+# (page "DCP", "conditions for merging and where they fail")
+
+def brute_variant(q_row, kv, kv_pos, q_pos, scale, window=0, softcap=0.0, sink=None):
+    """The variant definitions evaluated term by term with math.fsum."""
+    vis = [i for i in range(len(kv))
+           if kv_pos[i] <= q_pos and (window <= 0 or kv_pos[i] > q_pos - window)]
+    s = []
+    for i in vis:
+        x = scale * math.fsum(float(q_row[d]) * float(kv[i][d]) for d in range(D))
+        s.append(softcap * math.tanh(x / softcap) if softcap > 0 else x)
+    terms = s + ([sink] if sink is not None else [])
+    if not terms:
+        return [0.0] * V, -math.inf
+    m = max(terms)
+    e = [math.exp(x - m) for x in s]
+    Z = math.fsum(e + ([math.exp(sink - m)] if sink is not None else []))
+    o = [math.fsum(e[j] * float(kv[vis[j]][c]) for j in range(len(vis))) / Z for c in range(V)]
+    return o, m + math.log(Z)
+
+
+VARIANTS = [dict(window=3), dict(window=1), dict(softcap=0.5), dict(sinks=[0.7, -1.3]),
+            dict(window=4, softcap=1.0, sinks=[2.0, 0.1])]
+
+
+def _close(o, lse, bo, bl):
+    assert np.allclose(o, bo, rtol=1e-12, atol=1e-13)
+    if math.isinf(bl):
+        assert lse == -math.inf
+    else:
+        assert abs(lse - bl) <= 1e-12 * max(1.0, abs(bl))
+
+
+@pytest.mark.parametrize("var", VARIANTS)
+def test_variants_against_brute_force(var):
+    rng = np.random.default_rng(7)
+    S, H, q_len = 11, 2, 2
+    q, kv = rand_case(rng, S, H, q_len, kv_std=1.0)
+    o, lse = A.full_attention(q, kv, S, SCALE, **var)
+    sinks = var.get("sinks")
+    for t in range(q_len):
+        for h in range(H):
+            bo, bl = brute_variant(q[t, h], kv, list(range(S)), S - q_len + t, SCALE, var.get("window", 0),
+                                   var.get("softcap", 0.0), None if sinks is None else sinks[h])
+            _close(o[t, h], lse[t, h], bo, bl)
+    # one stripe of a block round-robin layout, the sink on this stripe
+    pos = L.stripe_positions(S, 3, 2)[1]
+    o, lse = A.stripe_attention(q, kv, S, pos, SCALE, **var)
+    for t in range(q_len):
+        for h in range(H):
+            bo, bl = brute_variant(q[t, h], [kv[p] for p in pos.tolist()], pos.tolist(), S - q_len + t, SCALE,
+                                   var.get("window", 0), var.get("softcap", 0.0),
+                                   None if sinks is None else sinks[h])
+            _close(o[t, h], lse[t, h], bo, bl)
+
+
+def test_window_of_one_sees_only_the_query_position():
+    rng = np.random.default_rng(8)
+    S, H, q_len = 9, 3, 3
+    q, kv = rand_case(rng, S, H, q_len)
+    o, lse = A.full_attention(q, kv, S, SCALE, window=1)
+    for t in range(q_len):
+        p = S - q_len + t
+        for h in range(H):
+            assert np.allclose(o[t, h], kv[p, :V], rtol=0, atol=1e-15)
+            assert abs(lse[t, h] - SCALE * float(q[t, h] @ kv[p])) < 1e-12
+
+
+def test_window_covering_the_context_changes_nothing():
+    rng = np.random.default_rng(9)
+    S, H, q_len = 20, 2, 4
+    q, kv = rand_case(rng, S, H, q_len)
+    o0, l0 = A.full_attention(q, kv, S, SCALE)
+    o1, l1 = A.full_attention(q, kv, S, SCALE, window=S)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # W = S - q_len + 1: query t sees p >= t, so the first query keeps every
+    # position and the last one loses positions 0 .. q_len - 2
+    o2, l2 = A.full_attention(q, kv, S, SCALE, window=S - q_len + 1)
+    assert np.array_equal(o2[0], o0[0]) and np.array_equal(l2[0], l0[0])
+    assert not np.allclose(o2[-1], o0[-1], rtol=1e-6, atol=0)
+    o3, l3 = A.full_attention(q[-1:], kv[q_len - 1:], S - q_len + 1, SCALE)   # the last query on what it keeps
+    assert np.allclose(o2[-1], o3[0], rtol=1e-12, atol=1e-14) and np.allclose(l2[-1], l3[0], rtol=1e-12)
+
+
+def test_softcap_saturates_to_a_two_level_softmax():
+    # q along dim 0 only, huge: every capped score is +c or -c to fp64 rounding,
+    # so the weights are e^c for keys with kv[.,0] > 0 and e^-c for the others
+    rng = np.random.default_rng(10)
+    S, c = 12, 1.5
+    kv = rng.standard_normal((S, D)) * 0.5
+    sign = np.where(rng.random(S) < 0.4, 1.0, -1.0)
+    kv[:, 0] = sign
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = 1e6
+    o, lse = A.full_attention(q, kv, S, SCALE, softcap=c)
+    wp, wm = math.exp(c), math.exp(-c)
+    Z = wp * (sign > 0).sum() + wm * (sign < 0).sum()
+    want = (wp * kv[sign > 0, :V].sum(axis=0) + wm * kv[sign < 0, :V].sum(axis=0)) / Z
+    assert np.allclose(o[0, 0], want, rtol=1e-12, atol=1e-14)
+    assert abs(lse[0, 0] - math.log(Z)) < 1e-12
+
+
+def test_softcap_far_above_the_scores_is_the_plain_softmax():
+    rng = np.random.default_rng(11)
+    S, H, q_len = 15, 2, 2
+    q, kv = rand_case(rng, S, H, q_len)
+    o0, l0 = A.full_attention(q, kv, S, SCALE)
+    o1, l1 = A.full_attention(q, kv, S, SCALE, softcap=1e7)
+    assert np.allclose(o0, o1, rtol=1e-11, atol=1e-13) and np.allclose(l0, l1, rtol=1e-11, atol=1e-12)
+
+
+def test_sink_with_zero_query_closed_form():
+    # every score is 0: o = n / (n + e^sigma) * mean(v), lse = log(n + e^sigma)
+    rng = np.random.default_rng(12)
+    S, H, q_len = 10, 2, 3
+    kv = rng.standard_normal((S, D))
+    q = np.zeros((q_len, H, D))
+    sinks = np.array([0.3, -2.0])
+    o, lse = A.full_attention(q, kv, S, SCALE, sinks=sinks)
+    for t in range(q_len):
+        n = S - q_len + t + 1
+        for h in range(H):
+            f = n / (n + math.exp(sinks[h]))
+            assert np.allclose(o[t, h], f * kv[:n, :V].mean(axis=0), rtol=1e-12, atol=1e-14)
+            assert abs(lse[t, h] - math.log(n + math.exp(sinks[h]))) < 1e-12
+
+
+def test_sink_alone_and_minus_infinite_sink():
+    rng = np.random.default_rng(13)
+    S, H = 6, 2
+    q, kv = rand_case(rng, S, H, 1)
+    o0, l0 = A.full_attention(q, kv, S, SCALE)
+    o1, l1 = A.full_attention(q, kv, S, SCALE, sinks=[-np.inf, -np.inf])
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # a stripe with no visible row but the sink: o = 0, lse = sigma
+    o2, l2 = A.stripe_attention(q, kv, S, np.array([], dtype=np.int64), SCALE, sinks=[1.5, -0.5])
+    assert np.array_equal(o2, np.zeros_like(o2)) and np.allclose(l2[0], [1.5, -0.5], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("var", VARIANTS)
+@pytest.mark.parametrize("N,I", [(2, 1), (3, 2), (4, 1), (8, 1)])
+def test_variant_stripes_merge_to_full(var, N, I):
+    # the page's claim: with the sink added in exactly one shard, the merge of
+    # the stripes is the unsharded variant
+    rng = np.random.default_rng(N * 13 + I)
+    S, H, q_len = 37, 2, 3
+    q, kv = rand_case(rng, S, H, q_len)
+    o_full, l_full = A.full_attention(q, kv, S, SCALE, **var)
+    lists = L.stripe_positions(S, N, I)
+    parts = []
+    for r in range(N):
+        v = dict(var)
+        if r != N - 1:
+            v.pop("sinks", None)
+        parts.append(A.stripe_attention(q, kv, S, lists[r], SCALE, **v))
+    o, lse = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    assert np.allclose(o, o_full, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse, l_full, rtol=1e-12, atol=1e-12)
+
+
+def test_sink_added_on_every_stripe_is_counted_every_time():
+    # the merge adds up the partition functions: a sink on all N stripes
+    # enters N times, Z = Z_plain + N e^sigma
+    rng = np.random.default_rng(14)
+    S, H, N = 24, 2, 4
+    q, kv = rand_case(rng, S, H, 1)
+    sinks = np.array([0.4, 1.1])
+    _, l_plain = A.full_attention(q, kv, S, SCALE)
+    lists = L.stripe_positions(S, N, 1)
+    parts = [A.stripe_attention(q, kv, S, lists[r], SCALE, sinks=sinks) for r in range(N)]
+    _, lse = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    want = np.log(np.exp(l_plain[0]) + N * np.exp(sinks))
+    assert np.allclose(lse[0], want, rtol=1e-12, atol=1e-12)
