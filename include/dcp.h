@@ -155,7 +155,20 @@ int dcp_kv_write(dcp_layout layout, int32_t rank,
  *      (zero weight in the merge; page "PCP/DCP" section 4.1).
  * status device int32, nullable: DCP_ERANGE when a needed page id is outside
  *      [0, num_pages) or missing from the table (that request's output is
- *      then unspecified, memory outside the buffers is never read). */
+ *      then unspecified, memory outside the buffers is never read).
+ *
+ * Variants that keep the merge exact (page "DCP", conditions for merging:
+ * a mask only shrinks the visible set, a sink is one extra logit term in one
+ * shard, an elementwise logit transform couples no positions):
+ * window   W > 0: a query at global position t sees t - W < p <= t (sliding
+ *          window); 0: the whole context.  < 0: DCP_EINVAL.
+ * softcap  c > 0: every scaled score s becomes c * tanh(s / c) before the
+ *          softmax; 0: none.  Negative, NaN or inf: DCP_EINVAL.
+ * sinks    [n_heads] fp32 device, nullable: a natural-log logit per head that
+ *          joins the softmax denominator with value zero.  Pass it on
+ *          exactly one rank's call: the merge adds the stripes' partition
+ *          functions, so a sink given to k ranks counts k times.  A row with
+ *          no visible position then gets o = 0 and lse = the sink. */
 typedef struct dcp_attn_args {
   dcp_layout layout;
   int32_t rank;
@@ -178,6 +191,9 @@ typedef struct dcp_attn_args {
   float* o;
   float* lse;
   int32_t* status;
+  int32_t window;
+  float softcap;
+  const float* sinks;
 } dcp_attn_args;
 
 /* Workspace bytes dcp_stripe_attn needs for `args` (pointers are not read). */

@@ -41,6 +41,12 @@
 //    itself; otherwise each chunk writes an (o, lse) partial and a second
 //    launch merges a request's chunks with the same exact LSE merge as across
 //    stripes (the chunks are a disjoint partition of the stripe's rows).
+//  * Variants that keep the merge exact (page "DCP", conditions for merging):
+//    a sliding window only moves each row's first visible local row (and the
+//    request's first tile); a logit softcap transforms each score right after
+//    QK^T (its own kernel instantiation); an attention sink adds one
+//    zero-valued logit per head to the denominator of the request's first
+//    chunk -- the caller gives it to one rank only.
 #include "dcp_common.h"
 #include "merge_impl.h"
 
@@ -125,6 +131,9 @@ struct Params {
   int32_t bt_cols;
   const int32_t* seq_len;
   float c2;                         // scale * log2(e)
+  int32_t window;                   // > 0: a query at t sees t - window < p <= t
+  float cap_in, cap_out;            // softcap: s -> cap_out * tanh(s * cap_in) (raw-score units)
+  const float* sinks;               // [H] natural-log sink logits, nullable
   int32_t out_base2;
   float* o;                         // final outputs (requests cut into one chunk)
   float* lse;
@@ -156,7 +165,8 @@ __device__ __forceinline__ int32_t wave_max_i(int32_t v) {
 __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // Work list of one stripe call.  Request b's local rows (what its last query
-// sees) make tiles_b tiles of 32; the request is cut into n_b >= 1 chunks of
+// sees, from the first row its first query's window reaches, aligned down to
+// a tile) make tiles_b tiles of 32; the request is cut into n_b >= 1 chunks of
 // cs_b = ceil(tiles_b / n_b) tiles (an empty request gets one empty chunk,
 // which writes its zero output).  With forced_splits = s: n_b = number of
 // chunks of ceil(tiles_b / s) tiles.  Otherwise the chunks are balanced over
@@ -168,37 +178,47 @@ __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 
 // chunk combine reads).
 struct WorkItem {
   int32_t b, k, n, cs, rows;        // request, chunk of it, its chunks, chunk length (tiles), rows
+  int32_t ft;                       // the request's first tile
   bool live;
 };
 
+// first local row any query of a request with S cached tokens can see
+__device__ __forceinline__ int32_t first_row(const Params& p, int32_t S) {
+  return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, p.rank) : 0;
+}
+
 __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
   const int lane = threadIdx.x & 63;
-  // local rows and tiles of request b; the first 256 requests' are loaded
-  // once (all loads in flight together) and kept in registers
+  // tiles of request b (from its first tile on); the first 256 requests'
+  // are loaded once (all loads in flight together) and kept in registers
   constexpr int kCached = 4;
-  int32_t rows_c[kCached];
+  auto tiles_for = [&](int32_t S) -> int32_t {
+    const int32_t rows = count_rows(S, p.N, p.I, p.rank);
+    return rows > 0 ? cdiv(rows, 32) - first_row(p, S) / 32 : 0;
+  };
+  int32_t tiles_c[kCached];
 #pragma unroll
   for (int j = 0; j < kCached; ++j) {
     const int32_t b = 64 * j + lane;
-    rows_c[j] = b < p.B ? p.seq_len[b] : 0;
+    tiles_c[j] = b < p.B ? p.seq_len[b] : 0;
   }
 #pragma unroll
-  for (int j = 0; j < kCached; ++j) rows_c[j] = count_rows(rows_c[j], p.N, p.I, p.rank);
-  auto rows_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
+  for (int j = 0; j < kCached; ++j) tiles_c[j] = tiles_for(tiles_c[j]);
+  auto tiles_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
     const int32_t b = b0 + lane;
     if (b0 < 64 * kCached) {
-      int32_t r = rows_c[0];
+      int32_t r = tiles_c[0];
 #pragma unroll
-      for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? rows_c[j] : r;
+      for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? tiles_c[j] : r;
       return r;
     }
-    return b < p.B ? count_rows(p.seq_len[b], p.N, p.I, p.rank) : 0;
+    return b < p.B ? tiles_for(p.seq_len[b]) : 0;
   };
   int32_t C = 1;
   if (p.forced_splits == 0) {
     int32_t total = 0, maxt = 0;
     for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
-      const int32_t t = cdiv(rows_of(b0), 32);
+      const int32_t t = tiles_of(b0);
       total += t;
       maxt = max(maxt, t);
     }
@@ -207,7 +227,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
     auto chunks_for = [&](int32_t len) -> int32_t {
       int32_t nc = 0;
       for (int32_t b0 = 0; b0 < p.B; b0 += 64)
-        nc += b0 + lane < p.B ? max(cdiv(cdiv(rows_of(b0), 32), len), 1) : 0;
+        nc += b0 + lane < p.B ? max(cdiv(tiles_of(b0), len), 1) : 0;
       return wave_sum_i(nc);
     };
     const int32_t target = p.target_chunks;
@@ -222,12 +242,11 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       }
     }
   }
-  WorkItem w{0, 0, 0, 0, 0, false};
+  WorkItem w{0, 0, 0, 0, 0, 0, false};
   int32_t carry = 0;
   for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
     const int32_t b = b0 + lane;
-    const int32_t rows = rows_of(b0);
-    const int32_t t = cdiv(rows, 32);
+    const int32_t t = tiles_of(b0);
     int32_t nb = 0;
     if (b < p.B) {
       if (p.forced_splits > 0) nb = t > 0 ? cdiv(t, cdiv(t, p.forced_splits)) : 1;
@@ -251,7 +270,9 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       w.b = b0 + l;
       w.k = c - __builtin_amdgcn_readlane(excl, l);
       w.n = __builtin_amdgcn_readlane(nb, l);
-      w.rows = __builtin_amdgcn_readlane(rows, l);
+      const int32_t S = p.seq_len[w.b];
+      w.rows = count_rows(S, p.N, p.I, p.rank);
+      w.ft = first_row(p, S) / 32;
       const int32_t tl = __builtin_amdgcn_readlane(t, l);
       w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
       if (!write_table) break;
@@ -321,7 +342,7 @@ __device__ __forceinline__ float other_half(float v) {
 // the tile loads, waves 4..7 accumulate PV for 128 value columns each -- so
 // one wave's softmax and LDS waits overlap the other wave's MFMAs on the
 // same SIMD; one barrier per tile, P^T double-buffered.
-template <int RB, bool kAligned>
+template <int RB, bool kAligned, bool kCap>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * kNW, 64 * kNW), amdgpu_waves_per_eu(2, 2)))
 stripe_attn_kernel(Params p) {
   static_assert(RB >= 1 && RB <= kMaxRB, "query-row blocks");
@@ -349,7 +370,7 @@ stripe_attn_kernel(Params p) {
 
   const int32_t S_b = p.seq_len[b];
   const int32_t max_vis = wi.rows;     // rows the last query sees
-  const int32_t row_lo = wi.k * wi.cs * kTile;
+  const int32_t row_lo = (wi.ft + wi.k * wi.cs) * kTile;
   int32_t row_hi = row_lo + wi.cs * kTile;
   row_hi = row_hi < max_vis ? row_hi : max_vis;
   const int ntiles = row_hi > row_lo ? (row_hi - row_lo + kTile - 1) / kTile : 0;
@@ -362,6 +383,9 @@ stripe_attn_kernel(Params p) {
   int32_t lim = count_rows(S_b - p.q_len + t + 1, p.N, p.I, p.rank);
   if (!valid) lim = row_hi;
   lim = lim < row_hi ? lim : row_hi;
+  // first visible row (sliding window): rows below it are masked
+  int32_t low = 0;
+  if (valid && p.window > 0) low = count_rows(S_b - p.q_len + t + 1 - p.window, p.N, p.I, p.rank);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds row n, dims
   // 16*ks + 8*half .. +7 for every k-step (QK waves, loaded on their path)
@@ -483,6 +507,14 @@ stripe_attn_kernel(Params p) {
   auto tok_of = [&](int i) { return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half; };
 
   const float c2 = p.c2;
+  // logit softcap, applied to the raw scores (kept in units where x * c2 is
+  // the capped score in base 2), before any masking
+  auto cap = [&](f32x16& x) {
+    if constexpr (kCap) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = p.cap_out * tanhf(x[i] * p.cap_in);
+    }
+  };
 
   // S^T = K Q^T of the tile in stage `st` over the 576 latent dims (K
   // fragments read kQkAhead steps ahead).
@@ -510,15 +542,15 @@ stripe_attn_kernel(Params p) {
   // the reference max moves); P^T stays in registers until the next tile.
   constexpr int kParts = 11;
   f32x16 sacc;
-  int32_t vis = 0;
+  int32_t vis = 0, vlo = 0;             // tile-relative visible rows [vlo, vis)
   float mx = 0.f, neg_m = 0.f, psum = 0.f;
   bf16x8 pk[2];
   int sbuf = 0;                       // buffer of the factors and flags the pieces publish
   auto softmax_part = [&](int part) {
     if (part == 0) {
-      if (__builtin_amdgcn_ballot_w64(vis < kTile) != 0) {
+      if (__builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) != 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis ? sacc[i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis && tok_of(i) >= vlo ? sacc[i] : -INFINITY;
       }
       mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
       mx = fmaxf(mx, fmaxf(fmaxf(sacc[4], sacc[5]), fmaxf(sacc[6], sacc[7])));
@@ -559,7 +591,7 @@ stripe_attn_kernel(Params p) {
   // large weights, or a tile that crosses some row's visible limit -- the
   // exact pieces above recompute it.
   auto softmax_tile = [&](bool first) {
-    if (!first && __builtin_amdgcn_ballot_w64(vis < kTile) == 0) {
+    if (!first && __builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) == 0) {
       const float nm = -m_run;
       float e[16];
 #pragma unroll
@@ -656,7 +688,9 @@ stripe_attn_kernel(Params p) {
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(0);
         sacc = qk(smem);
+        cap(sacc);
         vis = lim - row_lo;
+        vlo = low - row_lo;
         sbuf = 0;
         softmax_tile(true);
         write_p(0);
@@ -665,7 +699,9 @@ stripe_attn_kernel(Params p) {
           wait_tiles_then_barrier<kMyLoads>(0);
           if (it + 1 < ntiles) {
             sacc = qk(smem + ((it + 1) % kStages) * kStageBytes);
+            cap(sacc);
             vis = lim - (row_lo + (it + 1) * kTile);
+            vlo = low - (row_lo + (it + 1) * kTile);
             sbuf = (it + 1) & 1;
             softmax_tile(false);
             write_p((it + 1) & 1);
@@ -722,8 +758,20 @@ stripe_attn_kernel(Params p) {
   float* const inv_lds = reinterpret_cast<float*>(smem + kInvOff);
   if (qk_wave) {
     const float l_tot = l_run + other_half(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    if (p.sinks != nullptr && wi.k == 0 && valid) {
+      // the sink's term 2^sg joins the denominator of the request's first
+      // chunk, against a reference that covers both
+      const float sg = p.sinks[R % p.H] * kLog2e;
+      if (sg > -INFINITY) {
+        const float ref = l_tot > 0.f ? fmaxf(m_run, sg) : sg;
+        const float a = l_tot > 0.f ? __builtin_amdgcn_exp2f(m_run - ref) : 0.f;
+        const float lt = l_tot * a + __builtin_amdgcn_exp2f(sg - ref);
+        inv = a / lt;
+        lse2 = ref + __builtin_amdgcn_logf(lt);
+      }
+    }
     if (half == 0) {
       inv_lds[wave * 32 + n] = inv;
       if (valid) {
@@ -789,6 +837,8 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   if (a->bt_cols < 1 || a->num_pages < 1) return DCP_EINVAL;
   if (a->lse_base != 0 && a->lse_base != 1) return DCP_EINVAL;
   if (a->num_splits < 0) return DCP_EINVAL;
+  if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
+  if (a->softcap > 0.f && !(a->scale > 0.f)) return DCP_EINVAL;
   const int64_t M = (int64_t)a->q_len * a->n_heads;
   const int64_t max_rows = (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
@@ -856,13 +906,18 @@ chunk_combine_kernel(int32_t B, int32_t M, int32_t v4, const int32_t* __restrict
                 lse + row);
 }
 
-template <int RB>
+template <int RB, bool kCap>
 int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
   if (prm.P % kTile == 0)
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, true>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, true, kCap>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   else
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, false>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, false, kCap>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   return launch_status();
+}
+
+template <int RB>
+int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
+  return prm.cap_out > 0.f ? launch<RB, true>(prm, blocks, stream) : launch<RB, false>(prm, blocks, stream);
 }
 
 }  // namespace attn
@@ -910,6 +965,10 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.bt_cols = a->bt_cols;
   prm.seq_len = a->seq_len;
   prm.c2 = a->scale * kLog2e;
+  prm.window = a->window;
+  prm.cap_in = a->softcap > 0.f ? a->scale / a->softcap : 0.f;
+  prm.cap_out = a->softcap > 0.f ? a->softcap / a->scale : 0.f;
+  prm.sinks = a->sinks;
   prm.out_base2 = a->lse_base;
   prm.o = a->o;
   prm.lse = a->lse;

@@ -64,6 +64,9 @@ class dcp_attn_args(ctypes.Structure):
         ("o", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -188,7 +191,7 @@ def dcp_kv_write(lay: dcp_layout, rank: int, kv_new: torch.Tensor, pos: torch.Te
 
 
 def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits,
-               workspace, o, lse, status) -> dcp_attn_args:
+               workspace, o, lse, status, window=0, softcap=0.0) -> dcp_attn_args:
     B, q_len, H, D = q.shape
     a = dcp_attn_args()
     a.layout = lay
@@ -199,6 +202,8 @@ def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_sp
     a.scale = float(scale)
     a.lse_base = int(lse_base)
     a.num_splits = int(num_splits)
+    a.window = int(window)
+    a.softcap = float(softcap)
     return a
 
 
@@ -215,8 +220,11 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     block_table: torch.Tensor, seq_len: torch.Tensor, scale: float, lse_base: int = 0,
                     num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    status: Optional[torch.Tensor] = None):
-    """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H])."""
+                    status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
+                    sinks: Optional[torch.Tensor] = None):
+    """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
+
+    window / softcap / sinks select the mergeable variants (sinks: fp32 [H], on one rank only)."""
     dev = q.device
     if q.dim() != 4 or pool.dim() != 3 or block_table.dim() != 2:
         raise ValueError("q must be [B, q_len, H, 576], pool [pages, P, 576], block_table [B, cols]")
@@ -231,7 +239,10 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
         lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
     if o.numel() != B * q_len * H * V_DIM or lse.numel() != B * q_len * H:
         raise ValueError("o / lse have the wrong size")
-    a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status)
+    a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status,
+                   window, softcap)
+    if sinks is not None and sinks.numel() != H:
+        raise ValueError("sinks must hold one value per head")
     need = ctypes.c_size_t(0)
     _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
     if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
@@ -245,6 +256,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.o = _ptr(o, torch.float32, "o", dev)
     a.lse = _ptr(lse, torch.float32, "lse", dev)
     a.status = _ptr(status, torch.int32, "status", dev)
+    a.sinks = _ptr(sinks, torch.float32, "sinks", dev)
     _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
     return o, lse
 

@@ -96,6 +96,8 @@ def _args(lay=None, **kw):
     ("v_dim", 576, dcp.DCP_EUNSUPPORTED), ("num_pages", 0, dcp.DCP_EINVAL), ("bt_cols", 0, dcp.DCP_EINVAL),
     ("lse_base", 2, dcp.DCP_EINVAL), ("num_splits", -1, dcp.DCP_EINVAL), ("q", None, dcp.DCP_EINVAL),
     ("pool", None, dcp.DCP_EINVAL), ("seq_len", None, dcp.DCP_EINVAL), ("o", None, dcp.DCP_EINVAL),
+    ("window", -1, dcp.DCP_EINVAL), ("softcap", -1.0, dcp.DCP_EINVAL), ("softcap", float("nan"), dcp.DCP_EINVAL),
+    ("softcap", float("inf"), dcp.DCP_EINVAL),
 ])
 def test_stripe_attn_argument_errors(field, value, code):
     a = _args(**{field: value})
@@ -123,3 +125,31 @@ def test_lse_merge_argument_errors():
     assert L.dcp_lse_merge(8, 4, 512, FAKE, FAKE, 3, FAKE, None, None) == dcp.DCP_EINVAL
     assert L.dcp_lse_merge(8, 4, 512, None, FAKE, 0, FAKE, None, None) == dcp.DCP_EINVAL
     assert L.dcp_lse_merge(8, 0, 512, None, None, 0, None, None, None) == dcp.DCP_OK
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of dcp_layout and dcp_attn_args have the C layout:
+    every field's offset and the struct sizes, as a C compiler sees dcp.h."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    fields = [f for f, _ in dcp.dcp_attn_args._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "dcp.h"', "int main(void) {",
+           '  printf("sizeof %zu\\n", sizeof(dcp_attn_args));',
+           '  printf("sizeof_layout %zu\\n", sizeof(dcp_layout));']
+    src += [f'  printf("{f} %zu\\n", offsetof(dcp_attn_args, {f}));' for f in fields]
+    src += ["  return 0;", "}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", inc, str(c), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    assert int(out["sizeof"]) == ctypes.sizeof(dcp.dcp_attn_args)
+    assert int(out["sizeof_layout"]) == ctypes.sizeof(dcp.dcp_layout)
+    for f in fields:
+        assert int(out[f]) == getattr(dcp.dcp_attn_args, f).offset, f

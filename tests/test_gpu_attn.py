@@ -65,6 +65,36 @@ def test_fuzz_shapes_every_element(B, H_, q_len, N, I, P, lens, base, splits):
     check_all(s, splits)
 
 
+VARIANTS = [
+    # B, H, q_len, N, I, P, lens, base, splits, window, softcap, sinks, q_std
+    (3, 16, 1, 4, 1, 16, [1, 200, 577], "e", 0, 50, 0.0, False, 1.0),       # window inside one tile
+    (2, 96, 4, 8, 1, 64, [1100, 9], "2", 0, 300, 0.0, False, 1.0),          # drafts: each row its own start
+    (2, 96, 1, 8, 64, 64, [5000, 700], "2", 3, 2000, 0.0, False, 1.0),      # window across chunks, I = 64
+    (2, 33, 1, 3, 1, 32, [100, 333], "e", 0, 0, 1.5, False, 3.0),           # softcap near saturation
+    (2, 128, 2, 8, 1, 64, [2100, 65], "2", 0, 0, 0.8, False, 1.0),          # softcap, 2 row groups
+    (3, 96, 1, 8, 1, 64, [1, 7, 900], "e", 0, 0, 0.0, True, 1.0),           # sinks, empty stripes
+    (2, 96, 4, 8, 1, 64, [3000, 40], "2", 2, 700, 2.0, True, 1.0),          # all three, chunked
+]
+
+
+@pytest.mark.parametrize("B,H_,q_len,N,I,P,lens,base,splits,window,softcap,sink,q_std", VARIANTS)
+def test_variants_every_element(B, H_, q_len, N, I, P, lens, base, splits, window, softcap, sink, q_std):
+    w, lens = custom(B, H_, q_len, N, P, lens, base, q_std=q_std)
+    print(f"variant B={B} H={H_} q_len={q_len} N={N} I={I} P={P} lens={lens.tolist()} splits={splits} "
+          f"window={window} softcap={softcap} sink={sink}", flush=True)
+    s = H.make_setup(w, I, lens=lens)
+    sinks = None
+    if sink:
+        sinks = np.random.default_rng(1).normal(0.0, 2.0, H_)
+        sinks[0] = 9.0                      # a sink far above every score
+        sinks[-1] = -np.inf                 # no sink on this head
+    var = dict(window=window, softcap=softcap, sinks=sinks, sink_rank=N - 1)
+    o_parts, lse_parts, o, lse = H.run_step(s, splits, **var)
+    assert int(s.status.item()) == 0
+    for b in range(B):
+        H.check_request(s, o_parts, lse_parts, o, lse, b, **var)
+
+
 def test_split_counts_agree():
     w, lens = custom(2, 96, 1, 8, 64, [5000, 2048], "e")
     s = H.make_setup(w, 1, lens=lens)

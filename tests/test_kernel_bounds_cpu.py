@@ -189,7 +189,7 @@ def test_wait_counts_cover_the_tail():
         check_waits(ntiles, STAGES)
 
 
-def check_workload(w, I, plant=None, num_splits=0):
+def check_workload(w, I, plant=None, num_splits=0, window=0):
     lens = workloads.seq_lens(w)
     N, P = w.N, w.page_size
     counts = H.oracle_counts(lens, N, I)
@@ -201,11 +201,15 @@ def check_workload(w, I, plant=None, num_splits=0):
         W, mgroups, slots, forced, target = plan(B, M, cols, P, num_splits=num_splits)
         g = fast_chunks(plant)
         max_vis = count_rows(lens, N, I, r)
-        wl = work_list([cdiv(int(v), TILE) for v in max_vis], forced, target)
+        # with a sliding window a request starts at the tile holding the first
+        # row its first query sees
+        first = count_rows(lens - w.q_len + 1 - window, N, I, r) if window > 0 else np.zeros_like(max_vis)
+        ft = [int(f) // TILE for f in first]
+        wl = work_list([cdiv(int(v), TILE) - ft[b] if v > 0 else 0 for b, v in enumerate(max_vis)], forced, target)
         assert len(wl) <= slots                        # every chunk has a workgroup
         for (b, sp, nchunks, cs) in wl:
             if True:
-                row_lo = sp * cs * TILE
+                row_lo = (ft[b] + sp * cs) * TILE
                 row_hi = min(row_lo + cs * TILE, int(max_vis[b]))
                 ntiles = -(-(row_hi - row_lo) // TILE) if row_hi > row_lo else 0
                 for it in range(ntiles):                  # tiles past the split issue no loads
@@ -234,6 +238,12 @@ def check_workload(w, I, plant=None, num_splits=0):
 @pytest.mark.parametrize("name,I", [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)])
 def test_dma_loads_stay_in_the_tile_page(name, I):
     check_workload(workloads.WORKLOADS[name], I)
+
+
+@pytest.mark.parametrize("name,I,window", [("tiny", 1, 100), ("ragged", 1, 1000), ("dsv3", 1, 4097),
+                                           ("long", 64, 70000)])
+def test_window_chunks_stay_in_the_tile_page(name, I, window):
+    check_workload(workloads.WORKLOADS[name], I, window=window)
 
 
 def test_planted_missing_fast_clamp_is_caught():
