@@ -50,7 +50,9 @@ extern "C" {
  *            page "PCP/DCP" (obnotes) sections 5 and 6; vLLM-Ascend CP design,
  *            "block table", cp_kv_cache_interleave_size).
  * page_size  P >= 1, with P % I == 0 (the vLLM-Ascend design requires the
- *            block size to be a multiple of the interleave).
+ *            block size to be a multiple of the interleave) or I % P == 0
+ *            (a run of I tokens fills whole pages: page "PCP/DCP" (obnotes)
+ *            section 6 lets the block be k physical pages).
  * For a global position p:
  *   owner(p) = floor(p / I) mod N
  *   row(p)   = floor(p / (I*N)) * I + p mod I          (compact local row)

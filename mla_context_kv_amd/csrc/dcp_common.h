@@ -43,7 +43,7 @@ DCP_HD int64_t position_of(const Layout& L, int64_t j, int64_t r) {
 // size to be a multiple of the interleave)
 inline bool layout_ok(const dcp_layout& l) {
   return l.n_stripes >= 1 && l.interleave >= 1 && l.page_size >= 1 &&
-         l.page_size % l.interleave == 0;
+         (l.page_size % l.interleave == 0 || l.interleave % l.page_size == 0);
 }
 
 inline Layout to_layout(const dcp_layout& l) { return Layout{l.n_stripes, l.interleave}; }

@@ -54,6 +54,8 @@ FUZZ = [
     (1, 160, 1, 8, 16, 128, [3000], "e", 4),                      # 2 query-row groups, P = 128
     (2, 64, 2, 1, 1, 64, [300, 65], "e", 0),                      # N = 1: the stripe is the whole context
     (3, 8, 1, 5, 4, 8, [77, 1, 500], "2", 7),                     # page 8 < tile
+    (2, 96, 1, 8, 128, 64, [3000, 700], "2", 0),                  # interleave of 2 pages
+    (3, 16, 2, 4, 32, 16, [1, 200, 577], "e", 2),                 # interleave of 2 pages of 16
 ]
 
 

@@ -12,7 +12,8 @@ import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)]
+CASES = [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64),
+         ("dsv3", 128), ("ragged", 256)]                 # I = 2 and 4 pages of 64
 
 
 def _tokens(lens):
@@ -72,7 +73,7 @@ def test_slot_map_large_positions_and_errors():
     assert owner.item() == -1 and row.item() == -1 and int(status.item()) == dcp.DCP_ERANGE
 
 
-@pytest.mark.parametrize("N,I", [(8, 1), (8, 64), (4, 1), (3, 16), (1, 1)])
+@pytest.mark.parametrize("N,I", [(8, 1), (8, 64), (4, 1), (3, 16), (1, 1), (8, 128)])
 def test_local_count_bit_exact(N, I):
     dev = H.device()
     rng = np.random.default_rng(N * 100 + I)

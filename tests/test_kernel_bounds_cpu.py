@@ -235,7 +235,8 @@ def check_workload(w, I, plant=None, num_splits=0, window=0):
         assert (slots - 1) * M + (M - 1) < slots * M
 
 
-@pytest.mark.parametrize("name,I", [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64)])
+@pytest.mark.parametrize("name,I", [("tiny", 1), ("dsv3", 1), ("k3", 1), ("ragged", 1), ("long", 1), ("long", 64),
+                                    ("dsv3", 128), ("long", 256)])
 def test_dma_loads_stay_in_the_tile_page(name, I):
     check_workload(workloads.WORKLOADS[name], I)
 

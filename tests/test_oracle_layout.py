@@ -104,7 +104,7 @@ def test_rank1_extraction_worked_example():
 # ---- closed forms -----------------------------------------------------------
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("I", [1, 2, 4, 16, 64])
+@pytest.mark.parametrize("I", [1, 2, 4, 16, 64, 128])
 def test_simulation_equals_closed_forms(N, I):
     S = 5000
     owner, row = L.owner_and_row_table(S, N, I)
@@ -119,7 +119,7 @@ def test_simulation_equals_closed_forms(N, I):
         assert (owner == o4).all() and (row == r4).all()
 
 
-@pytest.mark.parametrize("N,I", [(1, 1), (3, 1), (8, 1), (4, 4), (8, 64), (3, 16)])
+@pytest.mark.parametrize("N,I", [(1, 1), (3, 1), (8, 1), (4, 4), (8, 64), (3, 16), (8, 128)])
 def test_local_counts_equal_local_len(N, I):
     for x in list(range(0, 300)) + [1000, 1333, 4097, 65535]:
         got = L.local_counts(x, N, I)
@@ -151,7 +151,7 @@ def test_count_invariants(N, I):
         assert L.interval_counts(a, n, N, I).sum() == n
 
 
-@pytest.mark.parametrize("N,I", [(1, 1), (8, 1), (8, 64), (3, 2)])
+@pytest.mark.parametrize("N,I", [(1, 1), (8, 1), (8, 64), (3, 2), (4, 128)])
 def test_owner_row_is_a_bijection_with_compact_rows(N, I):
     S = 2000
     owner, row = L.owner_and_row_table(S, N, I)
