@@ -10,7 +10,7 @@ What it computes, and where the pages define it:
 
 * ``layout``    -- which rank owns a global token position, the compact local
   row it is stored at, the per-rank token counts of an interval, and the
-  paged physical slot.  The striping is produced by *simulating* the
+  paged physical slot, and the prefill-to-decode token relayout plan.  The striping is produced by *simulating* the
   round-robin hand-out of tokens (page "DCP", section "core abstraction",
   idea one; page "PCP/DCP", sections 5 and 6), not by the closed forms; the
   closed forms are what the tests pin the simulation against.

@@ -164,3 +164,41 @@ def kv_write(pool: np.ndarray, kv_rows: np.ndarray, pos: np.ndarray, req: np.nda
     keep = slot >= 0
     out[slot[keep]] = kv_rows[keep]
     return out
+
+
+def relayout_plan(start: int, length: int, N: int, I: int, rank: int,
+                  src_table_row: np.ndarray, src_page_size: int,
+                  dst_table_row: np.ndarray, dst_page_size: int):
+    """Token relayout of one request from an unsharded prefill cache (DCP1) to
+    rank ``rank``'s striped decode pool.
+
+    Page "PCP/DCP" (obnotes), "PD + DCP: extracting this rank's tokens from
+    full source pages": on the prefill side request position t sits at row t
+    of the request's pages; the decode rank receives the positions it owns,
+    chosen by the request's global position (never by physical slot), read at
+    their source slots and stored compactly at its local rows.  SGLang DCP
+    docs, "DCP x PD disaggregation": the plan carries the exact token count,
+    so rows of a partly filled final page are never moved.
+
+    Positions [start, start + length) are moved (start > 0: a chunk after a
+    prefix).  Returns (positions, source slots, destination slots), in
+    position order; a slot is -1 where a table has no page for the row.
+    """
+    mine = stripe_positions(start + length, N, I)[rank]
+    rows = np.arange(len(mine), dtype=np.int64)          # local row = index in the rank's list
+    keep = mine >= start
+    positions, rows = mine[keep], rows[keep]
+    src = page_slot(src_table_row, positions, src_page_size)
+    dst = page_slot(dst_table_row, rows, dst_page_size)
+    return positions, src, dst
+
+
+def relayout(dst_pool: np.ndarray, src_pool: np.ndarray, src_slots: np.ndarray,
+             dst_slots: np.ndarray) -> np.ndarray:
+    """Apply a relayout plan: copy source row src_slots[i] to destination row
+    dst_slots[i] (pools viewed as [pages * page_size, row_dim]); pairs with a
+    missing slot are skipped.  Returns the new destination pool."""
+    out = dst_pool.copy()
+    ok = (np.asarray(src_slots) >= 0) & (np.asarray(dst_slots) >= 0)
+    out[np.asarray(dst_slots)[ok]] = src_pool[np.asarray(src_slots)[ok]]
+    return out

@@ -231,3 +231,54 @@ def test_kv_write_owner_filtered_and_chunked_equals_one_shot():
         # the middle chunk wrote exactly its interval share
         mid = L.kv_write(pool, rows[1000:1333], pos[1000:1333], req[1000:1333], N, I, P, rank, table)
         assert (mid != -7).all(axis=1).sum() == L.interval_counts(1000, 333, N, I)[rank]
+
+
+# ---- prefill (DCP1) -> decode (DCP-N) token relayout -------------------------
+
+def test_relayout_plan_reproduces_the_printed_extraction():
+    g = golden("rank1_extraction.json")
+    N, r, n, P = g["N"], g["rank"], g["length"], g["page_size"]
+    pos, src, dst = L.relayout_plan(0, n, N, 1, r, np.array(g["source_pages"]), P, np.array([g["dest_page"]]), P)
+    assert pos[: len(g["positions_head"])].tolist() == g["positions_head"] and pos[-1] == g["positions_last"]
+    assert src.tolist() == g["source_slots"] and len(pos) == g["tokens_received"]
+    lo, hi = g["dest_slot_range"]
+    assert dst.tolist() == list(range(lo, hi + 1))
+
+
+@pytest.mark.parametrize("N,I", [(8, 1), (4, 2), (8, 64), (3, 128)])
+def test_relayout_moves_exactly_the_owned_positions_of_the_chunk(N, I):
+    rng = np.random.default_rng(N + I)
+    P = 64
+    for start, length in [(0, 1), (0, 700), (1000, 333), (129, 64), (5, 0)]:
+        end = start + length
+        src_row = rng.permutation(64)[: -(-end // P)]
+        for r in range(N):
+            dst_row = rng.permutation(64)
+            pos, src, dst = L.relayout_plan(start, length, N, I, r, src_row, P, dst_row, P)
+            # exactly the rank's share of the chunk, in position order, by global position
+            assert len(pos) == L.interval_counts(start, length, N, I)[r]
+            assert ((pos >= start) & (pos < end)).all() and (np.diff(pos) > 0).all()
+            assert all(block_rr(int(p), N, I)[0] == r for p in pos)
+            # source slot = the position's row in the dense source pages
+            assert (src == src_row[pos // P] * P + pos % P).all()
+            # destination = the slot the owner-filtered write would give the same position
+            _, _, want = L.slot_map(pos, np.zeros_like(pos), N, I, P, r, dst_row[None, :])
+            assert (dst == want).all()
+
+
+def test_relayout_then_decode_pool_equals_the_owner_filtered_write():
+    rng = np.random.default_rng(3)
+    N, I, P, S = 4, 2, 16, 150
+    rows = rng.standard_normal((S, 5))
+    src_row = rng.permutation(20)[: -(-S // P)]
+    src_pool = np.full((20 * P, 5), np.nan)
+    src_pool[src_row[np.arange(S) // P] * P + np.arange(S) % P] = rows
+    for r in range(N):
+        dst_row = rng.permutation(30)
+        empty = np.full((30 * P, 5), np.nan)
+        a = empty
+        for start, length in [(0, 61), (61, 40), (101, 49)]:          # chunked transfer
+            _, src, dst = L.relayout_plan(start, length, N, I, r, src_row, P, dst_row, P)
+            a = L.relayout(a, src_pool, src, dst)
+        b = L.kv_write(empty, rows, np.arange(S), np.zeros(S, dtype=np.int64), N, I, P, r, dst_row[None, :])
+        assert np.array_equal(a, b, equal_nan=True)
