@@ -120,6 +120,34 @@ int dcp_kv_write(dcp_layout layout, int32_t rank,
                  void* pool, int64_t num_pages,
                  int32_t* status, void* stream);
 
+/* dcp_relayout -- prefill (DCP1) to decode (DCP-N) token relayout.
+ * Page "PCP/DCP" (obnotes), "PD + DCP: extracting this rank's tokens from
+ * full source pages"; SGLang DCP docs, "DCP x PD disaggregation".  For each
+ * request b the positions [start[b], start[b] + len[b]) that rank `rank`
+ * owns -- chosen by the request's global position -- are copied from the
+ * request's dense source pages (position t at source row t) to the rank's
+ * compact pool (local row j at block_table[b][j / P] * P + j % P).  Exactly
+ * count_r(start + len) - count_r(start) rows are moved per request, so rows
+ * of a partly filled final source page never leak; nothing else is written.
+ * row_dim           row length in bf16 (the same on both sides), % 8 == 0.
+ * src_pool          [src_pages][src_page_size][row_dim] bf16 device.
+ * src_block_table   [batch][src_bt_cols] int32 device: the request's source pages.
+ * start, len        [batch] int64 device (start >= 0 and len >= 0, else the
+ *                   request is skipped and DCP_ERANGE raised).
+ * max_len           host int64, an upper bound of len used to size the launch
+ *                   (a longer len is still moved completely, more slowly).
+ * block_table, bt_cols, pool, num_pages  the rank's pool as in dcp_kv_write
+ *                   (page size = layout.page_size).
+ * A row whose source or destination page is missing or out of range is
+ * skipped and raises DCP_ERANGE.  batch > 65535: DCP_EUNSUPPORTED. */
+int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim,
+                 const void* src_pool, int64_t src_pages, int32_t src_page_size,
+                 const int32_t* src_block_table, int32_t src_bt_cols,
+                 const int64_t* start, const int64_t* len, int32_t batch, int64_t max_len,
+                 const int32_t* block_table, int32_t bt_cols,
+                 void* pool, int64_t num_pages,
+                 int32_t* status, void* stream);
+
 /* Arguments of one rank's stripe attention (absorbed MLA decode).
  * Query row i of request b, query t, head h: q[b][t][h][0..575] =
  * [absorbed nope part (512) || rope part (64)] (page "MLA 的 DCP", section 2).

@@ -1,12 +1,15 @@
-// Integer side of DCP: slot map, per-rank interval counts and the
-// owner-filtered paged KV write.
+// Integer side of DCP: slot map, per-rank interval counts, the
+// owner-filtered paged KV write and the prefill-to-decode token relayout.
 //
 // Ownership is a pure function of the global position (page "DCP"
 // (zdszero), "core abstraction", idea one); runs of I tokens go to the ranks
 // in turn (page "PCP/DCP" (obnotes), section 6); a row's slot is its page id
 // times the page size plus its offset in the page (page "PCP/DCP", "KV cache
 // management"); a new latent row is stored only on its owner (page
-// "MLA 的 Decode Context Parallelism", section 4, stage 2).
+// "MLA 的 Decode Context Parallelism", section 4, stage 2); a dense prefill
+// cache is relaid out by selecting the positions a decode rank owns (page
+// "PCP/DCP", "PD + DCP: extracting this rank's tokens from full source
+// pages").
 #include "dcp_common.h"
 
 namespace dcp {
@@ -109,6 +112,41 @@ kv_write_kernel(Layout L, int64_t P, int32_t rank, const uint4* __restrict__ kv_
   }
 }
 
+// Prefill-to-decode token relayout: rank r's local rows j0 .. j1-1 of
+// request b (j0 = count_r(start), j1 = count_r(start + len)) are the
+// positions it owns in the chunk; row j holds position p = position_of(j),
+// which sits at row p of the request's dense source pages.  One row per group
+// of 8 lanes, 16-byte chunks as in the write above; grid y = request.
+__global__ void __launch_bounds__(kThreads)
+relayout_kernel(Layout L, int32_t rank, int32_t chunks, const uint4* __restrict__ src,
+                int64_t src_pages, int64_t Ps, const int32_t* __restrict__ src_bt, int32_t src_cols,
+                const int64_t* __restrict__ start, const int64_t* __restrict__ len,
+                const int32_t* __restrict__ bt, int32_t bt_cols, int64_t Pd, uint4* __restrict__ dst,
+                int64_t num_pages, int32_t* status) {
+  const int64_t b = blockIdx.y;
+  const int64_t a = start[b], l = len[b];
+  const int lane8 = threadIdx.x & 7;
+  if (a < 0 || l < 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag_range(status);
+    return;
+  }
+  const int64_t j0 = count_of(L, a, rank), j1 = count_of(L, a + l, rank);
+  const int64_t groups = (int64_t)gridDim.x * (blockDim.x / 8);
+  for (int64_t j = j0 + (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8; j < j1; j += groups) {
+    const int64_t p = position_of(L, j, rank);
+    const int64_t sc = p / Ps, dc = j / Pd;
+    const int32_t spg = sc < src_cols ? src_bt[b * src_cols + sc] : -1;
+    const int32_t dpg = dc < bt_cols ? bt[b * bt_cols + dc] : -1;
+    if (spg < 0 || spg >= src_pages || dpg < 0 || dpg >= num_pages) {
+      if (lane8 == 0) flag_range(status);
+      continue;
+    }
+    const uint4* from = src + ((int64_t)spg * Ps + p % Ps) * chunks;
+    uint4* to = dst + ((int64_t)dpg * Pd + j % Pd) * chunks;
+    for (int c = lane8; c < chunks; c += 8) to[c] = from[c];
+  }
+}
+
 }  // namespace
 }  // namespace dcp
 
@@ -155,5 +193,28 @@ extern "C" int dcp_kv_write(dcp_layout layout, int32_t rank, const void* kv_new,
                      (hipStream_t)stream, to_layout(layout), (int64_t)layout.page_size, rank,
                      (const uint4*)kv_new, row_dim / 8, T, pos, req, block_table, bt_rows, bt_cols,
                      (uint4*)pool, num_pages, status);
+  return launch_status();
+}
+
+extern "C" int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim, const void* src_pool,
+                            int64_t src_pages, int32_t src_page_size, const int32_t* src_block_table,
+                            int32_t src_bt_cols, const int64_t* start, const int64_t* len, int32_t batch,
+                            int64_t max_len, const int32_t* block_table, int32_t bt_cols, void* pool,
+                            int64_t num_pages, int32_t* status, void* stream) {
+  if (!layout_ok(layout) || rank < 0 || rank >= layout.n_stripes) return DCP_EINVAL;
+  if (row_dim < 8 || row_dim % 8 != 0 || batch < 0 || max_len < 0) return DCP_EINVAL;
+  if (src_page_size < 1 || src_pages < 1 || src_bt_cols < 1 || bt_cols < 1 || num_pages < 1) return DCP_EINVAL;
+  if (batch == 0) return DCP_OK;
+  if (batch > 65535) return DCP_EUNSUPPORTED;
+  if (src_pool == nullptr || src_block_table == nullptr || len == nullptr || block_table == nullptr ||
+      pool == nullptr || start == nullptr)
+    return DCP_EINVAL;
+  // rows of one request are at most its owned share of max_len positions
+  const Layout L = to_layout(layout);
+  const int64_t rows = (max_len / (L.N * L.I) + 1) * L.I;
+  dim3 grid(grid_for(rows, kThreads / 8), (unsigned)batch);
+  hipLaunchKernelGGL(relayout_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, L, rank, row_dim / 8,
+                     (const uint4*)src_pool, src_pages, (int64_t)src_page_size, src_block_table, src_bt_cols,
+                     start, len, block_table, bt_cols, (int64_t)layout.page_size, (uint4*)pool, num_pages, status);
   return launch_status();
 }

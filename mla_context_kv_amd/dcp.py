@@ -84,6 +84,8 @@ _SIGNATURES = {
     "dcp_stripe_attn_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "dcp_relayout": (ctypes.c_int, [dcp_layout, _I32, _I32, _VP, _I64, _I32, _VP, _I32, _VP, _VP, _I32, _I64,
+                                    _VP, _I32, _VP, _I64, _VP, _VP]),
 }
 
 
@@ -188,6 +190,32 @@ def dcp_kv_write(lay: dcp_layout, rank: int, kv_new: torch.Tensor, pos: torch.Te
                             _ptr(pool, torch.bfloat16, "pool", dev), int(pool.shape[0]),
                             _ptr(status, torch.int32, "status", dev), _stream(dev))
     _check(rc, "dcp_kv_write")
+
+
+def dcp_relayout(lay: dcp_layout, rank: int, src_pool: torch.Tensor, src_block_table: torch.Tensor,
+                 start: torch.Tensor, length: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
+                 max_len: Optional[int] = None, status: Optional[torch.Tensor] = None) -> None:
+    """Copy the positions [start[b], start[b] + length[b]) that rank `rank` owns from
+    request b's dense prefill pages (src_pool [pages, Ps, D], src_block_table [B, cols])
+    into the rank's compact pool (pool [pages, P, D], block_table [B, cols])."""
+    dev = pool.device
+    if src_pool.dim() != 3 or pool.dim() != 3 or src_pool.shape[2] != pool.shape[2]:
+        raise ValueError("src_pool and pool must be [pages, page_size, D] with the same D")
+    if pool.shape[1] != lay.page_size:
+        raise ValueError("pool page size does not match the layout")
+    B = int(start.numel())
+    if length.numel() != B or src_block_table.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("start, length and both block tables need one row per request")
+    if max_len is None:
+        max_len = int(length.max().item()) if B else 0
+    rc = lib().dcp_relayout(lay, int(rank), int(pool.shape[2]), _ptr(src_pool, torch.bfloat16, "src_pool", dev),
+                            int(src_pool.shape[0]), int(src_pool.shape[1]),
+                            _ptr(src_block_table, torch.int32, "src_block_table", dev), int(src_block_table.shape[1]),
+                            _ptr(start, torch.int64, "start", dev), _ptr(length, torch.int64, "length", dev), B,
+                            int(max_len), _ptr(block_table, torch.int32, "block_table", dev),
+                            int(block_table.shape[1]), _ptr(pool, torch.bfloat16, "pool", dev), int(pool.shape[0]),
+                            _ptr(status, torch.int32, "status", dev), _stream(dev))
+    _check(rc, "dcp_relayout")
 
 
 def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits,

@@ -15,7 +15,7 @@ FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails
 def test_library_exports_every_declared_function():
     names = dcp.header_functions()
     assert {"dcp_slot_map", "dcp_local_count", "dcp_kv_write", "dcp_stripe_attn",
-            "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror"} <= set(names)
+            "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror", "dcp_relayout"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -153,3 +153,21 @@ def test_binding_structs_match_the_header(tmp_path):
     assert int(out["sizeof_layout"]) == ctypes.sizeof(dcp.dcp_layout)
     for f in fields:
         assert int(out[f]) == getattr(dcp.dcp_attn_args, f).offset, f
+
+
+def test_relayout_argument_errors():
+    lay = dcp.layout(8, 1, 64)
+    def call(**kw):
+        a = dict(lay=lay, rank=1, row_dim=576, src=FAKE, src_pages=10, ps=64, sbt=FAKE, scols=4, start=FAKE,
+                 len=FAKE, batch=2, max_len=100, bt=FAKE, cols=4, pool=FAKE, pages=10)
+        a.update(kw)
+        return L.dcp_relayout(a["lay"], a["rank"], a["row_dim"], a["src"], a["src_pages"], a["ps"], a["sbt"],
+                              a["scols"], a["start"], a["len"], a["batch"], a["max_len"], a["bt"], a["cols"],
+                              a["pool"], a["pages"], None, None)
+    assert call(lay=dcp.layout(8, 3, 64)) == dcp.DCP_EINVAL
+    for kw in (dict(rank=8), dict(rank=-1), dict(row_dim=570), dict(row_dim=0), dict(batch=-1), dict(max_len=-1),
+               dict(ps=0), dict(src_pages=0), dict(scols=0), dict(cols=0), dict(pages=0), dict(src=None),
+               dict(sbt=None), dict(start=None), dict(len=None), dict(bt=None), dict(pool=None)):
+        assert call(**kw) == dcp.DCP_EINVAL, kw
+    assert call(batch=70000) == dcp.DCP_EUNSUPPORTED
+    assert call(batch=0, src=None) == dcp.DCP_OK          # nothing to move: no launch

@@ -164,3 +164,86 @@ def test_kv_write_out_of_range_page_is_skipped_and_flagged():
     # rank 0 owns positions 0,2,..,22 -> rows 0..11: pages 0, 5 (skipped), 1
     assert pool[0].float().sum().item() == 32 and pool[1].float().sum().item() == 32
     assert pool[2].float().sum().item() == 0
+
+
+# ---- prefill (DCP1) -> decode token relayout ---------------------------------
+
+NAN16 = 0x7FC0      # bfloat16 quiet NaN: rows never written keep it
+
+
+def _relayout_case(N, I, P, Ps, lens, seed):
+    rng = np.random.default_rng(seed)
+    B, D = len(lens), workloads.ROW_DIM
+    src_need = [-(-int(S) // Ps) for S in lens]
+    src_pages = sum(src_need) + 3
+    perm = rng.permutation(src_pages)
+    src_bt = np.full((B, max(src_need)), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(src_need):
+        src_bt[b, :n] = perm[k:k + n]
+        k += n
+    g = torch.Generator().manual_seed(seed)
+    src = (torch.randn((src_pages, Ps, D), generator=g) * 0.5).to(torch.bfloat16)
+    return rng, src_bt, src
+
+
+@pytest.mark.parametrize("N,I,P,Ps", [(8, 1, 64, 64), (4, 2, 16, 16), (8, 64, 64, 64), (3, 128, 64, 64),
+                                      (8, 1, 64, 16)])
+def test_relayout_bit_exact_chunked(N, I, P, Ps):
+    dev = H.device()
+    lens = [1, 700, 1333, 64]
+    B, D = len(lens), workloads.ROW_DIM
+    print(f"relayout N={N} I={I} P={P} Ps={Ps} lens={lens}", flush=True)
+    rng, src_bt, src = _relayout_case(N, I, P, Ps, lens, N * 1000 + I + P)
+    src_d = src.to(dev)
+    src_bt_d = torch.from_numpy(src_bt).to(dev)
+    src16 = src.view(torch.int16).reshape(-1, D).numpy()
+    lay = dcp.layout(N, I, P)
+    for r in range(N):
+        counts = [int(OL.local_counts(int(S), N, I)[r]) for S in lens]
+        need = [max(1, -(-c // P)) for c in counts]
+        pages = sum(need) + 2
+        perm = rng.permutation(pages)
+        bt = np.full((B, max(need)), -1, dtype=np.int32)
+        k = 0
+        for b, n in enumerate(need):
+            bt[b, :n] = perm[k:k + n]
+            k += n
+        pool = torch.full((pages, P, D), NAN16, dtype=torch.int16).view(torch.bfloat16).to(dev)
+        want = np.full((pages * P, D), NAN16, dtype=np.int16)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # every request moved in two chunks: a prefix and the rest (global positions)
+        cut = [int(S) // 3 for S in lens]
+        for starts, lengths in [([0] * B, cut), (cut, [int(S) - c for S, c in zip(lens, cut)])]:
+            st = torch.tensor(starts, dtype=torch.int64, device=dev)
+            ln = torch.tensor(lengths, dtype=torch.int64, device=dev)
+            dcp.dcp_relayout(lay, r, src_d, src_bt_d, st, ln, torch.from_numpy(bt).to(dev), pool, status=status)
+            for b in range(B):
+                _, s_sl, d_sl = OL.relayout_plan(starts[b], lengths[b], N, I, r, src_bt[b], Ps, bt[b], P)
+                want = OL.relayout(want, src16, s_sl, d_sl)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        got = pool.view(torch.int16).reshape(-1, D).cpu().numpy()
+        assert np.array_equal(got, want), f"rank {r}"
+
+
+def test_relayout_missing_page_is_skipped_and_flagged():
+    dev = H.device()
+    N, I, P = 4, 1, 16
+    lens = [200]
+    rng, src_bt, src = _relayout_case(N, I, P, P, lens, 5)
+    src_bt[0, 3] = -1                                        # positions 48..63 have no source page
+    D = workloads.ROW_DIM
+    pool = torch.full((8, P, D), NAN16, dtype=torch.int16).view(torch.bfloat16).to(dev)
+    bt = np.arange(4, dtype=np.int32)[None, :]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dcp.dcp_relayout(dcp.layout(N, I, P), 1, src.to(dev), torch.from_numpy(src_bt).to(dev),
+                     torch.zeros(1, dtype=torch.int64, device=dev), torch.tensor([200], device=dev),
+                     torch.from_numpy(bt).to(dev), pool, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == dcp.DCP_ERANGE
+    pos, s_sl, d_sl = OL.relayout_plan(0, 200, N, I, 1, src_bt[0], P, bt[0], P)
+    want = OL.relayout(np.full((8 * P, D), NAN16, dtype=np.int16), src.view(torch.int16).reshape(-1, D).numpy(),
+                       s_sl, d_sl)
+    assert np.array_equal(pool.view(torch.int16).reshape(-1, D).cpu().numpy(), want)
+    assert (s_sl < 0).sum() == 4                             # rank 1 owns 49, 53, 57, 61 of that page
