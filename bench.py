@@ -10,6 +10,10 @@ Prints one JSON line: KV GB/s as `value`, microseconds per step, the roofline
 of the dominant kernel (the stripe attention, timed per launch with HIP events
 on its stream) and the float64 CPU oracle timed on a bounded sample of the
 same workload on this host's cores.
+
+Secondary measurements (not the headline): --softcap / --window / --sinks time
+the same step with a mergeable variant switched on; --op relayout times the
+prefill-to-decode token relayout of the whole batch into the N ranks' pools.
 """
 
 from __future__ import annotations
@@ -42,6 +46,11 @@ def parse():
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="step", choices=["step", "relayout"],
+                    help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
+    ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
+    ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -87,6 +96,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.op == "relayout":
+        run_relayout(args)
+        return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
     I = args.interleave
@@ -139,7 +151,13 @@ def main():
         ws_bytes = max(ws_bytes, need.value)
         attn_args.append(a)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sinks = None
+    if args.sinks:
+        g = torch.Generator().manual_seed(7)
+        sinks = torch.randn(w.H, generator=g).to(dev)
     for r, a in enumerate(attn_args):
+        a.window, a.softcap = args.window, args.softcap
+        a.sinks = sinks.data_ptr() if sinks is not None and r == N - 1 else None
         a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
@@ -196,12 +214,19 @@ def main():
 
     # ---- algorithmic work
     local = counts.astype(np.int64)                                  # rows per (request, rank)
-    kv_bytes = float(lens.sum()) * ROW_BYTES
+    if args.window > 0:
+        # rows some query of the request sees: the last S - first window start
+        first = np.clip(lens - w.q_len + 1 - args.window, 0, None)
+        local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
+    kv_bytes = float(local.sum()) * ROW_BYTES
     q_bytes = w.B * M * ROW_BYTES
     part_bytes = w.B * M * (512 + 1) * 4                               # one stripe's (o_r, lse_r)
     vis = np.zeros(w.B)
     for t in range(w.q_len):
-        vis += np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
+        seen = np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
+        if args.window > 0:
+            seen = np.minimum(seen, args.window)
+        vis += seen
     flops = float((vis * w.H).sum()) * FLOP_PER_ROW_QUERY
     kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: one stripe-attention launch (its algorithmic bytes: the
@@ -212,7 +237,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     cpu = None
-    if sample is not None:
+    if sample is not None and not (args.window or args.softcap or args.sinks):
         from oracle import attention as OA
         from oracle import layout as OL
         try:
@@ -255,7 +280,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": int(lens.max()), "H": w.H, "q_len": w.q_len, "N": N,
                    "interleave": I, "page_size": P, "lse_base": w.lse_base, "kv_bytes": int(kv_bytes),
-                   "launches_per_step": N + 1},
+                   "launches_per_step": N + 1,
+                   **({"variant": {"window": args.window, "softcap": args.softcap, "sinks": bool(args.sinks)}}
+                      if (args.window or args.softcap or args.sinks) else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
@@ -263,6 +290,114 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine",
                      "bytes_per_launch": int(stripe_bytes.mean())},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_relayout(args):
+    """Prefill-to-decode token relayout of the whole batch: the requests sit in
+    dense 64-token source pages (random page order); one step moves every
+    request into all N ranks' compact pools (N dcp_relayout calls).  Bytes:
+    every latent row read once and written once."""
+    import torch
+    from mla_context_kv_amd import dcp, stripes, workloads
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    I, N, P = args.interleave, w.N, w.page_size
+    lay = dcp.layout(N, I, P)
+    lens = workloads.seq_lens(w)
+    B, D = w.B, workloads.ROW_DIM
+    t0 = time.perf_counter()
+    src_need = -(-lens // P)
+    src_cols = int(src_need.max())
+    src_pages = int(src_need.sum())
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(src_pages).astype(np.int32)
+    src_bt = np.full((B, src_cols), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        src_bt[b, :src_need[b]] = perm[k:k + src_need[b]]
+        k += src_need[b]
+    src = torch.empty((src_pages, P, D), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        rows = workloads.make_request_kv(w, b, int(lens[b]), dev)
+        pad = torch.zeros((int(src_need[b]) * P - int(lens[b]), D), dtype=torch.bfloat16, device=dev)
+        idx = torch.from_numpy(src_bt[b, :src_need[b]].astype(np.int64)).to(dev)
+        src.index_copy_(0, idx, torch.cat([rows, pad]).view(-1, P, D))
+    counts = dcp.dcp_local_count(lay, torch.from_numpy(lens.astype(np.int64)).to(dev)).cpu().numpy()
+    tables, pool_pages = workloads.make_block_tables(w, stripes.pages_from_counts(counts, P))
+    pools = [torch.empty((pool_pages, P, D), dtype=torch.bfloat16, device=dev) for _ in range(N)]
+    bts = [torch.from_numpy(t).to(dev) for t in tables]
+    src_bt_d = torch.from_numpy(src_bt).to(dev)
+    start = torch.zeros(B, dtype=torch.int64, device=dev)
+    length = torch.from_numpy(lens.astype(np.int64)).to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for r in range(N):
+            if events is not None:
+                events[r].record(stream)
+            dcp.dcp_relayout(lay, r, src, src_bt_d, start, length, bts[r], pools[r], max_len=int(lens.max()),
+                             status=status)
+        if events is not None:
+            events[N].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
+    per_call_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+    moved = counts.sum(axis=0) * ROW_BYTES * 2                       # per rank: read + write
+    achieved = float(np.mean(moved / (per_call_ms.mean(axis=0) * 1e-3))) / 1e9
+    gbs = float(lens.sum()) * ROW_BYTES * 2 / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import layout as OL
+        n_req = min(4, B)
+        cpu_s = 0.0
+        nbytes = 0
+        for b in range(n_req):
+            # the request's source pages (bit patterns), renumbered 0..n-1: not timed
+            src_b = src[torch.from_numpy(src_bt[b, :src_need[b]].astype(np.int64)).to(dev)].view(torch.int16)
+            src16 = src_b.reshape(-1, D).cpu().numpy()
+            local_bt = np.arange(src_need[b], dtype=np.int32)
+            t3 = time.perf_counter()
+            for r in range(N):
+                dst = np.empty((int(-(-counts[b, r] // P)) * P, D), dtype=np.int16)
+                _, s_sl, d_sl = OL.relayout_plan(0, int(lens[b]), N, I, r, local_bt, P,
+                                                 np.arange(dst.shape[0] // P, dtype=np.int32), P)
+                OL.relayout(dst, src16, s_sl, d_sl)
+            cpu_s += time.perf_counter() - t3
+            nbytes += int(lens[b]) * ROW_BYTES * 2
+        cpu = {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seconds": round(cpu_s, 3),
+               "sample": f"{n_req} of {B} requests: plan + row copy into all {N} ranks' pools in NumPy"}
+
+    out = {
+        "metric": "prefill-to-decode token relayout GB/s (read + write), K3 batch into N rank pools, 1 GPU",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "op": "relayout", "B": B, "S": int(lens.max()), "N": N, "interleave": I,
+                   "page_size": P, "bytes_moved": int(lens.sum()) * ROW_BYTES * 2},
+        "per_call_us": [round(float(x) * 1e3, 1) for x in per_call_ms.mean(axis=0)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "one dcp_relayout call (relayout_kernel)"},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

@@ -16,6 +16,7 @@ namespace dcp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kLatentChunks = 576 * 2 / 16;   // 16-byte chunks of one latent row
 
 int grid_for(int64_t work, int64_t per_block) {
   int64_t g = ceil_div(work, per_block);
@@ -143,7 +144,16 @@ relayout_kernel(Layout L, int32_t rank, int32_t chunks, const uint4* __restrict_
     }
     const uint4* from = src + ((int64_t)spg * Ps + p % Ps) * chunks;
     uint4* to = dst + ((int64_t)dpg * Pd + j % Pd) * chunks;
-    for (int c = lane8; c < chunks; c += 8) to[c] = from[c];
+    if (chunks == kLatentChunks) {
+      // latent rows: all nine loads of the lane in flight before its stores
+      uint4 v[kLatentChunks / 8];
+#pragma unroll
+      for (int k = 0; k < kLatentChunks / 8; ++k) v[k] = from[lane8 + 8 * k];
+#pragma unroll
+      for (int k = 0; k < kLatentChunks / 8; ++k) to[lane8 + 8 * k] = v[k];
+    } else {
+      for (int c = lane8; c < chunks; c += 8) to[c] = from[c];
+    }
   }
 }
 
