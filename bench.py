@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
+    ap.add_argument("--parts", type=int, default=0,
+                    help="k > 0: every rank writes k unmerged parts per request and one merge folds all N*k")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -133,8 +135,9 @@ def main():
     setup_s = time.perf_counter() - t0
 
     M = w.q_len * w.H
-    o_parts = torch.empty((N, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
-    lse_parts = torch.empty((N, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    K = max(args.parts, 1)                       # parts per rank (1: the rank's merged o_r)
+    o_parts = torch.empty((N * K, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((N * K, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -144,8 +147,9 @@ def main():
     attn_args = []
     ws_bytes = 0
     for r in range(N):
-        a = dcp._attn_args(lay, r, q, sp.pools[r], sp.tables[r], sp.seq_len, workloads.SCALE, base, args.splits,
-                           None, None, None, None)
+        a = dcp._attn_args(lay, r, q, sp.pools[r], sp.tables[r], sp.seq_len, workloads.SCALE, base,
+                           args.parts if args.parts > 0 else args.splits, None, None, None, None,
+                           partials=1 if args.parts > 0 else 0)
         need = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
@@ -161,11 +165,11 @@ def main():
         a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
-        a.o, a.lse, a.status = o_parts[r].data_ptr(), lse_parts[r].data_ptr(), status.data_ptr()
+        a.o, a.lse, a.status = o_parts[r * K].data_ptr(), lse_parts[r * K].data_ptr(), status.data_ptr()
     refs = [ctypes.byref(a) for a in attn_args]
     sh = stream.cuda_stream
     rows = w.B * M
-    merge_call = (N, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
+    merge_call = (N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
 
     def step(events=None):
         for r in range(N):
@@ -220,7 +224,7 @@ def main():
         local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
     kv_bytes = float(local.sum()) * ROW_BYTES
     q_bytes = w.B * M * ROW_BYTES
-    part_bytes = w.B * M * (512 + 1) * 4                               # one stripe's (o_r, lse_r)
+    part_bytes = K * w.B * M * (512 + 1) * 4                           # one stripe's (o_r, lse_r), or its K parts
     vis = np.zeros(w.B)
     for t in range(w.q_len):
         seen = np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
@@ -236,8 +240,9 @@ def main():
     achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
+    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1)
     cpu = None
-    if sample is not None and not (args.window or args.softcap or args.sinks):
+    if sample is not None and not (args.window or args.softcap or args.sinks or args.parts):
         from oracle import attention as OA
         from oracle import layout as OL
         try:
@@ -282,13 +287,16 @@ def main():
                    "interleave": I, "page_size": P, "lse_base": w.lse_base, "kv_bytes": int(kv_bytes),
                    "launches_per_step": N + 1,
                    **({"variant": {"window": args.window, "softcap": args.softcap, "sinks": bool(args.sinks)}}
-                      if (args.window or args.softcap or args.sinks) else {})},
+                      if (args.window or args.softcap or args.sinks) else {}),
+                   **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if secondary else measured_traffic(w.name),
+                     "kernel": (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
+                                if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine"),
                      "bytes_per_launch": int(stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

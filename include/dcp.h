@@ -224,7 +224,21 @@ typedef struct dcp_attn_args {
   int32_t window;
   float softcap;
   const float* sinks;
+  int32_t partials;
 } dcp_attn_args;
+
+/* Unmerged parts (page "DCP", "unification with online softmax": the split
+ * inside a stripe and the split across stripes are one merge, so both can be
+ * folded into a single pass when o_r itself is not needed):
+ * partials  0: o, lse are o_r, lse_r as above.  1 (needs num_splits = k >= 1):
+ *           every request's stripe is cut into exactly k parts of
+ *           ceil(t / k) tiles of 32 local rows (t = the request's tiles,
+ *           counted from the tile of the first row its first query sees), part
+ *           c holding tiles c*ceil(t/k) .. ; each part is written unmerged,
+ *           normalised over its own rows: o [k][B][q_len][H][v_dim],
+ *           lse [k][B][q_len][H] (an empty part: o = 0, lse = -inf; the sink,
+ *           if any, joins part 0).  No workspace.  dcp_lse_merge over the
+ *           N*k parts of all ranks gives the merged result directly. */
 
 /* Workspace bytes dcp_stripe_attn needs for `args` (pointers are not read). */
 int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);

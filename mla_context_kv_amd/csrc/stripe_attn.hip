@@ -123,6 +123,8 @@ struct Params {
   int32_t RB, mgroups;
   int32_t slots;                    // chunk slots of the workspace (grid = slots * mgroups)
   int32_t forced_splits;            // > 0: that many chunks per request; 0: balanced chunks
+  int32_t partials;                 // > 0: exactly this many chunks per request, each written
+                                    // unmerged to o / lse as part (chunk, request) -- no combine
   int32_t target_chunks;            // balanced: at most this many chunks (when >= B)
   const __bf16* q;
   const char* pool;
@@ -185,6 +187,25 @@ struct WorkItem {
 // first local row any query of a request with S cached tokens can see
 __device__ __forceinline__ int32_t first_row(const Params& p, int32_t S) {
   return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, p.rank) : 0;
+}
+
+// Unmerged parts: chunk c is part c % k of request c / k (k = partials); a
+// request of t tiles has parts of ceil(t / k) tiles, the last ones empty when
+// t < k (an empty part writes o = 0, lse = -inf: zero weight in the merge).
+__device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
+  WorkItem w{0, 0, 0, 0, 0, 0, false};
+  const int32_t k = p.partials;
+  w.b = c / k;
+  w.live = w.b < p.B;
+  if (!w.live) return w;
+  w.k = c - w.b * k;
+  w.n = k;
+  const int32_t S = p.seq_len[w.b];
+  w.rows = count_rows(S, p.N, p.I, p.rank);
+  w.ft = first_row(p, S) / 32;
+  const int32_t t = w.rows > 0 ? cdiv(w.rows, 32) - w.ft : 0;
+  w.cs = t > 0 ? cdiv(t, k) : 0;
+  return w;
 }
 
 __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
@@ -363,10 +384,13 @@ stripe_attn_kernel(Params p) {
   if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
   const int mg = id % p.mgroups;
   const int32_t chunk = id / p.mgroups;
-  const WorkItem wi = find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
+  const WorkItem wi = p.partials > 0 ? part_work(p, chunk)
+                                      : find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
   if (!wi.live) return;                // past the last chunk (the same in every wave)
   const int b = wi.b;
-  const bool direct = wi.n == 1;       // the request's only chunk writes the output itself
+  // the request's only chunk, and every unmerged part, writes the output itself
+  const bool direct = wi.n == 1 || p.partials > 0;
+  const int64_t out_row0 = ((p.partials > 0 ? (int64_t)wi.k * p.B : 0) + b) * p.M;   // first output row
 
   const int32_t S_b = p.seq_len[b];
   const int32_t max_vis = wi.rows;     // rows the last query sees
@@ -780,7 +804,7 @@ stripe_attn_kernel(Params p) {
     if (half == 0) {
       inv_lds[wave * 32 + n] = inv;
       if (valid) {
-        if (direct) p.lse[(int64_t)b * p.M + R] = p.out_base2 ? lse2 : lse2 * kLn2;
+        if (direct) p.lse[out_row0 + R] = p.out_base2 ? lse2 : lse2 * kLn2;
         else p.ws_lse[(int64_t)chunk * p.M + R] = lse2;
       }
     }
@@ -788,7 +812,7 @@ stripe_attn_kernel(Params p) {
   lds_barrier();
   if (!pv_wave) return;
   float* out_base;
-  if (direct) out_base = p.o + (int64_t)b * p.M * kDV;
+  if (direct) out_base = p.o + out_row0 * kDV;
   else out_base = p.ws_o + (int64_t)chunk * p.M * kDV;
   out_base += cgrp * kWaveCols * 32;
   {
@@ -842,6 +866,7 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   if (a->bt_cols < 1 || a->num_pages < 1) return DCP_EINVAL;
   if (a->lse_base != 0 && a->lse_base != 1) return DCP_EINVAL;
   if (a->num_splits < 0) return DCP_EINVAL;
+  if (a->partials != 0 && (a->partials != 1 || a->num_splits < 1)) return DCP_EINVAL;
   if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
   if (a->softcap > 0.f && !(a->scale > 0.f)) return DCP_EINVAL;
   const int64_t M = (int64_t)a->q_len * a->n_heads;
@@ -861,7 +886,12 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   }
   pl->mgroups = (int)ceil_div(M, 32 * pl->RB);
   const int64_t tiles_max = ceil_div(max_rows, kTile);
-  if (a->num_splits > 0) {
+  if (a->partials) {
+    // unmerged parts: exactly num_splits per request, some possibly empty
+    pl->forced = a->num_splits;
+    pl->target = 0;
+    pl->slots = (int64_t)a->batch * a->num_splits;
+  } else if (a->num_splits > 0) {
     // a fixed number of chunks per request
     pl->forced = (int32_t)(a->num_splits < tiles_max ? a->num_splits : tiles_max);
     pl->target = 0;
@@ -878,7 +908,7 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
     pl->slots = pl->target > a->batch ? pl->target : a->batch;
   }
   if (pl->slots * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
-  pl->combine = pl->forced != 1;
+  pl->combine = pl->forced != 1 && !a->partials;
   // chunk partials (o, base-2 lse) and the chunk table
   if (pl->combine) {
     const size_t part = (size_t)pl->slots * M * (kDV + 1) * sizeof(float);
@@ -962,6 +992,7 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.mgroups = pl.mgroups;
   prm.slots = (int32_t)pl.slots;
   prm.forced_splits = pl.forced;
+  prm.partials = a->partials ? a->num_splits : 0;
   prm.target_chunks = pl.target;
   prm.q = (const __bf16*)a->q;
   prm.pool = (const char*)a->pool;

@@ -67,6 +67,7 @@ class dcp_attn_args(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("softcap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
+        ("partials", ctypes.c_int32),
     ]
 
 
@@ -219,7 +220,7 @@ def dcp_relayout(lay: dcp_layout, rank: int, src_pool: torch.Tensor, src_block_t
 
 
 def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits,
-               workspace, o, lse, status, window=0, softcap=0.0) -> dcp_attn_args:
+               workspace, o, lse, status, window=0, softcap=0.0, partials=0) -> dcp_attn_args:
     B, q_len, H, D = q.shape
     a = dcp_attn_args()
     a.layout = lay
@@ -232,6 +233,7 @@ def _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_sp
     a.num_splits = int(num_splits)
     a.window = int(window)
     a.softcap = float(softcap)
+    a.partials = int(partials)
     return a
 
 
@@ -249,10 +251,12 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
-                    sinks: Optional[torch.Tensor] = None):
+                    sinks: Optional[torch.Tensor] = None, partials: bool = False):
     """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
 
-    window / softcap / sinks select the mergeable variants (sinks: fp32 [H], on one rank only)."""
+    window / softcap / sinks select the mergeable variants (sinks: fp32 [H], on one rank only).
+    partials=True (with num_splits = k >= 1) returns the k unmerged parts instead:
+    o [k,B,q_len,H,512], lse [k,B,q_len,H]."""
     dev = q.device
     if q.dim() != 4 or pool.dim() != 3 or block_table.dim() != 2:
         raise ValueError("q must be [B, q_len, H, 576], pool [pages, P, 576], block_table [B, cols]")
@@ -261,14 +265,18 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
         raise ValueError("pool must be [pages, page_size, head_dim]")
     if block_table.shape[0] != B or seq_len.numel() != B:
         raise ValueError("block_table and seq_len need one row per request")
+    k = int(num_splits) if partials else 1
+    if partials and k < 1:
+        raise ValueError("partials needs num_splits >= 1")
+    lead = (k,) if partials else ()
     if o is None:
-        o = torch.empty((B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+        o = torch.empty(lead + (B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
-    if o.numel() != B * q_len * H * V_DIM or lse.numel() != B * q_len * H:
+        lse = torch.empty(lead + (B, q_len, H), dtype=torch.float32, device=dev)
+    if o.numel() != k * B * q_len * H * V_DIM or lse.numel() != k * B * q_len * H:
         raise ValueError("o / lse have the wrong size")
     a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status,
-                   window, softcap)
+                   window, softcap, 1 if partials else 0)
     if sinks is not None and sinks.numel() != H:
         raise ValueError("sinks must hold one value per head")
     need = ctypes.c_size_t(0)

@@ -97,7 +97,7 @@ def _args(lay=None, **kw):
     ("lse_base", 2, dcp.DCP_EINVAL), ("num_splits", -1, dcp.DCP_EINVAL), ("q", None, dcp.DCP_EINVAL),
     ("pool", None, dcp.DCP_EINVAL), ("seq_len", None, dcp.DCP_EINVAL), ("o", None, dcp.DCP_EINVAL),
     ("window", -1, dcp.DCP_EINVAL), ("softcap", -1.0, dcp.DCP_EINVAL), ("softcap", float("nan"), dcp.DCP_EINVAL),
-    ("softcap", float("inf"), dcp.DCP_EINVAL),
+    ("softcap", float("inf"), dcp.DCP_EINVAL), ("partials", 2, dcp.DCP_EINVAL), ("partials", -1, dcp.DCP_EINVAL),
 ])
 def test_stripe_attn_argument_errors(field, value, code):
     a = _args(**{field: value})
@@ -171,3 +171,11 @@ def test_relayout_argument_errors():
         assert call(**kw) == dcp.DCP_EINVAL, kw
     assert call(batch=70000) == dcp.DCP_EUNSUPPORTED
     assert call(batch=0, src=None) == dcp.DCP_OK          # nothing to move: no launch
+
+
+def test_unmerged_parts_need_a_split_count_and_no_workspace():
+    a = _args(partials=1, num_splits=0)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+    n = ctypes.c_size_t(1)
+    a = _args(partials=1, num_splits=4)
+    assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK and n.value == 0

@@ -170,3 +170,53 @@ def test_status_flags_bad_page_without_faulting():
                                  status=s.status)
     torch.cuda.synchronize()
     assert int(s.status.item()) == dcp.DCP_ERANGE
+
+
+PARTS = [
+    # B, H, q_len, N, I, P, lens, base, k, window
+    (3, 96, 1, 8, 1, 64, [1, 700, 5000], "2", 4, 0),              # empty parts (short requests)
+    (2, 128, 4, 8, 64, 64, [3000, 65], "e", 3, 0),                # drafts, 2 row groups, interleave 64
+    (2, 96, 1, 4, 1, 64, [9000, 2000], "2", 5, 1000),             # sliding window: parts start at its tile
+]
+
+
+@pytest.mark.parametrize("B,H_,q_len,N,I,P,lens,base,k,window", PARTS)
+def test_unmerged_parts_merge_to_full(B, H_, q_len, N, I, P, lens, base, k, window):
+    from oracle import layout as OL
+    w, lens = custom(B, H_, q_len, N, P, lens, base)
+    print(f"parts B={B} H={H_} q_len={q_len} N={N} I={I} lens={lens.tolist()} k={k} window={window}", flush=True)
+    s = H.make_setup(w, I, lens=lens)
+    dev = s.q.device
+    o_parts = torch.empty((N, k, B, q_len, H_, workloads.V_DIM), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((N, k, B, q_len, H_), dtype=torch.float32, device=dev)
+    for r in range(N):
+        dcp.dcp_stripe_attn(s.lay, r, s.q, s.sp.pools[r], s.sp.tables[r], s.sp.seq_len, workloads.SCALE,
+                            s.base_flag, num_splits=k, o=o_parts[r], lse=lse_parts[r], status=s.status,
+                            window=window, partials=True)
+    o, lse = dcp.dcp_lse_merge(o_parts.view(N * k, B, q_len, H_, workloads.V_DIM),
+                               lse_parts.view(N * k, B, q_len, H_), s.base_flag)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    for b in range(B):
+        q64, kv64, S = H.request_inputs(s, b)
+        ref_o, ref_l = OA.full_attention(q64, kv64, S, workloads.SCALE, window=window)
+        H.assert_o_close(o[b].cpu().numpy(), ref_o, f"merged parts, request {b}")
+        H.assert_lse_close(lse[b].cpu().numpy(), OA.to_base(ref_l, base), f"merged parts lse, request {b}")
+        # every part against the oracle over the rows the header assigns to it
+        qp = np.repeat(OA.query_positions(S, q_len), H_)
+        lists = OL.stripe_positions(S, N, I)
+        for r in range(N):
+            pos = lists[r]
+            first = 0 if window == 0 else len(pos[pos < S - q_len + 1 - window])
+            t = -(-len(pos) // 32) - first // 32 if len(pos) else 0
+            cs = -(-t // k) if t else 0
+            for c in range(k):
+                lo = (first // 32 + c * cs) * 32
+                hi = min(lo + cs * 32, len(pos))
+                sel = pos[lo:hi] if hi > lo else pos[:0]
+                po, pl = OA.attention_rows(q64.reshape(q_len * H_, -1), qp, kv64[sel], sel, workloads.SCALE,
+                                           window=window)
+                H.assert_o_close(o_parts[r, c, b].cpu().numpy().reshape(q_len * H_, -1), po,
+                                 f"part {c}, request {b}, stripe {r}")
+                H.assert_lse_close(lse_parts[r, c, b].cpu().numpy().reshape(-1), OA.to_base(pl, base),
+                                   f"part lse {c}, request {b}, stripe {r}")

@@ -189,7 +189,7 @@ def test_wait_counts_cover_the_tail():
         check_waits(ntiles, STAGES)
 
 
-def check_workload(w, I, plant=None, num_splits=0, window=0):
+def check_workload(w, I, plant=None, num_splits=0, window=0, partials=0):
     lens = workloads.seq_lens(w)
     N, P = w.N, w.page_size
     counts = H.oracle_counts(lens, N, I)
@@ -205,7 +205,13 @@ def check_workload(w, I, plant=None, num_splits=0, window=0):
         # row its first query sees
         first = count_rows(lens - w.q_len + 1 - window, N, I, r) if window > 0 else np.zeros_like(max_vis)
         ft = [int(f) // TILE for f in first]
-        wl = work_list([cdiv(int(v), TILE) - ft[b] if v > 0 else 0 for b, v in enumerate(max_vis)], forced, target)
+        tiles = [cdiv(int(v), TILE) - ft[b] if v > 0 else 0 for b, v in enumerate(max_vis)]
+        if partials:
+            # unmerged parts: exactly k per request, ceil(t / k) tiles each
+            slots = B * partials
+            wl = [(b, c, partials, cdiv(t, partials) if t else 0) for b, t in enumerate(tiles) for c in range(partials)]
+        else:
+            wl = work_list(tiles, forced, target)
         assert len(wl) <= slots                        # every chunk has a workgroup
         for (b, sp, nchunks, cs) in wl:
             if True:
@@ -239,6 +245,11 @@ def check_workload(w, I, plant=None, num_splits=0, window=0):
                                     ("dsv3", 128), ("long", 256)])
 def test_dma_loads_stay_in_the_tile_page(name, I):
     check_workload(workloads.WORKLOADS[name], I)
+
+
+@pytest.mark.parametrize("name,I,k", [("k3", 1, 4), ("ragged", 1, 3), ("long", 64, 7), ("tiny", 1, 5)])
+def test_unmerged_parts_stay_in_the_tile_page(name, I, k):
+    check_workload(workloads.WORKLOADS[name], I, partials=k)
 
 
 @pytest.mark.parametrize("name,I,window", [("tiny", 1, 100), ("ragged", 1, 1000), ("dsv3", 1, 4097),
