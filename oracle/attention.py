@@ -203,3 +203,64 @@ def to_base(lse_e: np.ndarray, base: str) -> np.ndarray:
     if base == "2":
         return lse_e / LN2
     raise ValueError("base must be 'e' or '2'")
+
+
+# ---- head-return exchange: packed (o bf16, lse fp32) all-to-all payload ------
+#
+# Page "DCP" (zdszero), "merge: All-to-All": each rank cuts its partial O_r by
+# head into N slices and sends slice d, together with the matching LSE, to the
+# rank that owns those heads, in one packed buffer; the receiver merges the N
+# partials of its H/N heads.  Page "MLA 的 Decode Context Parallelism",
+# section 4: the payload is 64 x 96 x (512 + 4) x 2 bytes at B = 64, i.e. a
+# record of 516 16-bit slots per (row, head): the output in bf16, then the LSE
+# as a float32 in two slots and two slots of padding (8-byte records).
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of float32 values, rounded to nearest, ties to even
+    (NaN stays a quiet NaN).  Written from the definition: keep the top 16 bits
+    of the float32 pattern after adding half an ulp of the kept part, plus one
+    more when the kept part is odd."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, ((b >> 16) | 0x40).astype(np.uint16), rounded)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pack_heads(o_r: np.ndarray, lse_r: np.ndarray, N: int) -> np.ndarray:
+    """One rank's packed send buffer.
+
+    o_r [rows, H, v] and lse_r [rows, H] (float32 values); H % N == 0.
+    Returns uint16 [N, rows, H/N, v + 4]: record (d, row, j) holds head
+    d*H/N + j -- its output as bf16, then its lse as the two 16-bit halves of
+    the float32 pattern (low half first), then two zero slots."""
+    o_r = np.asarray(o_r, dtype=np.float32)
+    lse_r = np.asarray(lse_r, dtype=np.float32)
+    rows, H, v = o_r.shape
+    if H % N:
+        raise ValueError("heads must split evenly over the ranks")
+    Hl = H // N
+    out = np.zeros((N, rows, Hl, v + 4), dtype=np.uint16)
+    lb = lse_r.view(np.uint32)
+    for d in range(N):
+        heads = slice(d * Hl, (d + 1) * Hl)
+        out[d, :, :, :v] = to_bf16_bits(o_r[:, heads, :])
+        out[d, :, :, v] = (lb[:, heads] & 0xFFFF).astype(np.uint16)
+        out[d, :, :, v + 1] = (lb[:, heads] >> 16).astype(np.uint16)
+    return out
+
+
+def unpack_merge(recv: np.ndarray, base: str = "e"):
+    """The owner's merge of what it received: recv [N, rows, Hl, v + 4] (record
+    layout of ``pack_heads``, part r from rank r) -> o [rows, Hl, v],
+    lse [rows, Hl] by the exact LSE merge, in float64."""
+    recv = np.asarray(recv, dtype=np.uint16)
+    v = recv.shape[-1] - 4
+    o_parts = bf16_bits_to_float(recv[..., :v])
+    lse_bits = recv[..., v].astype(np.uint32) | (recv[..., v + 1].astype(np.uint32) << 16)
+    lse_parts = lse_bits.view(np.float32).astype(np.float64)
+    return lse_merge(o_parts, lse_parts, base)

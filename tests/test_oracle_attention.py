@@ -457,3 +457,58 @@ def test_sink_added_on_every_stripe_is_counted_every_time():
     _, lse = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     want = np.log(np.exp(l_plain[0]) + N * np.exp(sinks))
     assert np.allclose(lse[0], want, rtol=1e-12, atol=1e-12)
+
+
+# ---- head-return exchange (packed bf16 output + fp32 lse) --------------------
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-40, 3.4e38, 1.0 + 2 ** -8,
+                                  1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, 65504.0], dtype=np.float32)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(A.to_bf16_bits(x), want)
+    assert np.isnan(A.bf16_bits_to_float(A.to_bf16_bits(np.array([np.nan], dtype=np.float32)))).all()
+
+
+def test_pack_layout_and_round_trip():
+    rng = np.random.default_rng(22)
+    rows, H, N, v = 5, 12, 4, 8
+    o = rng.standard_normal((rows, H, v)).astype(np.float32)
+    lse = (rng.standard_normal((rows, H)) * 30).astype(np.float32)
+    lse[0, 3] = -np.inf
+    buf = A.pack_heads(o, lse, N)
+    assert buf.shape == (N, rows, H // N, v + 4)
+    for h in range(H):
+        d, j = divmod(h, H // N)
+        assert np.array_equal(A.bf16_bits_to_float(buf[d, :, j, :v]), A.bf16_bits_to_float(A.to_bf16_bits(o[:, h])))
+        bits = buf[d, :, j, v].astype(np.uint32) | (buf[d, :, j, v + 1].astype(np.uint32) << 16)
+        assert np.array_equal(bits.view(np.float32), lse[:, h])            # the lse travels exactly
+        assert (buf[d, :, j, v + 2:] == 0).all()
+    # the page's payload at B = 64, H = 96, v = 512: 64 x 96 x (512 + 4) x 2 bytes
+    assert A.pack_heads(np.zeros((64, 96, 512)), np.zeros((64, 96)), 8).nbytes == 64 * 96 * (512 + 4) * 2
+
+
+def test_head_return_merge_equals_full_attention_within_bf16():
+    # stripes -> per-rank packing -> all-to-all -> each owner merges its heads:
+    # every head of the full result, up to the bf16 rounding of the partials
+    rng = np.random.default_rng(23)
+    S, H, q_len, N = 53, 8, 2, 4
+    q, kv = rand_case(rng, S, H, q_len)
+    o_full, l_full = A.full_attention(q, kv, S, SCALE)
+    lists = L.stripe_positions(S, N, 1)
+    sends = []
+    for r in range(N):
+        o_r, l_r = A.stripe_attention(q, kv, S, lists[r], SCALE)
+        sends.append(A.pack_heads(o_r.reshape(q_len, H, V), l_r.reshape(q_len, H), N))
+    Hl = H // N
+    for d in range(N):
+        recv = np.stack([sends[r][d] for r in range(N)])                   # what rank d receives
+        o, lse = A.unpack_merge(recv)
+        heads = slice(d * Hl, (d + 1) * Hl)
+        ref = o_full[:, heads]
+        # a convex combination of parts, each within half a bf16 ulp (2^-8 relative) of its value
+        bound = 2.0 ** -8 * np.max(np.abs(np.stack([A.stripe_attention(q, kv, S, lists[r], SCALE)[0][:, heads]
+                                                    for r in range(N)])), axis=0) + 1e-12
+        assert (np.abs(o - ref) <= bound).all()
+        assert np.allclose(lse, l_full[:, heads], rtol=0, atol=1e-5)     # lse exact up to float32
