@@ -247,6 +247,26 @@ int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);
  * (o_r, lse_r) (page "DCP", idea two; page "MLA 的 DCP", section 3). */
 int dcp_stripe_attn(const dcp_attn_args* args, void* stream);
 
+/* Head-return exchange (page "DCP", "merge: All-to-All"; page "MLA 的 DCP",
+ * section 4, step 6): every rank packs its (o_r, lse_r) by destination -- the
+ * rank that owns the heads -- into one buffer; after the all-to-all each
+ * owner merges the N partials of its H/N heads.  Record of one (row, head):
+ * v_dim bf16 output values (rounded to nearest even), the float32 lse in the
+ * next two 16-bit slots, two zero slots: v_dim + 4 slots, 8-byte aligned.
+ *
+ * dcp_pack_heads -- o_r [rows][H][v_dim] fp32, lse_r [rows][H] fp32 (device;
+ *   rows = B * q_len) -> send [N][rows][H/N][v_dim + 4] 16-bit slots (device):
+ *   block d is what goes to rank d (heads d*H/N .. (d+1)*H/N - 1).
+ *   H % N != 0 or v_dim % 4 != 0: DCP_EINVAL.
+ * dcp_merge_heads -- recv [N][rows][v_dim + 4] (device; block r came from rank
+ *   r, rows = B * q_len * H/N records) -> o [rows][v_dim] fp32, lse [rows] fp32
+ *   (nullable), the exact merge in lse_base (that of the packed lse).  Parts
+ *   with lse = -inf have zero weight and are not read. */
+int dcp_pack_heads(int32_t n_stripes, int64_t rows, int32_t n_heads, int32_t v_dim,
+                   const float* o_r, const float* lse_r, void* send, void* stream);
+int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* recv,
+                    int32_t lse_base, float* o, float* lse, void* stream);
+
 /* dcp_lse_merge -- exact merge of N stripes' partial results.
  * Page "DCP", "merge operator and numerical stability"; SGLang DCP docs,
  * "MLA decode dataflow": m = max_r lse_r, w_r = base^(lse_r - m),

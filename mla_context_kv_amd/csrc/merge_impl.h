@@ -35,26 +35,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Merge of one row by one wavefront.  Part r of the row: o at
-// o_parts[r * stride * v4 ...], lse at lse_parts[r * stride]; the result goes
-// to o_row[0 .. v4) and *lse_out (when not NULL).  in_base2 / out_base2
-// select the base of the input and output lse.  The lanes first hold the parts' lse
-// (64 parts at a time) for the max and the weight sum, then every lane merges
-// two 16-byte column slices, with the loads of 8 parts in flight before their
-// FMAs.  Parts of weight zero (lse = -inf, or an underflowed weight) are never
-// read.
-__device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t v4,
-                                              const float4* __restrict__ o_parts,
-                                              const float* __restrict__ lse_parts, int32_t in_base2,
-                                              int32_t out_base2, float4* __restrict__ o_row,
-                                              float* __restrict__ lse_out) {
+// Merge of one row by one wavefront.  `src` gives part r's lse (src.lse(r))
+// and its 16-byte column slice c as four floats (src.o4(r, c)); the result
+// goes to o_row[0 .. v4) and *lse_out (when not NULL).  in_base2 / out_base2
+// select the base of the input and output lse.  The lanes first hold the
+// parts' lse (64 parts at a time) for the max and the weight sum, then every
+// lane merges two 16-byte column slices, with the loads of 8 parts in flight
+// before their FMAs.  Parts of weight zero (lse = -inf, or an underflowed
+// weight) are never read.
+template <class Src>
+__device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src, int32_t in_base2,
+                                          int32_t out_base2, float4* __restrict__ o_row,
+                                          float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
   // weights are base^(lse_r - m): the difference is taken in the input base
   // (exact for nearby values) and only then scaled into base 2 for exp2
   const float to2 = in_base2 ? 1.0f : kLog2e;
   float m = -INFINITY;
   for (int r0 = 0; r0 < N; r0 += 64)
-    if (r0 + lane < N) m = fmaxf(m, lse_parts[(int64_t)(r0 + lane) * stride]);
+    if (r0 + lane < N) m = fmaxf(m, src.lse(r0 + lane));
   m = wave_max(m);
   if (m == -INFINITY) {
     for (int c = lane; c < v4; c += 64) o_row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -63,7 +62,7 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
   }
   float wsum = 0.f;
   for (int r0 = 0; r0 < N; r0 += 64) {
-    const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * stride] : -INFINITY;
+    const float x = r0 + lane < N ? src.lse(r0 + lane) : -INFINITY;
     wsum += x == -INFINITY ? 0.f : exp2f((x - m) * to2);
   }
   wsum = wave_sum(wsum);
@@ -73,7 +72,7 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
     const bool in0 = c0 < v4, in1 = c1 < v4;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
     for (int r0 = 0; r0 < N; r0 += 64) {
-      const float x = r0 + lane < N ? lse_parts[(int64_t)(r0 + lane) * stride] : -INFINITY;
+      const float x = r0 + lane < N ? src.lse(r0 + lane) : -INFINITY;
       const float w = x == -INFINITY ? 0.f : exp2f((x - m) * to2) * inv;   // lane k: weight of part r0 + k
       const int nr = min(64, N - r0);
       for (int u = 0; u < nr; u += 8) {
@@ -84,9 +83,8 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
           wu[k] = u + k < nr ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + k)) : 0.f;
           v0[k] = v1[k] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (wu[k] != 0.f) {
-            const float4* src = o_parts + (int64_t)(r0 + u + k) * stride * v4;
-            if (in0) v0[k] = src[c0];
-            if (in1) v1[k] = src[c1];
+            if (in0) v0[k] = src.o4(r0 + u + k, c0);
+            if (in1) v1[k] = src.o4(r0 + u + k, c1);
           }
         }
 #pragma unroll
@@ -111,6 +109,25 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
     const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
     *lse_out = m_out + (out_base2 ? lw2 : lw2 * kLn2);
   }
+}
+
+// fp32 parts: part r of the row at o_parts[r * stride * v4 ...], lse at
+// lse_parts[r * stride]
+struct Fp32Parts {
+  const float4* __restrict__ o;
+  const float* __restrict__ l;
+  int64_t stride;
+  int32_t v4;
+  __device__ float lse(int r) const { return l[(int64_t)r * stride]; }
+  __device__ float4 o4(int r, int c) const { return o[(int64_t)r * stride * v4 + c]; }
+};
+
+__device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t v4,
+                                              const float4* __restrict__ o_parts,
+                                              const float* __restrict__ lse_parts, int32_t in_base2,
+                                              int32_t out_base2, float4* __restrict__ o_row,
+                                              float* __restrict__ lse_out) {
+  merge_row(N, v4, Fp32Parts{o_parts, lse_parts, stride, v4}, in_base2, out_base2, o_row, lse_out);
 }
 
 // Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at

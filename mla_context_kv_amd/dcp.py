@@ -85,6 +85,8 @@ _SIGNATURES = {
     "dcp_stripe_attn_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "dcp_pack_heads": (ctypes.c_int, [_I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "dcp_merge_heads": (ctypes.c_int, [_I32, _I64, _I32, _VP, _I32, _VP, _VP, _VP]),
     "dcp_relayout": (ctypes.c_int, [dcp_layout, _I32, _I32, _VP, _I64, _I32, _VP, _I32, _VP, _VP, _I32, _I64,
                                     _VP, _I32, _VP, _I64, _VP, _VP]),
 }
@@ -315,4 +317,42 @@ def dcp_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, lse_base: int 
                              _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev),
                              _stream(dev))
     _check(rc, "dcp_lse_merge")
+    return o, lse
+
+
+def dcp_pack_heads(o_r: torch.Tensor, lse_r: torch.Tensor, n_stripes: int,
+                   send: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pack one rank's (o_r [B, q_len, H, V] fp32, lse_r [B, q_len, H] fp32) by head owner:
+    returns send int16 [N, B*q_len, H/N, V + 4] (bf16 output, fp32 lse, padding per record)."""
+    dev = o_r.device
+    H, v = int(o_r.shape[-2]), int(o_r.shape[-1])
+    rows = int(o_r.numel() // (H * v))
+    N = int(n_stripes)
+    if lse_r.numel() != rows * H or H % N:
+        raise ValueError("lse_r must be [..., H] matching o_r, and H a multiple of n_stripes")
+    if send is None:
+        send = torch.empty((N, rows, H // N, v + 4), dtype=torch.int16, device=dev)
+    if send.numel() != N * rows * (H // N) * (v + 4):
+        raise ValueError("send has the wrong size")
+    rc = lib().dcp_pack_heads(N, rows, H, v, _ptr(o_r, torch.float32, "o_r", dev), _ptr(lse_r, torch.float32, "lse_r", dev),
+                              _ptr(send, torch.int16, "send", dev), _stream(dev))
+    _check(rc, "dcp_pack_heads")
+    return send
+
+
+def dcp_merge_heads(recv: torch.Tensor, lse_base: int = 0, o: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None):
+    """The owner's merge of received records recv int16 [N, rows..., V + 4]:
+    returns o fp32 [rows..., V] and lse fp32 [rows...]."""
+    dev = recv.device
+    N = int(recv.shape[0])
+    v = int(recv.shape[-1]) - 4
+    rows = int(recv[0].numel() // (v + 4))
+    if o is None:
+        o = torch.empty(tuple(recv.shape[1:-1]) + (v,), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(tuple(recv.shape[1:-1]), dtype=torch.float32, device=dev)
+    rc = lib().dcp_merge_heads(N, rows, v, _ptr(recv, torch.int16, "recv", dev), int(lse_base),
+                               _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev), _stream(dev))
+    _check(rc, "dcp_merge_heads")
     return o, lse

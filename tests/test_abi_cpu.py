@@ -15,7 +15,8 @@ FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails
 def test_library_exports_every_declared_function():
     names = dcp.header_functions()
     assert {"dcp_slot_map", "dcp_local_count", "dcp_kv_write", "dcp_stripe_attn",
-            "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror", "dcp_relayout"} <= set(names)
+            "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror", "dcp_relayout", "dcp_pack_heads",
+            "dcp_merge_heads"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -179,3 +180,16 @@ def test_unmerged_parts_need_a_split_count_and_no_workspace():
     n = ctypes.c_size_t(1)
     a = _args(partials=1, num_splits=4)
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK and n.value == 0
+
+
+def test_pack_and_merge_heads_argument_errors():
+    assert L.dcp_pack_heads(8, 4, 12, 512, FAKE, FAKE, FAKE, None) == dcp.DCP_EINVAL     # 12 heads over 8
+    assert L.dcp_pack_heads(0, 4, 16, 512, FAKE, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_pack_heads(4, 4, 16, 510, FAKE, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_pack_heads(4, -1, 16, 512, FAKE, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_pack_heads(4, 4, 16, 512, None, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_pack_heads(4, 0, 16, 512, None, None, None, None) == dcp.DCP_OK
+    assert L.dcp_merge_heads(0, 4, 512, FAKE, 0, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_merge_heads(4, 4, 512, FAKE, 2, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_merge_heads(4, 4, 6, FAKE, 0, FAKE, FAKE, None) == dcp.DCP_EINVAL
+    assert L.dcp_merge_heads(4, 4, 512, None, 0, FAKE, FAKE, None) == dcp.DCP_EINVAL
