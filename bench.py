@@ -46,8 +46,9 @@ def parse():
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="step", choices=["step", "relayout"],
-                    help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout")
+    ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return"],
+                    help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout; "
+                         "head-return: pack by head owner + the owners' merges")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
@@ -100,6 +101,9 @@ def main():
         sys.exit(1)
     if args.op == "relayout":
         run_relayout(args)
+        return
+    if args.op == "head-return":
+        run_head_return(args)
         return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
@@ -300,6 +304,86 @@ def main():
                      "bytes_per_launch": int(stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_head_return(args):
+    """Head-return exchange at the workload's shape: each of the N ranks packs
+    its (o_r, lse_r) by head owner (dcp_pack_heads) and each owner merges the N
+    records of its H/N heads (dcp_merge_heads).  The all-to-all between them is
+    a plain block transpose on one GPU and is not timed.  Inputs: seeded
+    partial results of the right shape (their values do not change the work)."""
+    import torch
+    from mla_context_kv_amd import dcp, workloads
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    N, V = w.N, 512
+    rows = w.B * w.q_len
+    Hl = w.H // N
+    g = torch.Generator(device=dev).manual_seed(5)
+    o_r = [torch.randn((rows, w.H, V), generator=g, device=dev) for _ in range(N)]
+    lse_r = [torch.randn((rows, w.H), generator=g, device=dev) * 4 for _ in range(N)]
+    send = torch.empty((N, N, rows, Hl, V + 4), dtype=torch.int16, device=dev)
+    recv = torch.empty((N, N, rows, Hl, V + 4), dtype=torch.int16, device=dev)
+    o = torch.empty((N, rows, Hl, V), dtype=torch.float32, device=dev)
+    lse = torch.empty((N, rows, Hl), dtype=torch.float32, device=dev)
+    base = 1 if w.lse_base == "2" else 0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for r in range(N):
+            dcp.dcp_pack_heads(o_r[r], lse_r[r], N, send=send[r])
+        if ev is not None:
+            ev[0].record(stream)
+        recv.copy_(send.transpose(0, 1))                     # the all-to-all, emulated (not timed)
+        if ev is not None:
+            ev[1].record(stream)
+        for d in range(N):
+            dcp.dcp_merge_heads(recv[d], base, o=o[d], lse=lse[d])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        step(evs[k][1:])
+    torch.cuda.synchronize()
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    rec = V * 2 + 8
+    pack_bytes = N * (rows * w.H * (V * 4 + 4) + rows * w.H * rec)         # read fp32 partials, write records
+    merge_bytes = N * (N * rows * Hl * rec + rows * Hl * (V + 1) * 4)      # read N records per row, write o, lse
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attention as OA
+        n_rows = min(4 * w.q_len, rows)                        # 4 requests
+        parts = [(o_r[r][:n_rows].cpu().numpy(), lse_r[r][:n_rows].cpu().numpy()) for r in range(N)]
+        t1 = time.perf_counter()
+        sends = [OA.pack_heads(po, pl, N) for po, pl in parts]
+        for d in range(N):
+            OA.unpack_merge(np.stack([sends[r][d] for r in range(N)]), w.lse_base)
+        cpu_s = time.perf_counter() - t1
+        nb = (pack_bytes + merge_bytes) * n_rows / rows
+        cpu = {"value": round(nb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seconds": round(cpu_s, 3), "sample": f"{n_rows // w.q_len} of {w.B} requests: pack + merge in NumPy"}
+    t_ms = pack_ms + merge_ms
+    gbs = (pack_bytes + merge_bytes) / (t_ms * 1e-3) / 1e9
+    out = {
+        "metric": "head-return pack + owner merge GB/s (all N ranks, all-to-all excluded), 1 GPU",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "op": "head-return", "B": w.B, "q_len": w.q_len, "H": w.H, "N": N,
+                   "record_bytes": rec, "payload_bytes_per_rank": rows * w.H * rec},
+        "pack_us_all_ranks": round(pack_ms * 1e3, 1), "merge_us_all_owners": round(merge_ms * 1e3, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "N dcp_pack_heads + N dcp_merge_heads"},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
