@@ -39,6 +39,9 @@ no positions):
 * logit softcap c: each scaled score s becomes c * tanh(s / c);
 * attention sink: one extra logit sigma per query row with value zero, i.e.
   exp(sigma) joins the denominator; in a sharded run exactly one shard adds it.
+* position bias (linear in the distance, ALiBi style): the logit of position p
+  for a query at t gains slope * (p - t), after the softcap; it depends only
+  on the pair's own positions, so each shard adds it for its own positions.
 """
 
 from __future__ import annotations
@@ -52,7 +55,7 @@ LN2 = math.log(2.0)
 
 def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.ndarray,
                    scale: float, v_dim: int = 512, chunk: int | None = None,
-                   window: int = 0, softcap: float = 0.0, sink=None):
+                   window: int = 0, softcap: float = 0.0, sink=None, slope=None):
     """Softmax attention of R query rows over n latent rows, in float64.
 
     q      [R, D] query rows (D = 576)
@@ -62,6 +65,7 @@ def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.
     window > 0    also hides rows with kv_pos <= q_pos - window
     softcap > 0   replaces each scaled score s by softcap * tanh(s / softcap)
     sink   [R]    natural-log logit of an extra zero-valued term per row (None: none)
+    slope  [R]    position bias slope per row: logit += slope * (kv_pos - q_pos) (None: none)
     Returns o [R, v_dim] and the natural-log lse [R]; a query that sees no row
     (and has no sink) gets o = 0 and lse = -inf.
 
@@ -82,6 +86,8 @@ def attention_rows(q: np.ndarray, q_pos: np.ndarray, kv: np.ndarray, kv_pos: np.
         s = (kv[lo:hi] @ q.T) * scale                       # [rows, R]
         if softcap > 0:
             s = softcap * np.tanh(s / softcap)
+        if slope is not None:
+            s = s + np.asarray(slope, dtype=np.float64)[None, :] * (kv_pos[lo:hi, None] - q_pos[None, :])
         hidden = kv_pos[lo:hi, None] > q_pos[None, :]
         if window > 0:
             hidden |= kv_pos[lo:hi, None] <= q_pos[None, :] - window
@@ -121,7 +127,7 @@ def query_positions(S: int, q_len: int) -> np.ndarray:
 
 
 def _row_sinks(sinks, q_len: int, H: int):
-    """Per-head sink logits [H] as one value per query row (t, h), or None."""
+    """Per-head values [H] (sink logits, bias slopes) as one value per query row (t, h), or None."""
     if sinks is None:
         return None
     return np.tile(np.asarray(sinks, dtype=np.float64).reshape(H), q_len)
@@ -129,24 +135,25 @@ def _row_sinks(sinks, q_len: int, H: int):
 
 def full_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, scale: float,
                    v_dim: int = 512, chunk: int | None = None,
-                   window: int = 0, softcap: float = 0.0, sinks=None):
+                   window: int = 0, softcap: float = 0.0, sinks=None, slopes=None):
     """Unsharded attention of one request.
 
     q_req [q_len, H, D], kv_req [S, D] (logical order, position p at row p).
-    window / softcap as in ``attention_rows``; sinks [H] per-head sink logits.
+    window / softcap as in ``attention_rows``; sinks [H] per-head sink logits;
+    slopes [H] per-head position-bias slopes.
     Returns o [q_len, H, v_dim] and natural-log lse [q_len, H].
     """
     q_len, H, D = q_req.shape
     qp = np.repeat(query_positions(S, q_len), H)
     o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[:S],
                             np.arange(S, dtype=np.int64), scale, v_dim, chunk,
-                            window, softcap, _row_sinks(sinks, q_len, H))
+                            window, softcap, _row_sinks(sinks, q_len, H), _row_sinks(slopes, q_len, H))
     return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
 
 
 def stripe_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, positions: np.ndarray,
                      scale: float, v_dim: int = 512, chunk: int | None = None,
-                     window: int = 0, softcap: float = 0.0, sinks=None):
+                     window: int = 0, softcap: float = 0.0, sinks=None, slopes=None):
     """Local attention of one request on one stripe.
 
     ``positions`` are the global positions the rank owns (as handed out by
@@ -162,7 +169,7 @@ def stripe_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, positions: n
     qp = np.repeat(query_positions(S, q_len), H)
     o, lse = attention_rows(q_req.reshape(q_len * H, D), qp, kv_req[positions],
                             positions, scale, v_dim, chunk,
-                            window, softcap, _row_sinks(sinks, q_len, H))
+                            window, softcap, _row_sinks(sinks, q_len, H), _row_sinks(slopes, q_len, H))
     return o.reshape(q_len, H, v_dim), lse.reshape(q_len, H)
 
 

@@ -287,14 +287,15 @@ def test_chunked_evaluation_is_the_same_sum():
 # ---- mergeable variants: sliding window, logit softcap, attention sink ------
 # (page "DCP", "conditions for merging and where they fail")
 
-def brute_variant(q_row, kv, kv_pos, q_pos, scale, window=0, softcap=0.0, sink=None):
+def brute_variant(q_row, kv, kv_pos, q_pos, scale, window=0, softcap=0.0, sink=None, slope=0.0):
     """The variant definitions evaluated term by term with math.fsum."""
     vis = [i for i in range(len(kv))
            if kv_pos[i] <= q_pos and (window <= 0 or kv_pos[i] > q_pos - window)]
     s = []
     for i in vis:
         x = scale * math.fsum(float(q_row[d]) * float(kv[i][d]) for d in range(D))
-        s.append(softcap * math.tanh(x / softcap) if softcap > 0 else x)
+        x = softcap * math.tanh(x / softcap) if softcap > 0 else x
+        s.append(x + slope * (kv_pos[i] - q_pos))
     terms = s + ([sink] if sink is not None else [])
     if not terms:
         return [0.0] * V, -math.inf
@@ -306,7 +307,8 @@ def brute_variant(q_row, kv, kv_pos, q_pos, scale, window=0, softcap=0.0, sink=N
 
 
 VARIANTS = [dict(window=3), dict(window=1), dict(softcap=0.5), dict(sinks=[0.7, -1.3]),
-            dict(window=4, softcap=1.0, sinks=[2.0, 0.1])]
+            dict(window=4, softcap=1.0, sinks=[2.0, 0.1]), dict(slopes=[0.25, 0.0625]),
+            dict(slopes=[0.5, 1.0], softcap=2.0, sinks=[0.0, 1.0])]
 
 
 def _close(o, lse, bo, bl):
@@ -324,10 +326,11 @@ def test_variants_against_brute_force(var):
     q, kv = rand_case(rng, S, H, q_len, kv_std=1.0)
     o, lse = A.full_attention(q, kv, S, SCALE, **var)
     sinks = var.get("sinks")
+    slopes = var.get("slopes", [0.0] * H)
     for t in range(q_len):
         for h in range(H):
             bo, bl = brute_variant(q[t, h], kv, list(range(S)), S - q_len + t, SCALE, var.get("window", 0),
-                                   var.get("softcap", 0.0), None if sinks is None else sinks[h])
+                                   var.get("softcap", 0.0), None if sinks is None else sinks[h], slopes[h])
             _close(o[t, h], lse[t, h], bo, bl)
     # one stripe of a block round-robin layout, the sink on this stripe
     pos = L.stripe_positions(S, 3, 2)[1]
@@ -336,7 +339,7 @@ def test_variants_against_brute_force(var):
         for h in range(H):
             bo, bl = brute_variant(q[t, h], [kv[p] for p in pos.tolist()], pos.tolist(), S - q_len + t, SCALE,
                                    var.get("window", 0), var.get("softcap", 0.0),
-                                   None if sinks is None else sinks[h])
+                                   None if sinks is None else sinks[h], slopes[h])
             _close(o[t, h], lse[t, h], bo, bl)
 
 
@@ -512,3 +515,35 @@ def test_head_return_merge_equals_full_attention_within_bf16():
                                                     for r in range(N)])), axis=0) + 1e-12
         assert (np.abs(o - ref) <= bound).all()
         assert np.allclose(lse, l_full[:, heads], rtol=0, atol=1e-5)     # lse exact up to float32
+
+
+def test_position_bias_with_zero_query_is_geometric():
+    # every score is 0: position p of a query at t has weight exp(-lam (t - p)),
+    # a geometric series over p = 0..t
+    rng = np.random.default_rng(15)
+    S, H, q_len = 12, 2, 2
+    kv = rng.standard_normal((S, D))
+    q = np.zeros((q_len, H, D))
+    lam = np.array([0.3, 1.7])
+    o, lse = A.full_attention(q, kv, S, SCALE, slopes=lam)
+    for t in range(q_len):
+        pq = S - q_len + t
+        for h in range(H):
+            r = math.exp(-lam[h])
+            w = np.array([r ** (pq - p) for p in range(pq + 1)])
+            assert np.allclose(o[t, h], (w[:, None] * kv[:pq + 1, :V]).sum(axis=0) / w.sum(), rtol=1e-12, atol=1e-14)
+            assert abs(lse[t, h] - math.log((1 - r ** (pq + 1)) / (1 - r))) < 1e-12
+
+
+def test_position_bias_uses_global_positions_on_a_stripe():
+    # on a stripe the bias of a row is its GLOBAL distance: with q = 0 and
+    # token round robin, rank r's weights are exp(-lam (t - p)) over its own p
+    rng = np.random.default_rng(16)
+    S, N, lam = 20, 4, 0.4
+    kv = rng.standard_normal((S, D))
+    q = np.zeros((1, 1, D))
+    for r, pos in enumerate(L.stripe_positions(S, N, 1)):
+        o, lse = A.stripe_attention(q, kv, S, pos, SCALE, slopes=[lam])
+        w = np.exp(-lam * (S - 1 - pos))
+        assert np.allclose(o[0, 0], (w[:, None] * kv[pos, :V]).sum(axis=0) / w.sum(), rtol=1e-12, atol=1e-14)
+        assert abs(lse[0, 0] - math.log(w.sum())) < 1e-12
