@@ -198,7 +198,11 @@ int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim,
  *          joins the softmax denominator with value zero.  Pass it on
  *          exactly one rank's call: the merge adds the stripes' partition
  *          functions, so a sink given to k ranks counts k times.  A row with
- *          no visible position then gets o = 0 and lse = the sink. */
+ *          no visible position then gets o = 0 and lse = the sink.
+ * bias_slopes [n_heads] fp32 device, nullable: linear position bias (ALiBi
+ *          style) -- the logit of position p for a query at t of head h gains
+ *          bias_slopes[h] * (p - t), natural-log units, after the softcap.
+ *          Positions are global, so every rank passes the same slopes. */
 typedef struct dcp_attn_args {
   dcp_layout layout;
   int32_t rank;
@@ -225,6 +229,7 @@ typedef struct dcp_attn_args {
   float softcap;
   const float* sinks;
   int32_t partials;
+  const float* bias_slopes;
 } dcp_attn_args;
 
 /* Unmerged parts (page "DCP", "unification with online softmax": the split

@@ -43,8 +43,9 @@
 //    stripes (the chunks are a disjoint partition of the stripe's rows).
 //  * Variants that keep the merge exact (page "DCP", conditions for merging):
 //    a sliding window only moves each row's first visible local row (and the
-//    request's first tile); a logit softcap transforms each score right after
-//    QK^T (its own kernel instantiation); an attention sink adds one
+//    request's first tile); a logit softcap and a linear position bias
+//    transform each score right after QK^T (their own kernel instantiation;
+//    the bias uses the row's GLOBAL position); an attention sink adds one
 //    zero-valued logit per head to the denominator of the request's first
 //    chunk -- the caller gives it to one rank only.
 #include "dcp_common.h"
@@ -136,6 +137,8 @@ struct Params {
   int32_t window;                   // > 0: a query at t sees t - window < p <= t
   float cap_in, cap_out;            // softcap: s -> cap_out * tanh(s * cap_in) (raw-score units)
   const float* sinks;               // [H] natural-log sink logits, nullable
+  const float* slopes;              // [H] position-bias slopes (natural-log units), nullable
+  float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
   float* o;                         // final outputs (requests cut into one chunk)
   float* lse;
@@ -363,7 +366,7 @@ __device__ __forceinline__ float other_half(float v) {
 // the tile loads, waves 4..7 accumulate PV for 128 value columns each -- so
 // one wave's softmax and LDS waits overlap the other wave's MFMAs on the
 // same SIMD; one barrier per tile, P^T double-buffered.
-template <int RB, bool kAligned, bool kCap>
+template <int RB, bool kAligned, bool kLogit>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * kNW, 64 * kNW), amdgpu_waves_per_eu(2, 2)))
 stripe_attn_kernel(Params p) {
   static_assert(RB >= 1 && RB <= kMaxRB, "query-row blocks");
@@ -531,16 +534,35 @@ stripe_attn_kernel(Params p) {
   auto tok_of = [&](int i) { return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + half; };
 
   const float c2 = p.c2;
-  // logit softcap, applied to the raw scores (kept in units where x * c2 is
-  // the capped score in base 2), before any masking.  tanh(y) = 1 - 2 / (e^2y + 1):
-  // one exp and one reciprocal; saturates to +-1 (e^2y = inf or 0), and its
-  // absolute error (a few ulp of 1) is a negligible shift of the capped score.
-  auto cap = [&](f32x16& x) {
-    if constexpr (kCap) {
+  // Logit transforms on the raw scores of the tile starting at local row j0
+  // (kept in units where x * c2 is the logit in base 2), before any masking.
+  // Softcap: tanh(y) = 1 - 2 / (e^2y + 1), one exp and one reciprocal; it
+  // saturates to +-1 (e^2y = inf or 0), and its absolute error (a few ulp of
+  // 1) is a negligible shift of the capped score.  Position bias: + slope *
+  // (p - t) with p the row's global position p = floor(j / I) I N + r I + j mod I.
+  float bias_raw = 0.f;                 // this row's slope in raw-score units
+  int32_t q_pos = 0;                    // this row's query position
+  if constexpr (kLogit) {
+    if (p.slopes != nullptr && valid) bias_raw = p.slopes[R % p.H] * p.inv_scale;
+    q_pos = S_b - p.q_len + t;
+  }
+  auto cap = [&](f32x16& x, int32_t j0) {
+    if constexpr (kLogit) {
+      if (p.cap_out > 0.f) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e2y = __builtin_amdgcn_exp2f(x[i] * p.cap_in * (2.0f * kLog2e));
-        x[i] = p.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2y + 1.0f));
+        for (int i = 0; i < 16; ++i) {
+          const float e2y = __builtin_amdgcn_exp2f(x[i] * p.cap_in * (2.0f * kLog2e));
+          x[i] = p.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2y + 1.0f));
+        }
+      }
+      if (p.slopes != nullptr) {
+        const int32_t round = p.N * p.I;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t j = j0 + tok_of(i);
+          const int32_t pos = (j / p.I) * round + p.rank * p.I + j % p.I;
+          x[i] += bias_raw * (float)(pos - q_pos);
+        }
       }
     }
   };
@@ -717,7 +739,7 @@ stripe_attn_kernel(Params p) {
       if (ntiles > 0) {
         wait_tiles_then_barrier<kMyLoads>(0);
         sacc = qk(smem);
-        cap(sacc);
+        cap(sacc, row_lo);
         vis = lim - row_lo;
         vlo = low - row_lo;
         sbuf = 0;
@@ -728,7 +750,7 @@ stripe_attn_kernel(Params p) {
           wait_tiles_then_barrier<kMyLoads>(0);
           if (it + 1 < ntiles) {
             sacc = qk(smem + ((it + 1) % kStages) * kStageBytes);
-            cap(sacc);
+            cap(sacc, row_lo + (it + 1) * kTile);
             vis = lim - (row_lo + (it + 1) * kTile);
             vlo = low - (row_lo + (it + 1) * kTile);
             sbuf = (it + 1) & 1;
@@ -868,7 +890,7 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   if (a->num_splits < 0) return DCP_EINVAL;
   if (a->partials != 0 && (a->partials != 1 || a->num_splits < 1)) return DCP_EINVAL;
   if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
-  if (a->softcap > 0.f && !(a->scale > 0.f)) return DCP_EINVAL;
+  if ((a->softcap > 0.f || a->bias_slopes != nullptr) && !(a->scale > 0.f)) return DCP_EINVAL;
   const int64_t M = (int64_t)a->q_len * a->n_heads;
   const int64_t max_rows = (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
@@ -941,18 +963,19 @@ chunk_combine_kernel(int32_t B, int32_t M, int32_t v4, const int32_t* __restrict
                 lse + row);
 }
 
-template <int RB, bool kCap>
+template <int RB, bool kLogit>
 int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
   if (prm.P % kTile == 0)
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, true, kCap>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, true, kLogit>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   else
-    hipLaunchKernelGGL((stripe_attn_kernel<RB, false, kCap>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
+    hipLaunchKernelGGL((stripe_attn_kernel<RB, false, kLogit>), dim3((unsigned)blocks), dim3(64 * kNW), 0, stream, prm);
   return launch_status();
 }
 
 template <int RB>
 int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
-  return prm.cap_out > 0.f ? launch<RB, true>(prm, blocks, stream) : launch<RB, false>(prm, blocks, stream);
+  const bool logit = prm.cap_out > 0.f || prm.slopes != nullptr;
+  return logit ? launch<RB, true>(prm, blocks, stream) : launch<RB, false>(prm, blocks, stream);
 }
 
 }  // namespace attn
@@ -1005,6 +1028,8 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.cap_in = a->softcap > 0.f ? a->scale / a->softcap : 0.f;
   prm.cap_out = a->softcap > 0.f ? a->softcap / a->scale : 0.f;
   prm.sinks = a->sinks;
+  prm.slopes = a->bias_slopes;
+  prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
   prm.o = a->o;
   prm.lse = a->lse;

@@ -68,6 +68,7 @@ class dcp_attn_args(ctypes.Structure):
         ("softcap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
         ("partials", ctypes.c_int32),
+        ("bias_slopes", ctypes.c_void_p),
     ]
 
 
@@ -253,10 +254,12 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
-                    sinks: Optional[torch.Tensor] = None, partials: bool = False):
+                    sinks: Optional[torch.Tensor] = None, partials: bool = False,
+                    bias_slopes: Optional[torch.Tensor] = None):
     """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
 
-    window / softcap / sinks select the mergeable variants (sinks: fp32 [H], on one rank only).
+    window / softcap / sinks / bias_slopes select the mergeable variants (sinks: fp32 [H], on one
+    rank only; bias_slopes: fp32 [H], on every rank).
     partials=True (with num_splits = k >= 1) returns the k unmerged parts instead:
     o [k,B,q_len,H,512], lse [k,B,q_len,H]."""
     dev = q.device
@@ -281,6 +284,8 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                    window, softcap, 1 if partials else 0)
     if sinks is not None and sinks.numel() != H:
         raise ValueError("sinks must hold one value per head")
+    if bias_slopes is not None and bias_slopes.numel() != H:
+        raise ValueError("bias_slopes must hold one value per head")
     need = ctypes.c_size_t(0)
     _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
     if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
@@ -295,6 +300,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.lse = _ptr(lse, torch.float32, "lse", dev)
     a.status = _ptr(status, torch.int32, "status", dev)
     a.sinks = _ptr(sinks, torch.float32, "sinks", dev)
+    a.bias_slopes = _ptr(bias_slopes, torch.float32, "bias_slopes", dev)
     _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
     return o, lse
 

@@ -76,19 +76,21 @@ def make_setup(w: workloads.Workload, interleave: int = 1, lens=None, nan_fill: 
 
 
 def run_step(s: Setup, num_splits: int = 0, window: int = 0, softcap: float = 0.0, sinks=None,
-             sink_rank: int = 0):
+             sink_rank: int = 0, slopes=None):
     """All N stripe attentions + merge, as one decode step (sinks, fp64 [H],
-    go to rank sink_rank only)."""
+    go to rank sink_rank only; position-bias slopes [H] to every rank)."""
     w = s.w
     dev = s.q.device
     N = s.lay.n_stripes
     o_parts = torch.empty((N, w.B, w.q_len, w.H, workloads.V_DIM), dtype=torch.float32, device=dev)
     lse_parts = torch.empty((N, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     sk = None if sinks is None else torch.tensor(np.asarray(sinks), dtype=torch.float32, device=dev)
+    sl = None if slopes is None else torch.tensor(np.asarray(slopes), dtype=torch.float32, device=dev)
     for r in range(N):
         dcp.dcp_stripe_attn(s.lay, r, s.q, s.sp.pools[r], s.sp.tables[r], s.sp.seq_len, workloads.SCALE,
                             s.base_flag, num_splits=num_splits, o=o_parts[r], lse=lse_parts[r], status=s.status,
-                            window=window, softcap=softcap, sinks=sk if r == sink_rank else None)
+                            window=window, softcap=softcap, sinks=sk if r == sink_rank else None,
+                            bias_slopes=sl)
     o, lse = dcp.dcp_lse_merge(o_parts, lse_parts, s.base_flag)
     torch.cuda.synchronize()
     return o_parts, lse_parts, o, lse
@@ -128,14 +130,18 @@ def assert_lse_close(got, ref, what=""):
 
 
 def check_request(s: Setup, o_parts, lse_parts, o, lse, b: int, heads=None, chunk=None, window=0, softcap=0.0,
-                  sinks=None, sink_rank=0):
+                  sinks=None, sink_rank=0, slopes=None):
     """Compare request b's merged output and every stripe's partial with the oracle."""
     q64, kv64, S = request_inputs(s, b, heads)
     hsel = slice(None) if heads is None else heads
     sinks = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
     if sinks is not None and heads is not None:
         sinks = sinks[heads]
-    var = dict(window=window, softcap=softcap)
+    if slopes is not None:
+        slopes = np.asarray(slopes, dtype=np.float32).astype(np.float64)
+        if heads is not None:
+            slopes = slopes[heads]
+    var = dict(window=window, softcap=softcap, slopes=slopes)
     ref_o, ref_l = OA.full_attention(q64, kv64, S, workloads.SCALE, chunk=chunk, sinks=sinks, **var)
     assert_o_close(o[b][:, hsel].cpu().numpy(), ref_o, f"merged o, request {b}")
     assert_lse_close(lse[b][:, hsel].cpu().numpy(), OA.to_base(ref_l, s.w.lse_base), f"merged lse, request {b}")

@@ -105,6 +105,12 @@ def test_stripe_attn_argument_errors(field, value, code):
     assert L.dcp_stripe_attn(ctypes.byref(a), None) == code
 
 
+def test_softcap_and_position_bias_need_a_positive_scale():
+    for kw in (dict(softcap=1.0, scale=0.0), dict(bias_slopes=0x1000, scale=-1.0)):
+        a = _args(**kw)
+        assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL, kw
+
+
 def test_stripe_attn_workspace_size_and_missing_workspace():
     a = _args(num_splits=3, bt_cols=100)
     n = ctypes.c_size_t(0)

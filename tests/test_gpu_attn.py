@@ -76,6 +76,8 @@ VARIANTS = [
     (2, 128, 2, 8, 1, 64, [2100, 65], "2", 0, 0, 0.8, False, 1.0),          # softcap, 2 row groups
     (3, 96, 1, 8, 1, 64, [1, 7, 900], "e", 0, 0, 0.0, True, 1.0),           # sinks, empty stripes
     (2, 96, 4, 8, 1, 64, [3000, 40], "2", 2, 700, 2.0, True, 1.0),          # all three, chunked
+    (2, 96, 1, 8, 1, 64, [3000, 333], "2", 0, 0, 0.0, "bias", 1.0),        # position bias over global positions
+    (2, 64, 3, 4, 64, 64, [2000, 65], "e", 3, 500, 1.5, "bias", 1.0),      # bias + window + softcap, I = 64
 ]
 
 
@@ -85,12 +87,16 @@ def test_variants_every_element(B, H_, q_len, N, I, P, lens, base, splits, windo
     print(f"variant B={B} H={H_} q_len={q_len} N={N} I={I} P={P} lens={lens.tolist()} splits={splits} "
           f"window={window} softcap={softcap} sink={sink}", flush=True)
     s = H.make_setup(w, I, lens=lens)
-    sinks = None
-    if sink:
+    sinks = slopes = None
+    if sink == "bias":
+        # ALiBi-style slopes 2^(-8 (h+1) / H), and one head without bias
+        slopes = 2.0 ** (-8.0 * (np.arange(H_) + 1) / H_)
+        slopes[1] = 0.0
+    elif sink:
         sinks = np.random.default_rng(1).normal(0.0, 2.0, H_)
         sinks[0] = 9.0                      # a sink far above every score
         sinks[-1] = -np.inf                 # no sink on this head
-    var = dict(window=window, softcap=softcap, sinks=sinks, sink_rank=N - 1)
+    var = dict(window=window, softcap=softcap, sinks=sinks, sink_rank=N - 1, slopes=slopes)
     o_parts, lse_parts, o, lse = H.run_step(s, splits, **var)
     assert int(s.status.item()) == 0
     for b in range(B):
