@@ -271,3 +271,34 @@ def unpack_merge(recv: np.ndarray, base: str = "e"):
     lse_bits = recv[..., v].astype(np.uint32) | (recv[..., v + 1].astype(np.uint32) << 16)
     lse_parts = lse_bits.view(np.float32).astype(np.float64)
     return lse_merge(o_parts, lse_parts, base)
+
+
+# ---- sparse attention with a global top-k selection -------------------------
+#
+# Page "DCP", "conditions for merging and where they fail": sparse attention
+# such as DSA's top-k stays mergeable when the top-k selection is made
+# globally; each rank then attends only to the selected tokens it owns.
+
+def sparse_attention(q_req: np.ndarray, kv_req: np.ndarray, S: int, topk: np.ndarray, scale: float,
+                     positions=None, v_dim: int = 512):
+    """Attention of one request over a per-query-token selection.
+
+    q_req [q_len, H, D]; kv_req [S, D]; topk [q_len, K] global positions chosen
+    for each query token (shared by its H heads; -1 = unused slot; the valid
+    entries of a token are distinct).  Query t sees the selected positions
+    p <= S - q_len + t.  ``positions`` (a rank's owned positions) restricts the
+    selection to that stripe.  Returns o [q_len, H, v_dim], natural-log lse
+    [q_len, H] (o = 0, lse = -inf for an empty selection)."""
+    q_len, H, D = q_req.shape
+    topk = np.asarray(topk, dtype=np.int64).reshape(q_len, -1)
+    own = None if positions is None else set(np.asarray(positions, dtype=np.int64).tolist())
+    o = np.zeros((q_len, H, v_dim))
+    lse = np.full((q_len, H), -np.inf)
+    for t in range(q_len):
+        qp = S - q_len + t
+        sel = [int(p) for p in topk[t] if 0 <= p <= qp and (own is None or int(p) in own)]
+        sel = np.asarray(sel, dtype=np.int64)
+        ot, lt = attention_rows(q_req[t], np.full(H, qp), kv_req[sel] if len(sel) else kv_req[:0], sel,
+                                scale, v_dim)
+        o[t], lse[t] = ot, lt
+    return o, lse

@@ -547,3 +547,56 @@ def test_position_bias_uses_global_positions_on_a_stripe():
         w = np.exp(-lam * (S - 1 - pos))
         assert np.allclose(o[0, 0], (w[:, None] * kv[pos, :V]).sum(axis=0) / w.sum(), rtol=1e-12, atol=1e-14)
         assert abs(lse[0, 0] - math.log(w.sum())) < 1e-12
+
+
+# ---- sparse attention over a global top-k selection ---------------------------
+
+def _random_topk(rng, S, q_len, K):
+    out = np.full((q_len, K), -1, dtype=np.int64)
+    for t in range(q_len):
+        qp = S - q_len + t
+        n = min(K, qp + 1)
+        out[t, :n] = rng.choice(qp + 1, size=n, replace=False)
+    return out
+
+
+def test_sparse_selecting_everything_is_full_attention():
+    rng = np.random.default_rng(31)
+    S, H, q_len = 30, 2, 3
+    q, kv = rand_case(rng, S, H, q_len)
+    topk = np.stack([np.concatenate([rng.permutation(S - q_len + t + 1), np.full(q_len - 1 - t, -1)])
+                     for t in range(q_len)])
+    o, lse = A.sparse_attention(q, kv, S, topk, SCALE)
+    of, lf = A.full_attention(q, kv, S, SCALE)
+    assert np.allclose(o, of, rtol=1e-12, atol=1e-14) and np.allclose(lse, lf, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_against_brute_force_and_single_selection():
+    rng = np.random.default_rng(32)
+    S, H, q_len, K = 17, 2, 2, 5
+    q, kv = rand_case(rng, S, H, q_len, kv_std=1.0)
+    topk = _random_topk(rng, S, q_len, K)
+    topk[1, 0] = S + 3                                          # a position past the query: never seen
+    o, lse = A.sparse_attention(q, kv, S, topk, SCALE)
+    for t in range(q_len):
+        sel = [int(p) for p in topk[t] if 0 <= p <= S - q_len + t]
+        for h in range(H):
+            bo, bl = brute_attention(q[t, h], [kv[p] for p in sel], sel, S - q_len + t, SCALE)
+            _close(o[t, h], lse[t, h], bo, bl)
+    one = np.array([[4], [-1]])
+    o1, l1 = A.sparse_attention(q, kv, S, one, SCALE)
+    assert np.allclose(o1[0], kv[4, :V][None], rtol=0, atol=1e-15) and np.isneginf(l1[1]).all()
+
+
+@pytest.mark.parametrize("N,I", [(2, 1), (4, 1), (8, 1), (3, 4)])
+def test_sparse_stripes_merge_to_the_global_selection(N, I):
+    # the page's condition: select globally, each rank attends to the selected
+    # tokens it owns, the LSE merge gives the unsharded sparse result
+    rng = np.random.default_rng(33 + N)
+    S, H, q_len, K = 64, 2, 4, 12
+    q, kv = rand_case(rng, S, H, q_len)
+    topk = _random_topk(rng, S, q_len, K)
+    o_full, l_full = A.sparse_attention(q, kv, S, topk, SCALE)
+    parts = [A.sparse_attention(q, kv, S, topk, SCALE, positions=pos) for pos in L.stripe_positions(S, N, I)]
+    o, lse = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    assert np.allclose(o, o_full, rtol=1e-12, atol=1e-14) and np.allclose(lse, l_full, rtol=1e-12, atol=1e-12)
