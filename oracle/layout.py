@@ -202,3 +202,24 @@ def relayout(dst_pool: np.ndarray, src_pool: np.ndarray, src_slots: np.ndarray,
     ok = (np.asarray(src_slots) >= 0) & (np.asarray(dst_slots) >= 0)
     out[np.asarray(dst_slots)[ok]] = src_pool[np.asarray(src_slots)[ok]]
     return out
+
+
+def sparse_plan(topk: np.ndarray, S: int, N: int, I: int, rank: int):
+    """One rank's share of a global per-token selection of one request.
+
+    topk [q_len, K] global positions (-1 = unused slot).  Page "DCP",
+    conditions for merging: with a global top-k each rank attends only to the
+    selected tokens it owns.  Walks the slots in (token, slot) order and keeps
+    a position p of token t when 0 <= p <= S - q_len + t and the rank owns p.
+    Returns (local rows, selecting-token bits 1 << t) of the kept entries."""
+    topk = np.asarray(topk, dtype=np.int64)
+    q_len = topk.shape[0]
+    owner, row = owner_and_row_table(max(S, 1), N, I)
+    rows, bits = [], []
+    for t in range(q_len):
+        for p in topk[t]:
+            p = int(p)
+            if 0 <= p <= S - q_len + t and owner[p] == rank:
+                rows.append(int(row[p]))
+                bits.append(1 << t)
+    return np.asarray(rows, dtype=np.int64), np.asarray(bits, dtype=np.int64)

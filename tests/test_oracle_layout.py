@@ -282,3 +282,27 @@ def test_relayout_then_decode_pool_equals_the_owner_filtered_write():
             a = L.relayout(a, src_pool, src, dst)
         b = L.kv_write(empty, rows, np.arange(S), np.zeros(S, dtype=np.int64), N, I, P, r, dst_row[None, :])
         assert np.array_equal(a, b, equal_nan=True)
+
+
+# ---- a rank's share of a global sparse selection -----------------------------
+
+@pytest.mark.parametrize("N,I", [(8, 1), (4, 2), (3, 64)])
+def test_sparse_plan_keeps_exactly_the_owned_visible_selections(N, I):
+    rng = np.random.default_rng(N * 7 + I)
+    S, q_len, K = 500, 3, 40
+    topk = np.full((q_len, K), -1, dtype=np.int64)
+    for t in range(q_len):
+        topk[t, :K - 3] = rng.choice(S + 20, size=K - 3, replace=False)     # some past the token's position
+    kept = 0
+    for r in range(N):
+        rows, bits = L.sparse_plan(topk, S, N, I, r)
+        pos = L.stripe_positions(S, N, I)[r]
+        want_rows, want_bits = [], []
+        for t in range(q_len):
+            for p in topk[t]:
+                if 0 <= p <= S - q_len + t and block_rr(int(p), N, I)[0] == r:
+                    want_rows.append(int(np.searchsorted(pos, p)))            # its index in the rank's list
+                    want_bits.append(1 << t)
+        assert rows.tolist() == want_rows and bits.tolist() == want_bits
+        kept += len(rows)
+    assert kept == sum(int(((topk[t] >= 0) & (topk[t] <= S - q_len + t)).sum()) for t in range(q_len))
