@@ -202,7 +202,12 @@ int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim,
  * bias_slopes [n_heads] fp32 device, nullable: linear position bias (ALiBi
  *          style) -- the logit of position p for a query at t of head h gains
  *          bias_slopes[h] * (p - t), natural-log units, after the softcap.
- *          Positions are global, so every rank passes the same slopes. */
+ *          Positions are global, so every rank passes the same slopes.
+ * sparse_rows, sparse_bits, sparse_count, sparse_stride  nullable (all or
+ *          none): a sparse selection from dcp_sparse_plan for this rank.  The
+ *          stripe then attends, for each query token t, only to the entries
+ *          whose bit t is set (the selected positions it owns), instead of
+ *          its whole stripe.  With window > 0 or bias_slopes: DCP_EUNSUPPORTED. */
 typedef struct dcp_attn_args {
   dcp_layout layout;
   int32_t rank;
@@ -230,6 +235,10 @@ typedef struct dcp_attn_args {
   const float* sinks;
   int32_t partials;
   const float* bias_slopes;
+  const int32_t* sparse_rows;
+  const uint32_t* sparse_bits;
+  const int32_t* sparse_count;
+  int32_t sparse_stride;
 } dcp_attn_args;
 
 /* Unmerged parts (page "DCP", "unification with online softmax": the split
@@ -251,6 +260,23 @@ int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);
 /* dcp_stripe_attn -- one rank's local attention over its stripe, returning
  * (o_r, lse_r) (page "DCP", idea two; page "MLA 的 DCP", section 3). */
 int dcp_stripe_attn(const dcp_attn_args* args, void* stream);
+
+/* dcp_sparse_plan -- one rank's share of a global sparse selection.
+ * Page "DCP", conditions for merging: sparse attention such as DSA's top-k
+ * stays mergeable when the top-k is chosen globally and each rank attends only
+ * to the selected tokens it owns.
+ * topk_pos [batch][q_len][topk] int32 device: global positions chosen for each
+ *          query token (shared by its heads); -1 marks an unused slot; the
+ *          valid positions of one token must be distinct.  A position past
+ *          the token's own (S - q_len + t) is ignored.
+ * seq_len  [batch] int32 device, global lengths.
+ * rows, bits [batch][stride] device out (stride >= q_len * topk): the kept
+ *          entries of request b in (t, slot) order -- the rank's local row of
+ *          the position and 1 << t; count [batch] int32 out: entries kept.
+ * q_len > 32: DCP_EUNSUPPORTED. */
+int dcp_sparse_plan(dcp_layout layout, int32_t rank, int32_t batch, int32_t q_len, int32_t topk,
+                    const int32_t* topk_pos, const int32_t* seq_len, int32_t* rows, uint32_t* bits,
+                    int32_t* count, int32_t stride, void* stream);
 
 /* Head-return exchange (page "DCP", "merge: All-to-All"; page "MLA 的 DCP",
  * section 4, step 6): every rank packs its (o_r, lse_r) by destination -- the

@@ -157,6 +157,59 @@ relayout_kernel(Layout L, int32_t rank, int32_t chunks, const uint4* __restrict_
   }
 }
 
+// Sparse selection of one rank (page "DCP", conditions for merging: the
+// top-k is chosen globally and each rank attends to the selected tokens it
+// owns).  One workgroup per request walks its q_len * K selected positions in
+// order and keeps those that are valid (0 <= p <= the draft's position) and
+// owned by `rank`, with a workgroup prefix sum, so the list order is
+// deterministic: entry = (local row, bit of the draft that selected it).
+constexpr int kPlanThreads = 256;
+
+__global__ void __launch_bounds__(kPlanThreads)
+sparse_plan_kernel(Layout L, int32_t rank, int32_t q_len, int32_t K, const int32_t* __restrict__ topk,
+                   const int32_t* __restrict__ seq_len, int32_t* __restrict__ rows, uint32_t* __restrict__ bits,
+                   int32_t* __restrict__ count, int64_t stride) {
+  __shared__ int32_t wave_tot[kPlanThreads / 64];
+  const int64_t b = blockIdx.x;
+  const int32_t S = seq_len[b];
+  const int32_t n = q_len * K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* sel = topk + b * n;
+  int32_t carry = 0;
+  for (int32_t e0 = 0; e0 < n; e0 += kPlanThreads) {
+    const int32_t e = e0 + threadIdx.x;
+    bool keep = false;
+    int64_t row = 0;
+    uint32_t bit = 0;
+    if (e < n) {
+      const int32_t t = e / K;
+      const int64_t pos = sel[e];
+      if (pos >= 0 && pos <= (int64_t)S - q_len + t && owner_of(L, pos) == rank) {
+        keep = true;
+        row = row_of(L, pos);
+        bit = 1u << t;
+      }
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
+    const int32_t before_lane = __builtin_popcountll(mask & ((1ull << lane) - 1));
+    if (lane == 0) wave_tot[wave] = __builtin_popcountll(mask);
+    __syncthreads();
+    int32_t before_wave = 0, total = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      before_wave += w < wave ? wave_tot[w] : 0;
+      total += wave_tot[w];
+    }
+    if (keep) {
+      const int64_t at = b * stride + carry + before_wave + before_lane;
+      rows[at] = (int32_t)row;
+      bits[at] = bit;
+    }
+    carry += total;
+    __syncthreads();                                 // wave_tot is rewritten next round
+  }
+  if (threadIdx.x == 0) count[b] = carry;
+}
+
 }  // namespace
 }  // namespace dcp
 
@@ -226,5 +279,20 @@ extern "C" int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim, co
   hipLaunchKernelGGL(relayout_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, L, rank, row_dim / 8,
                      (const uint4*)src_pool, src_pages, (int64_t)src_page_size, src_block_table, src_bt_cols,
                      start, len, block_table, bt_cols, (int64_t)layout.page_size, (uint4*)pool, num_pages, status);
+  return launch_status();
+}
+
+extern "C" int dcp_sparse_plan(dcp_layout layout, int32_t rank, int32_t batch, int32_t q_len, int32_t topk,
+                               const int32_t* topk_pos, const int32_t* seq_len, int32_t* rows, uint32_t* bits,
+                               int32_t* count, int32_t stride, void* stream) {
+  if (!layout_ok(layout) || rank < 0 || rank >= layout.n_stripes) return DCP_EINVAL;
+  if (batch < 0 || q_len < 1 || topk < 1) return DCP_EINVAL;
+  if (q_len > 32) return DCP_EUNSUPPORTED;
+  if ((int64_t)q_len * topk > 0x7fffffff || stride < (int64_t)q_len * topk) return DCP_EINVAL;
+  if (batch == 0) return DCP_OK;
+  if (topk_pos == nullptr || seq_len == nullptr || rows == nullptr || bits == nullptr || count == nullptr)
+    return DCP_EINVAL;
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)batch), dim3(kPlanThreads), 0, (hipStream_t)stream,
+                     to_layout(layout), rank, q_len, topk, topk_pos, seq_len, rows, bits, count, (int64_t)stride);
   return launch_status();
 }

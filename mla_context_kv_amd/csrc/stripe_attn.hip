@@ -138,6 +138,10 @@ struct Params {
   float cap_in, cap_out;            // softcap: s -> cap_out * tanh(s * cap_in) (raw-score units)
   const float* sinks;               // [H] natural-log sink logits, nullable
   const float* slopes;              // [H] position-bias slopes (natural-log units), nullable
+  const int32_t* sp_rows;           // sparse selection: local rows [B][sp_stride], nullable
+  const uint32_t* sp_bits;          //   which query tokens selected each entry (bit t)
+  const int32_t* sp_count;          //   entries per request [B]
+  int32_t sp_stride;
   float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
   float* o;                         // final outputs (requests cut into one chunk)
@@ -192,6 +196,19 @@ __device__ __forceinline__ int32_t first_row(const Params& p, int32_t S) {
   return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, p.rank) : 0;
 }
 
+// What the chunks of request b cover: its local rows (the selected entries
+// with a sparse selection) and the tile of the first row any query sees.
+__device__ __forceinline__ int32_t req_rows(const Params& p, int32_t b) {
+  return p.sp_rows ? p.sp_count[b] : count_rows(p.seq_len[b], p.N, p.I, p.rank);
+}
+__device__ __forceinline__ int32_t req_first_tile(const Params& p, int32_t b) {
+  return p.sp_rows ? 0 : first_row(p, p.seq_len[b]) / 32;
+}
+__device__ __forceinline__ int32_t req_tiles(const Params& p, int32_t b) {
+  const int32_t rows = req_rows(p, b);
+  return rows > 0 ? cdiv(rows, 32) - req_first_tile(p, b) : 0;
+}
+
 // Unmerged parts: chunk c is part c % k of request c / k (k = partials); a
 // request of t tiles has parts of ceil(t / k) tiles, the last ones empty when
 // t < k (an empty part writes o = 0, lse = -inf: zero weight in the merge).
@@ -203,9 +220,8 @@ __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
   if (!w.live) return w;
   w.k = c - w.b * k;
   w.n = k;
-  const int32_t S = p.seq_len[w.b];
-  w.rows = count_rows(S, p.N, p.I, p.rank);
-  w.ft = first_row(p, S) / 32;
+  w.rows = req_rows(p, w.b);
+  w.ft = req_first_tile(p, w.b);
   const int32_t t = w.rows > 0 ? cdiv(w.rows, 32) - w.ft : 0;
   w.cs = t > 0 ? cdiv(t, k) : 0;
   return w;
@@ -216,18 +232,12 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
   // tiles of request b (from its first tile on); the first 256 requests'
   // are loaded once (all loads in flight together) and kept in registers
   constexpr int kCached = 4;
-  auto tiles_for = [&](int32_t S) -> int32_t {
-    const int32_t rows = count_rows(S, p.N, p.I, p.rank);
-    return rows > 0 ? cdiv(rows, 32) - first_row(p, S) / 32 : 0;
-  };
   int32_t tiles_c[kCached];
 #pragma unroll
   for (int j = 0; j < kCached; ++j) {
     const int32_t b = 64 * j + lane;
-    tiles_c[j] = b < p.B ? p.seq_len[b] : 0;
+    tiles_c[j] = b < p.B ? req_tiles(p, b) : 0;
   }
-#pragma unroll
-  for (int j = 0; j < kCached; ++j) tiles_c[j] = tiles_for(tiles_c[j]);
   auto tiles_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
     const int32_t b = b0 + lane;
     if (b0 < 64 * kCached) {
@@ -236,7 +246,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? tiles_c[j] : r;
       return r;
     }
-    return b < p.B ? tiles_for(p.seq_len[b]) : 0;
+    return b < p.B ? req_tiles(p, b) : 0;
   };
   int32_t C = 1;
   if (p.forced_splits == 0) {
@@ -294,9 +304,8 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       w.b = b0 + l;
       w.k = c - __builtin_amdgcn_readlane(excl, l);
       w.n = __builtin_amdgcn_readlane(nb, l);
-      const int32_t S = p.seq_len[w.b];
-      w.rows = count_rows(S, p.N, p.I, p.rank);
-      w.ft = first_row(p, S) / 32;
+      w.rows = req_rows(p, w.b);
+      w.ft = req_first_tile(p, w.b);
       const int32_t tl = __builtin_amdgcn_readlane(t, l);
       w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
       if (!write_table) break;
@@ -397,6 +406,12 @@ stripe_attn_kernel(Params p) {
 
   const int32_t S_b = p.seq_len[b];
   const int32_t max_vis = wi.rows;     // rows the last query sees
+  // sparse selection: the chunks run over entries of the request's list of
+  // selected local rows; with several drafts each entry carries the drafts
+  // that selected it
+  const bool sparse = p.sp_rows != nullptr;
+  const bool sparse_bits = sparse && p.q_len > 1;
+  const int64_t sp_base = sparse ? (int64_t)b * p.sp_stride : 0;
   const int32_t row_lo = (wi.ft + wi.k * wi.cs) * kTile;
   int32_t row_hi = row_lo + wi.cs * kTile;
   row_hi = row_hi < max_vis ? row_hi : max_vis;
@@ -407,7 +422,7 @@ stripe_attn_kernel(Params p) {
   const int R = row0 + wave * 32 + n;
   const bool valid = qk_wave && R < p.M;
   const int t = valid ? R / p.H : 0;
-  int32_t lim = count_rows(S_b - p.q_len + t + 1, p.N, p.I, p.rank);
+  int32_t lim = sparse ? row_hi : count_rows(S_b - p.q_len + t + 1, p.N, p.I, p.rank);
   if (!valid) lim = row_hi;
   lim = lim < row_hi ? lim : row_hi;
   // first visible row (sliding window): rows below it are masked
@@ -468,7 +483,7 @@ stripe_attn_kernel(Params p) {
   // (row s / 73, chunk s % 73) takes global chunk s - s / 73 of the tile; the
   // pad chunks fetch a neighbouring chunk of the same tile, never read from LDS.
   auto tile_is_fast = [&](int it) -> bool {
-    return kAligned && it < ntiles && row_hi - (row_lo + it * kTile) >= kTile;
+    return kAligned && !sparse && it < ntiles && row_hi - (row_lo + it * kTile) >= kTile;
   };
   auto fast_offset = [&](int k) -> uint32_t {
     const uint32_t s = (uint32_t)(load_slot0(k) + lane);
@@ -486,7 +501,7 @@ stripe_attn_kernel(Params p) {
     const int32_t J = row_lo + it * kTile;
     const int32_t rows_left = row_hi - J;          // >= 1 for a live tile
     const char* tb = nullptr;
-    if (kAligned) tb = tile_base_of(it);
+    if (kAligned && !sparse) tb = tile_base_of(it);
     const uint32_t lds_stage = lds0 + (it % kStages) * kStageBytes;
 #pragma unroll 1
     for (int k = 0; k < kMyLoads; ++k) {
@@ -497,12 +512,12 @@ stripe_attn_kernel(Params p) {
       if (tt >= rows_left) tt = 0;
       c = c < kChunks ? c : kChunks - 1;
       const char* src = zero;
-      if (kAligned) {
+      if (kAligned && !sparse) {
         if (tb) src = tb + tt * kRowBytes + c * 16;
       } else {
-        const int32_t j = J + tt;
+        const int32_t j = sparse ? p.sp_rows[sp_base + J + tt] : J + tt;
         const int32_t pi = j / p.P;
-        const int32_t pg = pi < p.bt_cols ? bt_row[pi] : -1;
+        const int32_t pg = j >= 0 && pi < p.bt_cols ? bt_row[pi] : -1;
         if (pg >= 0 && pg < p.num_pages) src = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes + c * 16;
         else flag_range(p.status);
       }
@@ -594,12 +609,21 @@ stripe_attn_kernel(Params p) {
   constexpr int kParts = 11;
   f32x16 sacc;
   int32_t vis = 0, vlo = 0;             // tile-relative visible rows [vlo, vis)
+  int32_t tj0 = 0;                      // the tile's first row (entry, with a sparse selection)
   float mx = 0.f, neg_m = 0.f, psum = 0.f;
   bf16x8 pk[2];
   int sbuf = 0;                       // buffer of the factors and flags the pieces publish
   auto softmax_part = [&](int part) {
     if (part == 0) {
-      if (__builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) != 0) {
+      if (sparse_bits) {
+        // several drafts: an entry is visible to the drafts that selected it
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = tok_of(i);
+          const bool sel = e < vis && ((p.sp_bits[sp_base + tj0 + (e < vis ? e : 0)] >> t) & 1u);
+          sacc[i] = sel ? sacc[i] : -INFINITY;
+        }
+      } else if (__builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) != 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = tok_of(i) < vis && tok_of(i) >= vlo ? sacc[i] : -INFINITY;
       }
@@ -642,7 +666,7 @@ stripe_attn_kernel(Params p) {
   // large weights, or a tile that crosses some row's visible limit -- the
   // exact pieces above recompute it.
   auto softmax_tile = [&](bool first) {
-    if (!first && __builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) == 0) {
+    if (!first && !sparse_bits && __builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) == 0) {
       const float nm = -m_run;
       float e[16];
 #pragma unroll
@@ -741,6 +765,7 @@ stripe_attn_kernel(Params p) {
         sacc = qk(smem);
         cap(sacc, row_lo);
         vis = lim - row_lo;
+        tj0 = row_lo;
         vlo = low - row_lo;
         sbuf = 0;
         softmax_tile(true);
@@ -752,6 +777,7 @@ stripe_attn_kernel(Params p) {
             sacc = qk(smem + ((it + 1) % kStages) * kStageBytes);
             cap(sacc, row_lo + (it + 1) * kTile);
             vis = lim - (row_lo + (it + 1) * kTile);
+            tj0 = row_lo + (it + 1) * kTile;
             vlo = low - (row_lo + (it + 1) * kTile);
             sbuf = (it + 1) & 1;
             softmax_tile(false);
@@ -891,8 +917,13 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   if (a->partials != 0 && (a->partials != 1 || a->num_splits < 1)) return DCP_EINVAL;
   if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
   if ((a->softcap > 0.f || a->bias_slopes != nullptr) && !(a->scale > 0.f)) return DCP_EINVAL;
+  if (a->sparse_rows != nullptr) {
+    if (a->sparse_bits == nullptr || a->sparse_count == nullptr || a->sparse_stride < 1) return DCP_EINVAL;
+    if (a->window > 0 || a->bias_slopes != nullptr) return DCP_EUNSUPPORTED;   // positions are not tracked
+    if (a->q_len > 32) return DCP_EUNSUPPORTED;                                // one selection bit per draft
+  }
   const int64_t M = (int64_t)a->q_len * a->n_heads;
-  const int64_t max_rows = (int64_t)a->bt_cols * a->layout.page_size;
+  const int64_t max_rows = a->sparse_rows ? (int64_t)a->sparse_stride : (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
   if ((int64_t)a->layout.n_stripes * a->layout.interleave > 0x7fffffff) return DCP_EUNSUPPORTED;
   // query rows per workgroup: up to 3 blocks of 32; above 96 rows the rows
@@ -1029,6 +1060,10 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.cap_out = a->softcap > 0.f ? a->softcap / a->scale : 0.f;
   prm.sinks = a->sinks;
   prm.slopes = a->bias_slopes;
+  prm.sp_rows = a->sparse_rows;
+  prm.sp_bits = a->sparse_bits;
+  prm.sp_count = a->sparse_count;
+  prm.sp_stride = a->sparse_stride;
   prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
   prm.o = a->o;

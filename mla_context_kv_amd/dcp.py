@@ -69,6 +69,10 @@ class dcp_attn_args(ctypes.Structure):
         ("sinks", ctypes.c_void_p),
         ("partials", ctypes.c_int32),
         ("bias_slopes", ctypes.c_void_p),
+        ("sparse_rows", ctypes.c_void_p),
+        ("sparse_bits", ctypes.c_void_p),
+        ("sparse_count", ctypes.c_void_p),
+        ("sparse_stride", ctypes.c_int32),
     ]
 
 
@@ -87,6 +91,7 @@ _SIGNATURES = {
     "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
     "dcp_pack_heads": (ctypes.c_int, [_I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "dcp_sparse_plan": (ctypes.c_int, [dcp_layout, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "dcp_merge_heads": (ctypes.c_int, [_I32, _I64, _I32, _VP, _I32, _VP, _VP, _VP]),
     "dcp_relayout": (ctypes.c_int, [dcp_layout, _I32, _I32, _VP, _I64, _I32, _VP, _I32, _VP, _VP, _I32, _I64,
                                     _VP, _I32, _VP, _I64, _VP, _VP]),
@@ -255,11 +260,12 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
                     sinks: Optional[torch.Tensor] = None, partials: bool = False,
-                    bias_slopes: Optional[torch.Tensor] = None):
+                    bias_slopes: Optional[torch.Tensor] = None, sparse=None):
     """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
 
     window / softcap / sinks / bias_slopes select the mergeable variants (sinks: fp32 [H], on one
-    rank only; bias_slopes: fp32 [H], on every rank).
+    rank only; bias_slopes: fp32 [H], on every rank).  sparse = (rows, bits, count) from
+    dcp_sparse_plan restricts the stripe to the rank's selected tokens.
     partials=True (with num_splits = k >= 1) returns the k unmerged parts instead:
     o [k,B,q_len,H,512], lse [k,B,q_len,H]."""
     dev = q.device
@@ -301,6 +307,14 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.status = _ptr(status, torch.int32, "status", dev)
     a.sinks = _ptr(sinks, torch.float32, "sinks", dev)
     a.bias_slopes = _ptr(bias_slopes, torch.float32, "bias_slopes", dev)
+    if sparse is not None:
+        rows, bits, count = sparse
+        if rows.shape[0] != B or bits.shape != rows.shape or count.numel() != B:
+            raise ValueError("sparse rows / bits must be [B, stride] and count [B]")
+        a.sparse_rows = _ptr(rows, torch.int32, "sparse rows", dev)
+        a.sparse_bits = _ptr(bits, torch.int32, "sparse bits", dev)
+        a.sparse_count = _ptr(count, torch.int32, "sparse count", dev)
+        a.sparse_stride = int(rows.shape[1])
     _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
     return o, lse
 
@@ -362,3 +376,25 @@ def dcp_merge_heads(recv: torch.Tensor, lse_base: int = 0, o: Optional[torch.Ten
                                _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev), _stream(dev))
     _check(rc, "dcp_merge_heads")
     return o, lse
+
+
+def dcp_sparse_plan(lay: dcp_layout, rank: int, topk_pos: torch.Tensor, seq_len: torch.Tensor,
+                    out=None):
+    """Rank `rank`'s share of a global selection topk_pos int32 [B, q_len, K] (-1 = unused):
+    returns (rows int32 [B, q_len*K], bits int32 [B, q_len*K], count int32 [B])."""
+    dev = topk_pos.device
+    if topk_pos.dim() != 3:
+        raise ValueError("topk_pos must be [B, q_len, K]")
+    B, q_len, K = (int(x) for x in topk_pos.shape)
+    if out is None:
+        rows = torch.empty((B, q_len * K), dtype=torch.int32, device=dev)
+        bits = torch.empty((B, q_len * K), dtype=torch.int32, device=dev)
+        count = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        rows, bits, count = out
+    rc = lib().dcp_sparse_plan(lay, int(rank), B, q_len, K, _ptr(topk_pos, torch.int32, "topk_pos", dev),
+                               _ptr(seq_len, torch.int32, "seq_len", dev), _ptr(rows, torch.int32, "rows", dev),
+                               _ptr(bits, torch.int32, "bits", dev), _ptr(count, torch.int32, "count", dev),
+                               int(rows.shape[1]), _stream(dev))
+    _check(rc, "dcp_sparse_plan")
+    return rows, bits, count

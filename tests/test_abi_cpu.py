@@ -16,7 +16,7 @@ def test_library_exports_every_declared_function():
     names = dcp.header_functions()
     assert {"dcp_slot_map", "dcp_local_count", "dcp_kv_write", "dcp_stripe_attn",
             "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror", "dcp_relayout", "dcp_pack_heads",
-            "dcp_merge_heads"} <= set(names)
+            "dcp_merge_heads", "dcp_sparse_plan"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -199,3 +199,24 @@ def test_pack_and_merge_heads_argument_errors():
     assert L.dcp_merge_heads(4, 4, 512, FAKE, 2, FAKE, FAKE, None) == dcp.DCP_EINVAL
     assert L.dcp_merge_heads(4, 4, 6, FAKE, 0, FAKE, FAKE, None) == dcp.DCP_EINVAL
     assert L.dcp_merge_heads(4, 4, 512, None, 0, FAKE, FAKE, None) == dcp.DCP_EINVAL
+
+
+def test_sparse_plan_and_sparse_attention_argument_errors():
+    lay = dcp.layout(8, 1, 64)
+    P = dcp.dcp_layout
+    call = lambda **kw: L.dcp_sparse_plan(kw.get("lay", lay), kw.get("rank", 0), kw.get("B", 2), kw.get("q_len", 1),
+                                          kw.get("K", 4), kw.get("topk", FAKE), kw.get("seq", FAKE), kw.get("rows", FAKE),
+                                          kw.get("bits", FAKE), kw.get("count", FAKE), kw.get("stride", 4), None)
+    for kw in (dict(rank=8), dict(B=-1), dict(q_len=0), dict(K=0), dict(stride=3), dict(topk=None), dict(seq=None),
+               dict(rows=None), dict(bits=None), dict(count=None), dict(lay=dcp.layout(8, 3, 64))):
+        assert call(**kw) == dcp.DCP_EINVAL, kw
+    assert call(q_len=33, stride=33 * 4) == dcp.DCP_EUNSUPPORTED
+    assert call(B=0, topk=None) == dcp.DCP_OK
+    # attention: all three sparse pointers or none; no window or position bias with a selection
+    a = _args(sparse_rows=0x1000, sparse_count=0x1000, sparse_stride=4)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+    a = _args(sparse_rows=0x1000, sparse_bits=0x1000, sparse_count=0x1000, sparse_stride=0)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+    for kw in (dict(window=16), dict(bias_slopes=0x1000), dict(q_len=33)):
+        a = _args(sparse_rows=0x1000, sparse_bits=0x1000, sparse_count=0x1000, sparse_stride=4, **kw)
+        assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EUNSUPPORTED, kw

@@ -226,3 +226,79 @@ def test_unmerged_parts_merge_to_full(B, H_, q_len, N, I, P, lens, base, k, wind
                                  f"part {c}, request {b}, stripe {r}")
                 H.assert_lse_close(lse_parts[r, c, b].cpu().numpy().reshape(-1), OA.to_base(pl, base),
                                    f"part lse {c}, request {b}, stripe {r}")
+
+
+# ---- sparse attention over a global top-k selection ---------------------------
+
+SPARSE = [
+    # B, H, q_len, N, I, P, lens, base, K, splits, extra
+    (3, 96, 1, 8, 1, 64, [3000, 9, 700], "2", 256, 0, None),        # DSA-style decode, an almost empty request
+    (2, 96, 4, 8, 1, 64, [2000, 300], "e", 64, 0, None),            # drafts with their own selections
+    (2, 64, 2, 4, 64, 64, [5000, 129], "2", 500, 3, "sink+cap"),    # chunks, interleave 64, sink and softcap
+]
+
+
+@pytest.mark.parametrize("B,H_,q_len,N,I,P,lens,base,K,splits,extra", SPARSE)
+def test_sparse_selection_every_element(B, H_, q_len, N, I, P, lens, base, K, splits, extra):
+    from oracle import layout as OL
+    w, lens = custom(B, H_, q_len, N, P, lens, base)
+    print(f"sparse B={B} H={H_} q_len={q_len} N={N} I={I} lens={lens.tolist()} K={K} splits={splits} {extra}",
+          flush=True)
+    s = H.make_setup(w, I, lens=lens)
+    dev = s.q.device
+    rng = np.random.default_rng(K + q_len)
+    topk = np.full((B, q_len, K), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(q_len):
+            vis = int(lens[b]) - q_len + t + 1
+            n = min(K - 2, vis + 3)
+            topk[b, t, :n] = rng.choice(vis + 3, size=n, replace=False)  # a few past the token: ignored
+    topk_d = torch.from_numpy(topk).to(dev)
+    softcap = 1.5 if extra else 0.0
+    sinks = np.random.default_rng(2).normal(0.0, 1.0, H_) if extra else None
+    sk = None if sinks is None else torch.tensor(sinks, dtype=torch.float32, device=dev)
+    o_parts = torch.empty((N, B, q_len, H_, workloads.V_DIM), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((N, B, q_len, H_), dtype=torch.float32, device=dev)
+    for r in range(N):
+        plan = dcp.dcp_sparse_plan(s.lay, r, topk_d, s.sp.seq_len)
+        torch.cuda.synchronize()
+        # the plan, bit-exact against the oracle's
+        for b in range(B):
+            want_rows, want_bits = OL.sparse_plan(topk[b], int(lens[b]), N, I, r)
+            n = int(plan[2][b].item())
+            assert n == len(want_rows)
+            assert plan[0][b, :n].cpu().numpy().tolist() == want_rows.tolist()
+            assert plan[1][b, :n].cpu().numpy().tolist() == want_bits.tolist()
+        dcp.dcp_stripe_attn(s.lay, r, s.q, s.sp.pools[r], s.sp.tables[r], s.sp.seq_len, workloads.SCALE,
+                            s.base_flag, num_splits=splits, o=o_parts[r], lse=lse_parts[r], status=s.status,
+                            softcap=softcap, sinks=sk if r == 0 else None, sparse=plan)
+    o, lse = dcp.dcp_lse_merge(o_parts, lse_parts, s.base_flag)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    sinks64 = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
+    for b in range(B):
+        q64, kv64, S = H.request_inputs(s, b)
+        lists = OL.stripe_positions(S, N, I)
+        for r in range(N):
+            ro, rl = _sparse_oracle(q64, kv64, S, topk[b], lists[r], softcap, sinks64 if r == 0 else None)
+            H.assert_o_close(o_parts[r, b].cpu().numpy(), ro, f"sparse o_r, request {b}, stripe {r}")
+            H.assert_lse_close(lse_parts[r, b].cpu().numpy(), OA.to_base(rl, base), f"sparse lse_r {b} {r}")
+        fo, fl = _sparse_oracle(q64, kv64, S, topk[b], None, softcap, sinks64)
+        H.assert_o_close(o[b].cpu().numpy(), fo, f"sparse merged o, request {b}")
+        H.assert_lse_close(lse[b].cpu().numpy(), OA.to_base(fl, base), f"sparse merged lse, request {b}")
+
+
+def _sparse_oracle(q64, kv64, S, topk, positions, softcap, sinks):
+    """The oracle's sparse attention, with the softcap and sink variants applied per token."""
+    q_len, H_, _ = q64.shape
+    if softcap == 0.0 and sinks is None:
+        return OA.sparse_attention(q64, kv64, S, topk, workloads.SCALE, positions=positions)
+    own = None if positions is None else set(np.asarray(positions).tolist())
+    o = np.zeros((q_len, H_, workloads.V_DIM))
+    lse = np.full((q_len, H_), -np.inf)
+    for t in range(q_len):
+        qp = S - q_len + t
+        sel = np.asarray([int(p) for p in topk[t] if 0 <= p <= qp and (own is None or int(p) in own)], dtype=np.int64)
+        o[t], lse[t] = OA.attention_rows(q64[t], np.full(H_, qp), kv64[sel] if len(sel) else kv64[:0], sel,
+                                         workloads.SCALE, softcap=softcap, sink=sinks)
+    return o, lse
