@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="k > 0: sparse attention over a global top-k selection per query token (plan + attention "
+                         "on every rank)")
     ap.add_argument("--parts", type=int, default=0,
                     help="k > 0: every rank writes k unmerged parts per request and one merge folds all N*k")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
@@ -159,12 +162,30 @@ def main():
         ws_bytes = max(ws_bytes, need.value)
         attn_args.append(a)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    plans = None
+    if args.topk > 0:
+        # a global selection: k distinct visible positions per query token
+        KT = args.topk
+        topk = torch.full((w.B, w.q_len, KT), -1, dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev).manual_seed(17)
+        for b in range(w.B):
+            for t in range(w.q_len):
+                vis = int(lens[b]) - w.q_len + t + 1
+                n = min(KT, vis)
+                topk[b, t, :n] = torch.randperm(vis, generator=g, device=dev)[:n].to(torch.int32)
+        plans = []
+        for r in range(N):
+            rows_t = torch.empty((w.B, w.q_len * KT), dtype=torch.int32, device=dev)
+            plans.append((rows_t, torch.empty_like(rows_t), torch.empty(w.B, dtype=torch.int32, device=dev)))
     sinks = None
     if args.sinks:
         g = torch.Generator().manual_seed(7)
         sinks = torch.randn(w.H, generator=g).to(dev)
     for r, a in enumerate(attn_args):
         a.window, a.softcap = args.window, args.softcap
+        if plans is not None:
+            a.sparse_rows, a.sparse_bits, a.sparse_count = (x.data_ptr() for x in plans[r])
+            a.sparse_stride = int(plans[r][0].shape[1])
         a.sinks = sinks.data_ptr() if sinks is not None and r == N - 1 else None
         a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
@@ -179,6 +200,12 @@ def main():
         for r in range(N):
             if events is not None:
                 events[r].record(stream)
+            if plans is not None:
+                rc = L.dcp_sparse_plan(lay, r, w.B, w.q_len, args.topk, topk.data_ptr(), sp.seq_len.data_ptr(),
+                                       plans[r][0].data_ptr(), plans[r][1].data_ptr(), plans[r][2].data_ptr(),
+                                       int(plans[r][0].shape[1]), sh)
+                if rc != 0:
+                    raise RuntimeError(f"dcp_sparse_plan: {dcp.strerror(rc)}")
             rc = L.dcp_stripe_attn(refs[r], sh)
             if rc != 0:
                 raise RuntimeError(f"dcp_stripe_attn: {dcp.strerror(rc)}")
@@ -222,7 +249,10 @@ def main():
 
     # ---- algorithmic work
     local = counts.astype(np.int64)                                  # rows per (request, rank)
-    if args.window > 0:
+    if args.topk > 0:
+        # rows the selection reaches on each rank (the plan's counts)
+        local = np.stack([plans[r][2].cpu().numpy() for r in range(N)], axis=1).astype(np.int64)
+    elif args.window > 0:
         # rows some query of the request sees: the last S - first window start
         first = np.clip(lens - w.q_len + 1 - args.window, 0, None)
         local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
@@ -234,6 +264,8 @@ def main():
         seen = np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
         if args.window > 0:
             seen = np.minimum(seen, args.window)
+        if args.topk > 0:
+            seen = np.minimum(seen, args.topk)
         vis += seen
     flops = float((vis * w.H).sum()) * FLOP_PER_ROW_QUERY
     kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -244,9 +276,9 @@ def main():
     achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1)
+    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk)
     cpu = None
-    if sample is not None and not (args.window or args.softcap or args.sinks or args.parts):
+    if sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk):
         from oracle import attention as OA
         from oracle import layout as OL
         try:
@@ -292,7 +324,8 @@ def main():
                    "launches_per_step": N + 1,
                    **({"variant": {"window": args.window, "softcap": args.softcap, "sinks": bool(args.sinks)}}
                       if (args.window or args.softcap or args.sinks) else {}),
-                   **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {})},
+                   **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {}),
+                   **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),

@@ -491,17 +491,34 @@ stripe_attn_kernel(Params p) {
     g = g < (uint32_t)(kTile * kChunks - 1) ? g : (uint32_t)(kTile * kChunks - 1);
     return g * 16u;
   };
-  // General loads (live tiles only): partial tiles and pages smaller than a
-  // tile.  A slot that holds no token of the split (rows past the split end)
-  // loads a chunk of the tile's first row instead, and the pad chunk loads
-  // chunk 71 of its row: finite data that the softmax masks to weight zero
-  // (or that is never read), so no stale, unowned or NaN row reaches the MFMAs.
+  // General loads (live tiles only): partial tiles, pages smaller than a
+  // tile and sparse selections.  Lane l < 32 first finds the address of the
+  // tile's row l (one round of dependent loads for the whole tile); each slot
+  // then takes its row's address from that lane.  A slot that holds no token
+  // of the split (rows past the split end) loads a chunk of the tile's first
+  // row instead, and the pad chunk loads chunk 71 of its row: finite data
+  // that the softmax masks to weight zero (or that is never read), so no
+  // stale, unowned or NaN row reaches the MFMAs.  A row whose page is out of
+  // range reads the zero row (and flags DCP_ERANGE).
   auto load_tile_general = [&](int it) {
     if (!loads_here) return;
     const int32_t J = row_lo + it * kTile;
     const int32_t rows_left = row_hi - J;          // >= 1 for a live tile
-    const char* tb = nullptr;
-    if (kAligned && !sparse) tb = tile_base_of(it);
+    const int l = lane & 31;
+    const int tl = l < rows_left ? l : 0;
+    const char* rowp = zero;
+    if (kAligned && !sparse) {
+      const char* tb = tile_base_of(it);
+      if (tb) rowp = tb + tl * kRowBytes;
+    } else {
+      const int32_t j = sparse ? p.sp_rows[sp_base + J + tl] : J + tl;
+      const int32_t pi = j / p.P;
+      const int32_t pg = j >= 0 && pi < p.bt_cols ? bt_row[pi] : -1;
+      if (pg >= 0 && pg < p.num_pages) rowp = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes;
+      else flag_range(p.status);
+    }
+    const uint64_t ra = reinterpret_cast<uint64_t>(rowp);
+    const uint32_t ra_lo = (uint32_t)ra, ra_hi = (uint32_t)(ra >> 32);
     const uint32_t lds_stage = lds0 + (it % kStages) * kStageBytes;
 #pragma unroll 1
     for (int k = 0; k < kMyLoads; ++k) {
@@ -511,17 +528,8 @@ stripe_attn_kernel(Params p) {
       int c = s - tt * kRowSlots;
       if (tt >= rows_left) tt = 0;
       c = c < kChunks ? c : kChunks - 1;
-      const char* src = zero;
-      if (kAligned && !sparse) {
-        if (tb) src = tb + tt * kRowBytes + c * 16;
-      } else {
-        const int32_t j = sparse ? p.sp_rows[sp_base + J + tt] : J + tt;
-        const int32_t pi = j / p.P;
-        const int32_t pg = j >= 0 && pi < p.bt_cols ? bt_row[pi] : -1;
-        if (pg >= 0 && pg < p.num_pages) src = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes + c * 16;
-        else flag_range(p.status);
-      }
-      dma16(src, lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane(s0 * 16));
+      const uint64_t a = ((uint64_t)(uint32_t)__shfl((int)ra_hi, tt, 64) << 32) | (uint32_t)__shfl((int)ra_lo, tt, 64);
+      dma16(reinterpret_cast<const char*>(a) + c * 16, lds_stage + (uint32_t)__builtin_amdgcn_readfirstlane(s0 * 16));
     }
   };
 
