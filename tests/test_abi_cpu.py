@@ -220,3 +220,11 @@ def test_sparse_plan_and_sparse_attention_argument_errors():
     for kw in (dict(window=16), dict(bias_slopes=0x1000), dict(q_len=33)):
         a = _args(sparse_rows=0x1000, sparse_bits=0x1000, sparse_count=0x1000, sparse_stride=4, **kw)
         assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EUNSUPPORTED, kw
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback: with libdcp.so absent every call raises instead of computing elsewhere."""
+    monkeypatch.setattr(dcp, "LIB_PATH", str(tmp_path / "libdcp.so"))
+    monkeypatch.setattr(dcp, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        dcp.lib()
