@@ -591,10 +591,11 @@ stripe_attn_kernel(Params p) {
   };
 
   // S^T = K Q^T of the tile in stage `st` over the 576 latent dims (K
-  // fragments read kQkAhead steps ahead).
+  // fragments read kQkAhead steps ahead).  One accumulator: the matrix core
+  // chains dependent MFMAs on their accumulator, and a second chain (tried)
+  // only costs 16 registers and a 16-add reduction per tile.
   auto qk = [&](const char* st) -> f32x16 {
-    // two accumulators (even and odd k-steps): no MFMA waits for the previous one
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    f32x16 acc = f32x16{};
     const char* kb = st + kq_off;
     bf16x8 kf[kKSteps];
 #pragma unroll
@@ -602,10 +603,10 @@ stripe_attn_kernel(Params p) {
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       if (ks + kQkAhead < kKSteps) kf[ks + kQkAhead] = *reinterpret_cast<const bf16x8*>(kb + 32 * (ks + kQkAhead));
-      acc[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc[ks & 1], 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return acc[0] + acc[1];
+    return acc;
   };
 
   // Online softmax of one tile in base 2 (QK waves), in kParts pieces.
