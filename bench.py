@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
+    ap.add_argument("--multi", action="store_true",
+                    help="all N stripes in one dcp_stripe_attn_multi launch (then the merge)")
     ap.add_argument("--topk", type=int, default=0,
                     help="k > 0: sparse attention over a global top-k selection per query token (plan + attention "
                          "on every rank)")
@@ -161,6 +163,12 @@ def main():
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
         attn_args.append(a)
+    multi_arr = None
+    if args.multi:
+        multi_arr = (dcp.dcp_attn_args * N)(*attn_args)
+        need = ctypes.c_size_t(0)
+        assert L.dcp_stripe_attn_multi_workspace(multi_arr, N, ctypes.byref(need)) == 0
+        ws_bytes = max(ws_bytes, need.value)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     plans = None
     if args.topk > 0:
@@ -192,11 +200,29 @@ def main():
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
         a.o, a.lse, a.status = o_parts[r * K].data_ptr(), lse_parts[r * K].data_ptr(), status.data_ptr()
     refs = [ctypes.byref(a) for a in attn_args]
+    if multi_arr is not None:
+        for r, a in enumerate(attn_args):
+            multi_arr[r] = a
     sh = stream.cuda_stream
     rows = w.B * M
     merge_call = (N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
 
     def step(events=None):
+        if multi_arr is not None:
+            if events is not None:
+                events[0].record(stream)
+            rc = L.dcp_stripe_attn_multi(multi_arr, N, sh)
+            if rc != 0:
+                raise RuntimeError(f"dcp_stripe_attn_multi: {dcp.strerror(rc)}")
+            if events is not None:
+                for r in range(1, N + 1):
+                    events[r].record(stream)
+            rc = L.dcp_lse_merge(*merge_call)
+            if rc != 0:
+                raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
+            if events is not None:
+                events[N + 1].record(stream)
+            return
         for r in range(N):
             if events is not None:
                 events[r].record(stream)
@@ -273,10 +299,16 @@ def main():
     # stripe's latent rows, the queries, and its (o_r, lse_r))
     stripe_bytes = local.sum(axis=0) * ROW_BYTES + q_bytes + part_bytes          # per rank
     launch_ms = per_stripe_ms.mean(axis=0)                                        # per rank
-    achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
+    if args.multi:
+        # one launch for all stripes: its bytes over its duration
+        launch_ms = launch_ms[:1]
+        achieved = float(stripe_bytes.sum() / (launch_ms[0] * 1e-3)) / 1e9
+    else:
+        achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk)
+    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
+                     or args.multi)
     cpu = None
     if sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk):
         from oracle import attention as OA
@@ -325,16 +357,18 @@ def main():
                    **({"variant": {"window": args.window, "softcap": args.softcap, "sinks": bool(args.sinks)}}
                       if (args.window or args.softcap or args.sinks) else {}),
                    **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {}),
-                   **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {})},
+                   **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {}),
+                   **({"one_launch_for_all_stripes": True} if args.multi else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if secondary else measured_traffic(w.name),
-                     "kernel": (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
-                                if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine"),
-                     "bytes_per_launch": int(stripe_bytes.mean())},
+                     "kernel": ("one dcp_stripe_attn_multi launch: all stripes" if args.multi else
+                                (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
+                                 if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")),
+                     "bytes_per_launch": int(stripe_bytes.sum() if args.multi else stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

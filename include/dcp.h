@@ -298,6 +298,21 @@ int dcp_pack_heads(int32_t n_stripes, int64_t rows, int32_t n_heads, int32_t v_d
 int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* recv,
                     int32_t lse_base, float* o, float* lse, void* stream);
 
+/* dcp_stripe_attn_multi -- the stripe attentions of n ranks in one launch.
+ * Page "DCP", idea two: every rank's local attention is independent of the
+ * others', so the n calls args[0..n) can run as one launch that balances the
+ * chunks of all ranks' requests over the GPU (on one GPU: the N-fold
+ * parallelism of all stripes at once).  Each args[i] is a complete
+ * dcp_stripe_attn argument block for its rank (own pool, block_table, o, lse,
+ * sinks, sparse selection); everything else -- layout, shapes, q, seq_len,
+ * scale, base, num_splits, window, softcap, bias_slopes, partials and whether
+ * a selection is given -- must be the same in all n (else DCP_EINVAL).  The
+ * workspace of args[0] serves the launch; size it with
+ * dcp_stripe_attn_multi_workspace.  Results equal n dcp_stripe_attn calls.
+ * 1 <= n <= 16 (n > 16: DCP_EUNSUPPORTED). */
+int dcp_stripe_attn_multi_workspace(const dcp_attn_args* args, int32_t n, size_t* bytes);
+int dcp_stripe_attn_multi(const dcp_attn_args* args, int32_t n, void* stream);
+
 /* dcp_lse_merge -- exact merge of N stripes' partial results.
  * Page "DCP", "merge operator and numerical stability"; SGLang DCP docs,
  * "MLA decode dataflow": m = max_r lse_r, w_r = base^(lse_r - m),

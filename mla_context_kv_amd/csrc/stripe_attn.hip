@@ -37,7 +37,8 @@
 //    values are read from LDS once per workgroup, not once per row block.
 //  * Work list: every request's rows are cut into chunks of whole tiles,
 //    balanced over the batch so that the grid is one round of workgroups
-//    (ragged lengths included).  A request's only chunk writes (o_r, lse_r)
+//    (ragged lengths included); dcp_stripe_attn_multi lists the requests of
+//    several ranks in one launch.  A request's only chunk writes (o_r, lse_r)
 //    itself; otherwise each chunk writes an (o, lse) partial and a second
 //    launch merges a request's chunks with the same exact LSE merge as across
 //    stripes (the chunks are a disjoint partition of the stripe's rows).
@@ -118,8 +119,26 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // makes the kernel read outside the pool.
 __device__ __align__(16) uint4 g_zero_row[kRowSlots];
 
+// What differs between the ranks of one launch (one rank per dcp_stripe_attn
+// call; up to kMaxRanks in dcp_stripe_attn_multi).
+struct RankPtrs {
+  const char* pool;
+  const int32_t* bt;
+  float* o;                         // final outputs (requests cut into one chunk)
+  float* lse;
+  const float* sinks;               // [H] natural-log sink logits, nullable
+  const int32_t* sp_rows;           // sparse selection: local rows [B][sp_stride]
+  const uint32_t* sp_bits;          //   which query tokens selected each entry (bit t)
+  const int32_t* sp_count;          //   entries per request [B]
+  int64_t num_pages;
+  int32_t rank, bt_cols, sp_stride, pad;
+};
+constexpr int kMaxRanks = 16;
+constexpr int kGroupChunkTiles = 512;   // longest chunk when a request's rows are cut into groups
+
 struct Params {
-  int32_t N, I, P, rank;
+  int32_t N, I, P;
+  int32_t nr;                       // ranks in the launch: request v is request v % B of rank slot v / B
   int32_t B, q_len, H, M;          // M = q_len * H query rows per request
   int32_t RB, mgroups;
   int32_t slots;                    // chunk slots of the workspace (grid = slots * mgroups)
@@ -128,29 +147,37 @@ struct Params {
                                     // unmerged to o / lse as part (chunk, request) -- no combine
   int32_t target_chunks;            // balanced: at most this many chunks (when >= B)
   const __bf16* q;
-  const char* pool;
-  int64_t num_pages;
-  const int32_t* bt;
-  int32_t bt_cols;
   const int32_t* seq_len;
   float c2;                         // scale * log2(e)
   int32_t window;                   // > 0: a query at t sees t - window < p <= t
   float cap_in, cap_out;            // softcap: s -> cap_out * tanh(s * cap_in) (raw-score units)
-  const float* sinks;               // [H] natural-log sink logits, nullable
   const float* slopes;              // [H] position-bias slopes (natural-log units), nullable
-  const int32_t* sp_rows;           // sparse selection: local rows [B][sp_stride], nullable
-  const uint32_t* sp_bits;          //   which query tokens selected each entry (bit t)
-  const int32_t* sp_count;          //   entries per request [B]
-  int32_t sp_stride;
+  int32_t sparse;                   // every rank has a sparse selection
   float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
-  float* o;                         // final outputs (requests cut into one chunk)
-  float* lse;
   float* ws_o;                      // chunk partials [slots][M][512], lse2 [slots][M]
   float* ws_lse;
-  int32_t* table;                   // chunks per request [B], first chunk of each request [B]
+  int32_t* table;                   // chunks per request [nr*B], first chunk of each request [nr*B]
   int32_t* status;
+  RankPtrs rk[kMaxRanks];
 };
+
+// the DCP rank and sparse count of rank slot ri (a per-lane slot: selected
+// from the wave-uniform parameters, so no parameter is indexed per lane)
+__device__ __forceinline__ int32_t rank_id(const Params& p, int32_t ri) {
+  int32_t r = p.rk[0].rank;
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i)
+    if (i < p.nr && ri == i) r = p.rk[i].rank;
+  return r;
+}
+__device__ __forceinline__ const int32_t* sp_count_of(const Params& p, int32_t ri) {
+  const int32_t* c = p.rk[0].sp_count;
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i)
+    if (i < p.nr && ri == i) c = p.rk[i].sp_count;
+  return c;
+}
 
 // 32-bit layout arithmetic (positions < 2^31: seq_len is int32)
 __device__ __forceinline__ int32_t count_rows(int32_t x, int32_t N, int32_t I, int32_t r) {
@@ -177,7 +204,9 @@ __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 
 // sees, from the first row its first query's window reaches, aligned down to
 // a tile) make tiles_b tiles of 32; the request is cut into n_b >= 1 chunks of
 // cs_b = ceil(tiles_b / n_b) tiles (an empty request gets one empty chunk,
-// which writes its zero output).  With forced_splits = s: n_b = number of
+// which writes its zero output).  Requests of all the ranks of a launch are
+// listed rank by rank (request v = request v % B of rank slot v / B).  With
+// forced_splits = s: n_b = number of
 // chunks of ceil(tiles_b / s) tiles.  Otherwise the chunks are balanced over
 // the whole batch: n_b = ceil(tiles_b / C) for the smallest of a few
 // candidate chunk lengths C that keeps the total under target_chunks (the
@@ -192,21 +221,24 @@ struct WorkItem {
 };
 
 // first local row any query of a request with S cached tokens can see
-__device__ __forceinline__ int32_t first_row(const Params& p, int32_t S) {
-  return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, p.rank) : 0;
+__device__ __forceinline__ int32_t first_row(const Params& p, int32_t S, int32_t rank) {
+  return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, rank) : 0;
 }
 
-// What the chunks of request b cover: its local rows (the selected entries
-// with a sparse selection) and the tile of the first row any query sees.
-__device__ __forceinline__ int32_t req_rows(const Params& p, int32_t b) {
-  return p.sp_rows ? p.sp_count[b] : count_rows(p.seq_len[b], p.N, p.I, p.rank);
+// What the chunks of (virtual) request v cover: its local rows on its rank
+// (the selected entries with a sparse selection) and the tile of the first
+// row any query sees.
+__device__ __forceinline__ int32_t req_rows(const Params& p, int32_t v) {
+  const int32_t ri = v / p.B, b = v - ri * p.B;
+  return p.sparse ? sp_count_of(p, ri)[b] : count_rows(p.seq_len[b], p.N, p.I, rank_id(p, ri));
 }
-__device__ __forceinline__ int32_t req_first_tile(const Params& p, int32_t b) {
-  return p.sp_rows ? 0 : first_row(p, p.seq_len[b]) / 32;
+__device__ __forceinline__ int32_t req_first_tile(const Params& p, int32_t v) {
+  const int32_t ri = v / p.B, b = v - ri * p.B;
+  return p.sparse ? 0 : first_row(p, p.seq_len[b], rank_id(p, ri)) / 32;
 }
-__device__ __forceinline__ int32_t req_tiles(const Params& p, int32_t b) {
-  const int32_t rows = req_rows(p, b);
-  return rows > 0 ? cdiv(rows, 32) - req_first_tile(p, b) : 0;
+__device__ __forceinline__ int32_t req_tiles(const Params& p, int32_t v) {
+  const int32_t rows = req_rows(p, v);
+  return rows > 0 ? cdiv(rows, 32) - req_first_tile(p, v) : 0;
 }
 
 // Unmerged parts: chunk c is part c % k of request c / k (k = partials); a
@@ -216,7 +248,7 @@ __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
   WorkItem w{0, 0, 0, 0, 0, 0, false};
   const int32_t k = p.partials;
   w.b = c / k;
-  w.live = w.b < p.B;
+  w.live = w.b < p.nr * p.B;
   if (!w.live) return w;
   w.k = c - w.b * k;
   w.n = k;
@@ -229,6 +261,7 @@ __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
 
 __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
   const int lane = threadIdx.x & 63;
+  const int32_t Bv = p.nr * p.B;                  // requests of all ranks in the launch
   // tiles of request b (from its first tile on); the first 256 requests'
   // are loaded once (all loads in flight together) and kept in registers
   constexpr int kCached = 4;
@@ -236,7 +269,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
 #pragma unroll
   for (int j = 0; j < kCached; ++j) {
     const int32_t b = 64 * j + lane;
-    tiles_c[j] = b < p.B ? req_tiles(p, b) : 0;
+    tiles_c[j] = b < Bv ? req_tiles(p, b) : 0;
   }
   auto tiles_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
     const int32_t b = b0 + lane;
@@ -246,43 +279,43 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? tiles_c[j] : r;
       return r;
     }
-    return b < p.B ? req_tiles(p, b) : 0;
+    return b < Bv ? req_tiles(p, b) : 0;
   };
   int32_t C = 1;
   if (p.forced_splits == 0) {
-    int32_t total = 0, maxt = 0;
-    for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
-      const int32_t t = tiles_of(b0);
-      total += t;
-      maxt = max(maxt, t);
-    }
+    int32_t total = 0;
+    for (int32_t b0 = 0; b0 < Bv; b0 += 64) total += tiles_of(b0);
     total = wave_sum_i(total);
-    maxt = max(wave_max_i(maxt), 1);
     auto chunks_for = [&](int32_t len) -> int32_t {
       int32_t nc = 0;
-      for (int32_t b0 = 0; b0 < p.B; b0 += 64)
-        nc += b0 + lane < p.B ? max(cdiv(tiles_of(b0), len), 1) : 0;
+      for (int32_t b0 = 0; b0 < Bv; b0 += 64)
+        nc += b0 + lane < Bv ? max(cdiv(tiles_of(b0), len), 1) : 0;
       return wave_sum_i(nc);
     };
     const int32_t target = p.target_chunks;
-    if (target <= p.B) {
-      C = maxt;                                    // one chunk per request
+    if (target <= Bv) {
+      // at least one chunk per request anyway: chunks of the mean per-CU share,
+      // so a long request is split and the rounds of workgroups stay balanced.
+      // The row groups of one chunk share its tiles through L2 only while they
+      // run in step, so with several groups a chunk is kept short.
+      C = max(cdiv(total, target), 1);
+      if (p.mgroups > 1) C = min(C, kGroupChunkTiles);
     } else {
       C = max(cdiv(total, target), 1);
       const int32_t T0 = chunks_for(C);
       if (T0 > target) {
         const int32_t C1 = cdiv(C * T0, target);
-        C = chunks_for(C1) <= target ? C1 : max(cdiv(total, target - p.B), 1);
+        C = chunks_for(C1) <= target ? C1 : max(cdiv(total, target - Bv), 1);
       }
     }
   }
   WorkItem w{0, 0, 0, 0, 0, 0, false};
   int32_t carry = 0;
-  for (int32_t b0 = 0; b0 < p.B; b0 += 64) {
+  for (int32_t b0 = 0; b0 < Bv; b0 += 64) {
     const int32_t b = b0 + lane;
     const int32_t t = tiles_of(b0);
     int32_t nb = 0;
-    if (b < p.B) {
+    if (b < Bv) {
       if (p.forced_splits > 0) nb = t > 0 ? cdiv(t, cdiv(t, p.forced_splits)) : 1;
       else nb = max(cdiv(t, C), 1);
     }
@@ -293,11 +326,11 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       if (lane >= d) x += y;
     }
     const int32_t incl = carry + x, excl = incl - nb;
-    if (write_table && b < p.B) {
+    if (write_table && b < Bv) {
       p.table[b] = nb;
-      p.table[p.B + b] = excl;
+      p.table[Bv + b] = excl;
     }
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(b < p.B && excl <= c && c < incl);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(b < Bv && excl <= c && c < incl);
     if (hit != 0 && !w.live) {
       const int l = __builtin_ctzll(hit);
       w.live = true;
@@ -399,7 +432,9 @@ stripe_attn_kernel(Params p) {
   const WorkItem wi = p.partials > 0 ? part_work(p, chunk)
                                       : find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
   if (!wi.live) return;                // past the last chunk (the same in every wave)
-  const int b = wi.b;
+  const int32_t ri = wi.b / p.B;       // rank slot of the launch
+  const int b = wi.b - ri * p.B;       // request
+  const RankPtrs& rk = p.rk[ri];
   // the request's only chunk, and every unmerged part, writes the output itself
   const bool direct = wi.n == 1 || p.partials > 0;
   const int64_t out_row0 = ((p.partials > 0 ? (int64_t)wi.k * p.B : 0) + b) * p.M;   // first output row
@@ -409,9 +444,9 @@ stripe_attn_kernel(Params p) {
   // sparse selection: the chunks run over entries of the request's list of
   // selected local rows; with several drafts each entry carries the drafts
   // that selected it
-  const bool sparse = p.sp_rows != nullptr;
+  const bool sparse = p.sparse != 0;
   const bool sparse_bits = sparse && p.q_len > 1;
-  const int64_t sp_base = sparse ? (int64_t)b * p.sp_stride : 0;
+  const int64_t sp_base = sparse ? (int64_t)b * rk.sp_stride : 0;
   const int32_t row_lo = (wi.ft + wi.k * wi.cs) * kTile;
   int32_t row_hi = row_lo + wi.cs * kTile;
   row_hi = row_hi < max_vis ? row_hi : max_vis;
@@ -422,12 +457,12 @@ stripe_attn_kernel(Params p) {
   const int R = row0 + wave * 32 + n;
   const bool valid = qk_wave && R < p.M;
   const int t = valid ? R / p.H : 0;
-  int32_t lim = sparse ? row_hi : count_rows(S_b - p.q_len + t + 1, p.N, p.I, p.rank);
+  int32_t lim = sparse ? row_hi : count_rows(S_b - p.q_len + t + 1, p.N, p.I, rk.rank);
   if (!valid) lim = row_hi;
   lim = lim < row_hi ? lim : row_hi;
   // first visible row (sliding window): rows below it are masked
   int32_t low = 0;
-  if (valid && p.window > 0) low = count_rows(S_b - p.q_len + t + 1 - p.window, p.N, p.I, p.rank);
+  if (valid && p.window > 0) low = count_rows(S_b - p.q_len + t + 1 - p.window, p.N, p.I, rk.rank);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds row n, dims
   // 16*ks + 8*half .. +7 for every k-step (QK waves, loaded on their path)
@@ -441,7 +476,7 @@ stripe_attn_kernel(Params p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(smem + kFlagOff)[threadIdx.x] = 0;   // ordered by the first barrier
   const char* zero = reinterpret_cast<const char*>(g_zero_row);
-  const int32_t* bt_row = p.bt + (int64_t)b * p.bt_cols;
+  const int32_t* bt_row = rk.bt + (int64_t)b * rk.bt_cols;
 
   // ---- page table of the split, one page id per lane, 64 pages at a time
   // (page-aligned tiles only: a tile lies inside one page)
@@ -450,7 +485,7 @@ stripe_attn_kernel(Params p) {
   auto load_page_table = [&](int32_t base) {
     pt_base = base;
     const int32_t pi = base + lane;
-    vpt = pi < p.bt_cols ? bt_row[pi] : -1;
+    vpt = pi < rk.bt_cols ? bt_row[pi] : -1;
     // Consume the loaded value right here, so the wait for this load happens
     // on this (rare) path; otherwise the compiler waits for every outstanding
     // vector-memory operation -- all in-flight tile loads -- at each later use.
@@ -463,11 +498,11 @@ stripe_attn_kernel(Params p) {
     const int32_t pi = J / p.P;
     if (pi - pt_base >= 64) load_page_table(pi);    // rare: long splits cross 64 pages
     const int32_t pg = __builtin_amdgcn_readlane(vpt, pi - pt_base);
-    if (pg < 0 || pg >= p.num_pages) {
+    if (pg < 0 || pg >= rk.num_pages) {
       if (lane == 0) flag_range(p.status);
       return nullptr;
     }
-    return p.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
+    return rk.pool + ((int64_t)pg * p.P + (J % p.P)) * kRowBytes;
   };
 
   // the loader wave issues all 37 loads of a tile
@@ -511,10 +546,10 @@ stripe_attn_kernel(Params p) {
       const char* tb = tile_base_of(it);
       if (tb) rowp = tb + tl * kRowBytes;
     } else {
-      const int32_t j = sparse ? p.sp_rows[sp_base + J + tl] : J + tl;
+      const int32_t j = sparse ? rk.sp_rows[sp_base + J + tl] : J + tl;
       const int32_t pi = j / p.P;
-      const int32_t pg = j >= 0 && pi < p.bt_cols ? bt_row[pi] : -1;
-      if (pg >= 0 && pg < p.num_pages) rowp = p.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes;
+      const int32_t pg = j >= 0 && pi < rk.bt_cols ? bt_row[pi] : -1;
+      if (pg >= 0 && pg < rk.num_pages) rowp = rk.pool + ((int64_t)pg * p.P + j % p.P) * kRowBytes;
       else flag_range(p.status);
     }
     const uint64_t ra = reinterpret_cast<uint64_t>(rowp);
@@ -583,7 +618,7 @@ stripe_attn_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int32_t j = j0 + tok_of(i);
-          const int32_t pos = (j / p.I) * round + p.rank * p.I + j % p.I;
+          const int32_t pos = (j / p.I) * round + rk.rank * p.I + j % p.I;
           x[i] += bias_raw * (float)(pos - q_pos);
         }
       }
@@ -629,7 +664,7 @@ stripe_attn_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int e = tok_of(i);
-          const bool sel = e < vis && ((p.sp_bits[sp_base + tj0 + (e < vis ? e : 0)] >> t) & 1u);
+          const bool sel = e < vis && ((rk.sp_bits[sp_base + tj0 + (e < vis ? e : 0)] >> t) & 1u);
           sacc[i] = sel ? sacc[i] : -INFINITY;
         }
       } else if (__builtin_amdgcn_ballot_w64(vis < kTile || vlo > 0) != 0) {
@@ -846,10 +881,10 @@ stripe_attn_kernel(Params p) {
     const float l_tot = l_run + other_half(l_run);
     float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     float lse2 = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    if (p.sinks != nullptr && wi.k == 0 && valid) {
+    if (rk.sinks != nullptr && wi.k == 0 && valid) {
       // the sink's term 2^sg joins the denominator of the request's first
       // chunk, against a reference that covers both
-      const float sg = p.sinks[R % p.H] * kLog2e;
+      const float sg = rk.sinks[R % p.H] * kLog2e;
       if (sg > -INFINITY) {
         const float ref = l_tot > 0.f ? fmaxf(m_run, sg) : sg;
         const float a = l_tot > 0.f ? __builtin_amdgcn_exp2f(m_run - ref) : 0.f;
@@ -861,7 +896,7 @@ stripe_attn_kernel(Params p) {
     if (half == 0) {
       inv_lds[wave * 32 + n] = inv;
       if (valid) {
-        if (direct) p.lse[out_row0 + R] = p.out_base2 ? lse2 : lse2 * kLn2;
+        if (direct) rk.lse[out_row0 + R] = p.out_base2 ? lse2 : lse2 * kLn2;
         else p.ws_lse[(int64_t)chunk * p.M + R] = lse2;
       }
     }
@@ -869,7 +904,7 @@ stripe_attn_kernel(Params p) {
   lds_barrier();
   if (!pv_wave) return;
   float* out_base;
-  if (direct) out_base = p.o + out_row0 * kDV;
+  if (direct) out_base = rk.o + out_row0 * kDV;
   else out_base = p.ws_o + (int64_t)chunk * p.M * kDV;
   out_base += cgrp * kWaveCols * 32;
   {
@@ -908,14 +943,16 @@ stripe_attn_kernel(Params p) {
 
 struct Plan {
   int RB, mgroups;
+  int64_t Bv;              // requests of all ranks in the launch
   int64_t slots;           // chunk slots; the grid has slots * mgroups workgroups
   int32_t forced, target;  // Params::forced_splits, Params::target_chunks
   bool combine;            // some request may have several chunks
   size_t ws_bytes, table_off;
 };
 
-int make_plan(const dcp_attn_args* a, Plan* pl) {
-  if (a == nullptr || pl == nullptr) return DCP_EINVAL;
+// Checks of one rank's arguments (pointers are not read).
+int check_args(const dcp_attn_args* a) {
+  if (a == nullptr) return DCP_EINVAL;
   if (!layout_ok(a->layout)) return DCP_EINVAL;
   if (a->rank < 0 || a->rank >= a->layout.n_stripes) return DCP_EINVAL;
   if (a->batch < 1 || a->q_len < 1 || a->n_heads < 1) return DCP_EINVAL;
@@ -935,6 +972,37 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
   const int64_t max_rows = a->sparse_rows ? (int64_t)a->sparse_stride : (int64_t)a->bt_cols * a->layout.page_size;
   if (M > (1 << 20) || max_rows > 0x7fffffff - 64) return DCP_EUNSUPPORTED;
   if ((int64_t)a->layout.n_stripes * a->layout.interleave > 0x7fffffff) return DCP_EUNSUPPORTED;
+  return DCP_OK;
+}
+
+// The ranks of one launch share everything but the rank's own data (pool,
+// table, outputs, sink, selection).
+bool same_launch(const dcp_attn_args& a, const dcp_attn_args& b) {
+  return a.layout.n_stripes == b.layout.n_stripes && a.layout.interleave == b.layout.interleave &&
+         a.layout.page_size == b.layout.page_size && a.batch == b.batch && a.q_len == b.q_len &&
+         a.n_heads == b.n_heads && a.q == b.q && a.seq_len == b.seq_len && a.scale == b.scale &&
+         a.lse_base == b.lse_base && a.num_splits == b.num_splits && a.window == b.window &&
+         a.softcap == b.softcap && a.partials == b.partials && a.bias_slopes == b.bias_slopes &&
+         (a.sparse_rows == nullptr) == (b.sparse_rows == nullptr);
+}
+
+int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
+  if (args == nullptr || pl == nullptr || n < 1) return DCP_EINVAL;
+  if (n > kMaxRanks) return DCP_EUNSUPPORTED;
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = check_args(&args[i]);
+    if (rc != DCP_OK) return rc;
+    if (!same_launch(args[0], args[i])) return DCP_EINVAL;
+  }
+  const dcp_attn_args* a = &args[0];
+  const int64_t M = (int64_t)a->q_len * a->n_heads;
+  int64_t max_rows = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t m = args[i].sparse_rows ? (int64_t)args[i].sparse_stride
+                                          : (int64_t)args[i].bt_cols * args[i].layout.page_size;
+    max_rows = m > max_rows ? m : max_rows;
+  }
+  pl->Bv = (int64_t)n * a->batch;
   // query rows per workgroup: up to 3 blocks of 32; above 96 rows the rows
   // are cut into groups (the workgroups of one group run side by side on
   // one XCD and share each KV tile through its L2), with the block count
@@ -952,14 +1020,16 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
     // unmerged parts: exactly num_splits per request, some possibly empty
     pl->forced = a->num_splits;
     pl->target = 0;
-    pl->slots = (int64_t)a->batch * a->num_splits;
+    pl->slots = pl->Bv * a->num_splits;
   } else if (a->num_splits > 0) {
     // a fixed number of chunks per request
     pl->forced = (int32_t)(a->num_splits < tiles_max ? a->num_splits : tiles_max);
     pl->target = 0;
-    pl->slots = (int64_t)a->batch * pl->forced;
+    pl->slots = pl->Bv * pl->forced;
   } else {
-    // balanced chunks: one workgroup per compute unit, all in one round
+    // balanced chunks: one workgroup per compute unit, in one round when the
+    // requests are fewer than the compute units; otherwise chunks of the mean
+    // per-unit share (at most target + requests of them)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
       int v = 0;
@@ -967,15 +1037,20 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
     }
     pl->forced = 0;
     pl->target = cus / pl->mgroups > 1 ? cus / pl->mgroups : 1;
-    pl->slots = pl->target > a->batch ? pl->target : a->batch;
+    pl->slots = pl->target > pl->Bv ? pl->target : pl->target + pl->Bv;
+    if (pl->target <= pl->Bv && pl->mgroups > 1) {
+      // chunks capped at kGroupChunkTiles tiles: at most that share of every request, plus one
+      const int64_t capped = pl->Bv * (ceil_div(tiles_max, kGroupChunkTiles) + 1);
+      pl->slots = capped > pl->slots ? capped : pl->slots;
+    }
   }
-  if (pl->slots * pl->mgroups > 0x7fffffff) return DCP_EUNSUPPORTED;
+  if (pl->slots * pl->mgroups > 0x7fffffff || pl->Bv > 0x7fffffff / 2) return DCP_EUNSUPPORTED;
   pl->combine = pl->forced != 1 && !a->partials;
   // chunk partials (o, base-2 lse) and the chunk table
   if (pl->combine) {
     const size_t part = (size_t)pl->slots * M * (kDV + 1) * sizeof(float);
     pl->table_off = (part + 255) & ~(size_t)255;
-    pl->ws_bytes = pl->table_off + (size_t)2 * a->batch * sizeof(int32_t);
+    pl->ws_bytes = pl->table_off + (size_t)2 * pl->Bv * sizeof(int32_t);
   } else {
     pl->table_off = 0;
     pl->ws_bytes = 0;
@@ -988,19 +1063,22 @@ int make_plan(const dcp_attn_args* a, Plan* pl) {
 // alone; the chunks partition the request's rows, so their partials merge
 // exactly like stripes (base-2 partial lse).
 __global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
-chunk_combine_kernel(int32_t B, int32_t M, int32_t v4, const int32_t* __restrict__ table,
-                     const float4* __restrict__ ws_o, const float* __restrict__ ws_lse, int32_t out_base2,
-                     float4* __restrict__ o, float* __restrict__ lse) {
+chunk_combine_kernel(Params p) {
   int64_t bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
   const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
-  if (row >= (int64_t)B * M) return;
-  const int32_t b = (int32_t)(row / M), m = (int32_t)(row % M);
-  const int32_t n = table[b];
+  const int64_t Bv = (int64_t)p.nr * p.B;
+  if (row >= Bv * p.M) return;
+  const int32_t v = (int32_t)(row / p.M), m = (int32_t)(row % p.M);
+  const int32_t n = p.table[v];
   if (n <= 1) return;
-  const int64_t c0 = table[B + b];
-  merge_one_row(n, M, v4, ws_o + (c0 * M + m) * v4, ws_lse + c0 * M + m, 1, out_base2, o + row * v4,
-                lse + row);
+  const int64_t c0 = p.table[Bv + v];
+  const int32_t ri = v / p.B, b = v - ri * p.B;
+  const RankPtrs& rk = p.rk[ri];
+  constexpr int v4 = kDV / 4;
+  const int64_t out = (int64_t)b * p.M + m;
+  merge_one_row(n, p.M, v4, reinterpret_cast<const float4*>(p.ws_o) + (c0 * p.M + m) * v4, p.ws_lse + c0 * p.M + m,
+                1, p.out_base2, reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
 }
 
 template <int RB, bool kLogit>
@@ -1018,35 +1096,26 @@ int launch(const Params& prm, int64_t blocks, hipStream_t stream) {
   return logit ? launch<RB, true>(prm, blocks, stream) : launch<RB, false>(prm, blocks, stream);
 }
 
-}  // namespace attn
-}  // namespace dcp
-
-using namespace dcp;
-using namespace dcp::attn;
-
-extern "C" int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes) {
-  if (bytes == nullptr) return DCP_EINVAL;
+// One launch (plus the chunk combine when a request has several chunks) for
+// the n ranks of `args`; the workspace of args[0] serves them all.
+int run(const dcp_attn_args* args, int32_t n, void* stream) {
   Plan pl;
-  const int rc = make_plan(args, &pl);
+  const int rc = make_plan(args, n, &pl);
   if (rc != DCP_OK) return rc;
-  *bytes = pl.ws_bytes;
-  return DCP_OK;
-}
-
-extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
-  Plan pl;
-  const int rc = make_plan(a, &pl);
-  if (rc != DCP_OK) return rc;
-  if (a->q == nullptr || a->pool == nullptr || a->block_table == nullptr || a->seq_len == nullptr ||
-      a->o == nullptr || a->lse == nullptr)
-    return DCP_EINVAL;
+  const dcp_attn_args* a = &args[0];
+  for (int32_t i = 0; i < n; ++i) {
+    const dcp_attn_args& x = args[i];
+    if (x.q == nullptr || x.pool == nullptr || x.block_table == nullptr || x.seq_len == nullptr ||
+        x.o == nullptr || x.lse == nullptr)
+      return DCP_EINVAL;
+  }
   if (pl.ws_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < pl.ws_bytes)) return DCP_EINVAL;
   const int64_t M = (int64_t)a->q_len * a->n_heads;
-  Params prm;
+  Params prm = {};
   prm.N = a->layout.n_stripes;
   prm.I = a->layout.interleave;
   prm.P = a->layout.page_size;
-  prm.rank = a->rank;
+  prm.nr = n;
   prm.B = a->batch;
   prm.q_len = a->q_len;
   prm.H = a->n_heads;
@@ -1058,29 +1127,35 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
   prm.partials = a->partials ? a->num_splits : 0;
   prm.target_chunks = pl.target;
   prm.q = (const __bf16*)a->q;
-  prm.pool = (const char*)a->pool;
-  prm.num_pages = a->num_pages;
-  prm.bt = a->block_table;
-  prm.bt_cols = a->bt_cols;
   prm.seq_len = a->seq_len;
   prm.c2 = a->scale * kLog2e;
   prm.window = a->window;
   prm.cap_in = a->softcap > 0.f ? a->scale / a->softcap : 0.f;
   prm.cap_out = a->softcap > 0.f ? a->softcap / a->scale : 0.f;
-  prm.sinks = a->sinks;
   prm.slopes = a->bias_slopes;
-  prm.sp_rows = a->sparse_rows;
-  prm.sp_bits = a->sparse_bits;
-  prm.sp_count = a->sparse_count;
-  prm.sp_stride = a->sparse_stride;
+  prm.sparse = a->sparse_rows != nullptr;
   prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
-  prm.o = a->o;
-  prm.lse = a->lse;
   prm.ws_o = pl.combine ? (float*)a->workspace : nullptr;
   prm.ws_lse = pl.combine ? prm.ws_o + (size_t)pl.slots * M * kDV : nullptr;
   prm.table = pl.combine ? (int32_t*)((char*)a->workspace + pl.table_off) : nullptr;
   prm.status = a->status;
+  for (int32_t i = 0; i < n; ++i) {
+    const dcp_attn_args& x = args[i];
+    RankPtrs& r = prm.rk[i];
+    r.pool = (const char*)x.pool;
+    r.bt = x.block_table;
+    r.o = x.o;
+    r.lse = x.lse;
+    r.sinks = x.sinks;
+    r.sp_rows = x.sparse_rows;
+    r.sp_bits = x.sparse_bits;
+    r.sp_count = x.sparse_count;
+    r.num_pages = x.num_pages;
+    r.rank = x.rank;
+    r.bt_cols = x.bt_cols;
+    r.sp_stride = x.sparse_stride;
+  }
   const int64_t blocks = pl.slots * pl.mgroups;
   hipStream_t s = (hipStream_t)stream;
   int r;
@@ -1090,9 +1165,33 @@ extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) {
     default: r = launch<3>(prm, blocks, s); break;
   }
   if (r != DCP_OK || !pl.combine) return r;
-  const int64_t rows = (int64_t)a->batch * M;
+  const int64_t rows = pl.Bv * M;
   hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)ceil_div(rows, kMergeRowsPerBlock)),
-                     dim3(64 * kMergeRowsPerBlock), 0, s, a->batch, (int32_t)M, kDV / 4, prm.table,
-                     (const float4*)prm.ws_o, prm.ws_lse, a->lse_base, (float4*)a->o, a->lse);
+                     dim3(64 * kMergeRowsPerBlock), 0, s, prm);
   return launch_status();
+}
+
+}  // namespace attn
+}  // namespace dcp
+
+using namespace dcp;
+using namespace dcp::attn;
+
+extern "C" int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes) {
+  return dcp_stripe_attn_multi_workspace(args, 1, bytes);
+}
+
+extern "C" int dcp_stripe_attn(const dcp_attn_args* a, void* stream) { return run(a, 1, stream); }
+
+extern "C" int dcp_stripe_attn_multi_workspace(const dcp_attn_args* args, int32_t n, size_t* bytes) {
+  if (bytes == nullptr) return DCP_EINVAL;
+  Plan pl;
+  const int rc = make_plan(args, n, &pl);
+  if (rc != DCP_OK) return rc;
+  *bytes = pl.ws_bytes;
+  return DCP_OK;
+}
+
+extern "C" int dcp_stripe_attn_multi(const dcp_attn_args* args, int32_t n, void* stream) {
+  return run(args, n, stream);
 }

@@ -89,6 +89,9 @@ _SIGNATURES = {
     "dcp_kv_write": (ctypes.c_int, [dcp_layout, _I32, _VP, _I32, _I64, _VP, _VP, _VP, _I32, _I32, _VP, _I64, _VP, _VP]),
     "dcp_stripe_attn_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
+    "dcp_stripe_attn_multi_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _I32,
+                                                       ctypes.POINTER(ctypes.c_size_t)]),
+    "dcp_stripe_attn_multi": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _I32, _VP]),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
     "dcp_pack_heads": (ctypes.c_int, [_I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP]),
     "dcp_sparse_plan": (ctypes.c_int, [dcp_layout, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
@@ -398,3 +401,54 @@ def dcp_sparse_plan(lay: dcp_layout, rank: int, topk_pos: torch.Tensor, seq_len:
                                int(rows.shape[1]), _stream(dev))
     _check(rc, "dcp_sparse_plan")
     return rows, bits, count
+
+
+def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_tables, seq_len: torch.Tensor,
+                          scale: float, lse_base: int = 0, num_splits: int = 0, o: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                          window: int = 0, softcap: float = 0.0, sinks=None, bias_slopes=None, sparse=None,
+                          workspace: Optional[torch.Tensor] = None):
+    """The stripe attentions of several ranks in one launch: ranks[i] with pools[i],
+    block_tables[i] (and sinks[i], sparse[i] when given per rank, else None).  Returns
+    o [n, B, q_len, H, 512] and lse [n, B, q_len, H], equal to n dcp_stripe_attn calls."""
+    dev = q.device
+    n = len(ranks)
+    B, q_len, H, D = q.shape
+    if len(pools) != n or len(block_tables) != n:
+        raise ValueError("one pool and one block table per rank")
+    if o is None:
+        o = torch.empty((n, B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((n, B, q_len, H), dtype=torch.float32, device=dev)
+    if o.shape[0] != n or lse.shape[0] != n:
+        raise ValueError("o / lse need one block per rank")
+    arr = (dcp_attn_args * n)()
+    for i in range(n):
+        a = _attn_args(lay, ranks[i], q, pools[i], block_tables[i], seq_len, scale, lse_base, num_splits,
+                       None, None, None, None, window, softcap, 0)
+        a.q = _ptr(q, torch.bfloat16, "q", dev)
+        a.pool = _ptr(pools[i], torch.bfloat16, "pool", dev)
+        a.block_table = _ptr(block_tables[i], torch.int32, "block_table", dev)
+        a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
+        a.o = _ptr(o[i], torch.float32, "o", dev)
+        a.lse = _ptr(lse[i], torch.float32, "lse", dev)
+        a.status = _ptr(status, torch.int32, "status", dev)
+        a.bias_slopes = _ptr(bias_slopes, torch.float32, "bias_slopes", dev)
+        if sinks is not None and sinks[i] is not None:
+            a.sinks = _ptr(sinks[i], torch.float32, "sinks", dev)
+        if sparse is not None:
+            rows, bits, count = sparse[i]
+            a.sparse_rows = _ptr(rows, torch.int32, "sparse rows", dev)
+            a.sparse_bits = _ptr(bits, torch.int32, "sparse bits", dev)
+            a.sparse_count = _ptr(count, torch.int32, "sparse count", dev)
+            a.sparse_stride = int(rows.shape[1])
+        arr[i] = a
+    need = ctypes.c_size_t(0)
+    _check(lib().dcp_stripe_attn_multi_workspace(arr, n, ctypes.byref(need)), "dcp_stripe_attn_multi_workspace")
+    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        arr[0].workspace = _ptr(workspace, None, "workspace", dev)
+        arr[0].workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().dcp_stripe_attn_multi(arr, n, _stream(dev)), "dcp_stripe_attn_multi")
+    return o, lse

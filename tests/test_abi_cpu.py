@@ -16,7 +16,8 @@ def test_library_exports_every_declared_function():
     names = dcp.header_functions()
     assert {"dcp_slot_map", "dcp_local_count", "dcp_kv_write", "dcp_stripe_attn",
             "dcp_stripe_attn_workspace", "dcp_lse_merge", "dcp_strerror", "dcp_relayout", "dcp_pack_heads",
-            "dcp_merge_heads", "dcp_sparse_plan"} <= set(names)
+            "dcp_merge_heads", "dcp_sparse_plan", "dcp_stripe_attn_multi",
+            "dcp_stripe_attn_multi_workspace"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -228,3 +229,19 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dcp, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="missing"):
         dcp.lib()
+
+
+def test_multi_rank_launch_argument_errors():
+    arr = (dcp.dcp_attn_args * 3)(_args(rank=0), _args(rank=1), _args(rank=2))
+    n = ctypes.c_size_t(0)
+    assert L.dcp_stripe_attn_multi_workspace(arr, 3, ctypes.byref(n)) == dcp.DCP_OK
+    # the three ranks' chunk slots: 2 requests each, 2 splits (the _args default)
+    assert n.value == -(-(3 * 2 * 2 * 16 * 513 * 4) // 256) * 256 + 2 * 3 * 2 * 4
+    assert L.dcp_stripe_attn_multi_workspace(arr, 0, ctypes.byref(n)) == dcp.DCP_EINVAL
+    big = (dcp.dcp_attn_args * 17)(*[_args(rank=i % 8) for i in range(17)])
+    assert L.dcp_stripe_attn_multi(big, 17, None) == dcp.DCP_EUNSUPPORTED
+    for field, value in (("q", 0x2000), ("batch", 3), ("num_splits", 3), ("softcap", 1.0), ("seq_len", 0x2000)):
+        arr = (dcp.dcp_attn_args * 2)(_args(rank=0), _args(rank=1, **{field: value}))
+        assert L.dcp_stripe_attn_multi(arr, 2, None) == dcp.DCP_EINVAL, field
+    arr = (dcp.dcp_attn_args * 2)(_args(rank=0), _args(rank=9))
+    assert L.dcp_stripe_attn_multi(arr, 2, None) == dcp.DCP_EINVAL

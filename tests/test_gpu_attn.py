@@ -302,3 +302,48 @@ def _sparse_oracle(q64, kv64, S, topk, positions, softcap, sinks):
         o[t], lse[t] = OA.attention_rows(q64[t], np.full(H_, qp), kv64[sel] if len(sel) else kv64[:0], sel,
                                          workloads.SCALE, softcap=softcap, sink=sinks)
     return o, lse
+
+
+
+# ---- all ranks in one launch ---------------------------------------------------
+
+MULTI = [
+    # name, I, lens, extra
+    ("tiny", 1, None, None),
+    ("custom", 1, [1, 7, 900, 3000, 65, 2], None),           # ragged, empty stripes
+    ("custom", 64, [2000, 129], "variants"),                  # interleave 64 with window, softcap, sink, bias
+]
+
+
+@pytest.mark.parametrize("name,I,lens,extra", MULTI)
+def test_multi_rank_launch_equals_per_rank_calls(name, I, lens, extra):
+    if name == "tiny":
+        w = workloads.WORKLOADS["tiny"]
+        lens = workloads.seq_lens(w)
+    else:
+        w, lens = custom(len(lens), 96, 2, 8, 64, lens, "2")
+    print(f"multi {name} I={I} lens={list(lens)} {extra}", flush=True)
+    s = H.make_setup(w, I, lens=lens)
+    N = s.lay.n_stripes
+    var = {}
+    sinks = None
+    if extra:
+        sinks = np.random.default_rng(4).normal(0.0, 1.0, w.H)
+        var = dict(window=900, softcap=2.0, slopes=2.0 ** (-8.0 * (np.arange(w.H) + 1) / w.H))
+    o_parts, lse_parts, o, lse = H.run_step(s, 0, sinks=sinks, sink_rank=N - 1, **var)
+    dev = s.q.device
+    sk = [None] * N
+    if sinks is not None:
+        sk[N - 1] = torch.tensor(sinks, dtype=torch.float32, device=dev)
+    sl = None if not extra else torch.tensor(var["slopes"], dtype=torch.float32, device=dev)
+    mo, ml = dcp.dcp_stripe_attn_multi(s.lay, list(range(N)), s.q, s.sp.pools, s.sp.tables, s.sp.seq_len,
+                                       workloads.SCALE, s.base_flag, status=s.status, window=var.get("window", 0),
+                                       softcap=var.get("softcap", 0.0), sinks=sk, bias_slopes=sl)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    # the same stripes as the per-rank calls (chunking may differ: compare within the bar)
+    H.assert_o_close(mo.cpu().numpy(), o_parts.cpu().numpy(), "multi-rank o_r vs per-rank o_r")
+    H.assert_lse_close(ml.cpu().numpy(), lse_parts.cpu().numpy(), "multi-rank lse_r vs per-rank")
+    mo2, ml2 = dcp.dcp_lse_merge(mo, ml, s.base_flag)
+    for b in range(w.B):
+        H.check_request(s, mo, ml, mo2, ml2, b, sinks=sinks, sink_rank=N - 1, **var)

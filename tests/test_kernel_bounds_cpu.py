@@ -62,7 +62,9 @@ def plan(B, M, bt_cols, P, cus=256, num_splits=0):
     else:
         forced = 0
         target = max(cus // mgroups, 1)
-        slots = max(target, B)
+        slots = target if target > B else target + B
+        if target <= B and mgroups > 1:
+            slots = max(slots, B * (-(-tiles_max // GROUP_CHUNK) + 1))
     return W, mgroups, slots, forced, target
 
 
@@ -70,17 +72,22 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def work_list(tiles, forced, target):
+GROUP_CHUNK = 512          # longest chunk when the rows are cut into several groups
+
+
+def work_list(tiles, forced, target, mgroups=1):
     """The kernel's chunks in chunk order: (request, chunk of it, its chunk
     count, chunk length in tiles).  Every request gets at least one chunk."""
     B = len(tiles)
     if forced > 0:
         n = [cdiv(t, cdiv(t, forced)) if t > 0 else 1 for t in tiles]
     else:
-        total, maxt = int(sum(tiles)), max(int(max(tiles)), 1)
+        total = int(sum(tiles))
         chunks_for = lambda C: sum(max(cdiv(t, C), 1) for t in tiles)
         if target <= B:
-            C = maxt
+            C = max(cdiv(total, target), 1)          # chunks of the mean per-unit share
+            if mgroups > 1:
+                C = min(C, GROUP_CHUNK)
         else:
             C = max(cdiv(total, target), 1)
             T0 = chunks_for(C)
@@ -115,8 +122,10 @@ def test_work_list_fits_the_grid_and_partitions_every_request():
             for ns in (0, 1, 3, 8):
                 forced = min(ns, 10 ** 6) if ns else 0
                 target = 0 if ns else max(256 // mgroups, 1)
-                slots = B * forced if ns else max(target, B)
-                wl = work_list(list(tiles), forced, target)
+                slots = B * forced if ns else (target if target > B else target + B)
+                if not ns and target <= B and mgroups > 1:
+                    slots = max(slots, B * (-(-int(tiles.max(initial=0)) // GROUP_CHUNK) + 1))
+                wl = work_list(list(tiles), forced, target, mgroups)
                 assert len(wl) <= slots
                 for b in range(B):
                     mine = [(k, n, cs) for (bb, k, n, cs) in wl if bb == b]
@@ -126,6 +135,10 @@ def test_work_list_fits_the_grid_and_partitions_every_request():
                     assert covered == tiles[b] and (len(mine) - 1) * cs < max(tiles[b], 1)
                 if not ns and tiles.sum() > 0 and target > B:
                     assert max(cs for (_, _, _, cs) in wl) <= 2 * cdiv(int(tiles.sum()), target - B) + 1
+                if not ns and tiles.sum() > 0 and target <= B:
+                    # no chunk longer than the mean share of a compute unit (nor the group cap)
+                    cap = cdiv(int(tiles.sum()), target)
+                    assert max(cs for (_, _, _, cs) in wl) <= (min(cap, GROUP_CHUNK) if mgroups > 1 else cap)
 
 
 def count_rows(x, N, I, r):
@@ -211,7 +224,7 @@ def check_workload(w, I, plant=None, num_splits=0, window=0, partials=0):
             slots = B * partials
             wl = [(b, c, partials, cdiv(t, partials) if t else 0) for b, t in enumerate(tiles) for c in range(partials)]
         else:
-            wl = work_list(tiles, forced, target)
+            wl = work_list(tiles, forced, target, mgroups)
         assert len(wl) <= slots                        # every chunk has a workgroup
         for (b, sp, nchunks, cs) in wl:
             if True:
