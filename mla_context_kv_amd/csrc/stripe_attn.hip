@@ -361,7 +361,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 // 16-byte direct-to-LDS load from a uniform base plus a per-lane 32-bit offset
 // (the scalar-base form: no 64-bit per-lane address arithmetic).  The KV
 // stream is read once, so the load is marked non-temporal: it does not push
-// the split partials and outputs out of L2 and the memory-side cache.
+// the chunk partials and outputs out of L2 and the memory-side cache.
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
   // the base is wave-uniform by construction; say so, so that it always lands
   // in an SGPR pair (free when the compiler already knows)
@@ -379,7 +379,7 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
 }
 
 // Wait until only the loads of the `after` most recent tiles (kPerTile per
-// wave each) are in flight, then barrier.  Tiles past the split issue no
+// wave each) are in flight, then barrier.  Tiles past the chunk issue no
 // loads, so near the end fewer tiles are in flight and the count drops with
 // them.  A count above the counter's range waits for a few loads more.
 template <int kPerTile>
@@ -453,7 +453,7 @@ stripe_attn_kernel(Params p) {
   const int ntiles = row_hi > row_lo ? (row_hi - row_lo + kTile - 1) / kTile : 0;
   const int row0 = mg * 32 * RB;       // first query row of this workgroup
 
-  // ---- QK wave: its query row and the row's visible limit inside the split
+  // ---- QK wave: its query row and the row's visible limit inside the chunk
   const int R = row0 + wave * 32 + n;
   const bool valid = qk_wave && R < p.M;
   const int t = valid ? R / p.H : 0;
@@ -478,7 +478,7 @@ stripe_attn_kernel(Params p) {
   const char* zero = reinterpret_cast<const char*>(g_zero_row);
   const int32_t* bt_row = rk.bt + (int64_t)b * rk.bt_cols;
 
-  // ---- page table of the split, one page id per lane, 64 pages at a time
+  // ---- page table of the chunk, one page id per lane, 64 pages at a time
   // (page-aligned tiles only: a tile lies inside one page)
   int32_t pt_base = kAligned ? row_lo / p.P : 0;
   int32_t vpt = -1;
@@ -496,7 +496,7 @@ stripe_attn_kernel(Params p) {
   auto tile_base_of = [&](int it) -> const char* {
     const int32_t J = row_lo + it * kTile;
     const int32_t pi = J / p.P;
-    if (pi - pt_base >= 64) load_page_table(pi);    // rare: long splits cross 64 pages
+    if (pi - pt_base >= 64) load_page_table(pi);    // rare: long chunks cross 64 pages
     const int32_t pg = __builtin_amdgcn_readlane(vpt, pi - pt_base);
     if (pg < 0 || pg >= rk.num_pages) {
       if (lane == 0) flag_range(p.status);
@@ -513,7 +513,7 @@ stripe_attn_kernel(Params p) {
     const int s0 = 64 * j;
     return s0 < kLastBase ? s0 : kLastBase;
   };
-  // A tile is "fast" when it is page-aligned and all 32 rows lie in the split:
+  // A tile is "fast" when it is page-aligned and all 32 rows lie in the chunk:
   // its 32 rows are 36,864 contiguous bytes, so slot s of the padded LDS tile
   // (row s / 73, chunk s % 73) takes global chunk s - s / 73 of the tile; the
   // pad chunks fetch a neighbouring chunk of the same tile, never read from LDS.
@@ -530,7 +530,7 @@ stripe_attn_kernel(Params p) {
   // tile and sparse selections.  Lane l < 32 first finds the address of the
   // tile's row l (one round of dependent loads for the whole tile); each slot
   // then takes its row's address from that lane.  A slot that holds no token
-  // of the split (rows past the split end) loads a chunk of the tile's first
+  // of the chunk (rows past the chunk end) loads a 16-byte piece of the tile's first
   // row instead, and the pad chunk loads chunk 71 of its row: finite data
   // that the softmax masks to weight zero (or that is never read), so no
   // stale, unowned or NaN row reaches the MFMAs.  A row whose page is out of
@@ -701,7 +701,7 @@ stripe_attn_kernel(Params p) {
       l_run += psum;
     }
   };
-  // Softmax of one whole tile (split-role waves).  After the split's first
+  // Softmax of one whole tile (split-role waves).  After the chunk's first
   // tile every row that sees the whole tile has a finite reference within 2^8
   // of its running max, so such a tile is first weighted against the current
   // reference: when no lane's sum of weights exceeds 2^8 (every weight is
