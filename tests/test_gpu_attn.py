@@ -347,3 +347,63 @@ def test_multi_rank_launch_equals_per_rank_calls(name, I, lens, extra):
     mo2, ml2 = dcp.dcp_lse_merge(mo, ml, s.base_flag)
     for b in range(w.B):
         H.check_request(s, mo, ml, mo2, ml2, b, sinks=sinks, sink_rank=N - 1, **var)
+
+
+@pytest.mark.parametrize("mode", ["splits", "parts", "sparse"])
+def test_multi_rank_launch_other_modes(mode):
+    # forced chunk counts, unmerged parts and sparse selections through the
+    # one-launch path, against the per-rank calls
+    w, lens = custom(3, 64, 2, 4, 64, [1500, 40, 700], "e")
+    print(f"multi mode {mode}", flush=True)
+    s = H.make_setup(w, 1, lens=lens)
+    dev = s.q.device
+    N = s.lay.n_stripes
+    kw = {}
+    k = 3
+    if mode == "splits":
+        kw = dict(num_splits=k)
+    elif mode == "parts":
+        kw = dict(num_splits=k, partials=True)
+    plans = None
+    if mode == "sparse":
+        rng = np.random.default_rng(9)
+        K = 100
+        topk = np.full((w.B, w.q_len, K), -1, dtype=np.int32)
+        for b in range(w.B):
+            for t in range(w.q_len):
+                vis = int(lens[b]) - w.q_len + t + 1
+                n = min(K, vis)
+                topk[b, t, :n] = rng.choice(vis, size=n, replace=False)
+        topk_d = torch.from_numpy(topk).to(dev)
+        plans = [dcp.dcp_sparse_plan(s.lay, r, topk_d, s.sp.seq_len) for r in range(N)]
+    lead = (k,) if mode == "parts" else ()
+    per_o = torch.empty((N,) + lead + (w.B, w.q_len, w.H, workloads.V_DIM), dtype=torch.float32, device=dev)
+    per_l = torch.empty((N,) + lead + (w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    for r in range(N):
+        dcp.dcp_stripe_attn(s.lay, r, s.q, s.sp.pools[r], s.sp.tables[r], s.sp.seq_len, workloads.SCALE,
+                            s.base_flag, o=per_o[r], lse=per_l[r], status=s.status,
+                            sparse=None if plans is None else plans[r], **kw)
+    if mode == "parts":
+        # the binding's multi call returns merged-shape outputs; build the part-shaped ones here
+        mo = torch.empty_like(per_o)
+        ml = torch.empty_like(per_l)
+        arr = (dcp.dcp_attn_args * N)()
+        for r in range(N):
+            a = dcp._attn_args(s.lay, r, s.q, s.sp.pools[r], s.sp.tables[r], s.sp.seq_len, workloads.SCALE,
+                               s.base_flag, k, None, None, None, None, 0, 0.0, 1)
+            a.q, a.pool, a.block_table, a.seq_len = (s.q.data_ptr(), s.sp.pools[r].data_ptr(),
+                                                     s.sp.tables[r].data_ptr(), s.sp.seq_len.data_ptr())
+            a.o, a.lse, a.status = mo[r].data_ptr(), ml[r].data_ptr(), s.status.data_ptr()
+            arr[r] = a
+        assert dcp.lib().dcp_stripe_attn_multi(arr, N, torch.cuda.current_stream().cuda_stream) == 0
+    else:
+        mo, ml = dcp.dcp_stripe_attn_multi(s.lay, list(range(N)), s.q, s.sp.pools, s.sp.tables, s.sp.seq_len,
+                                           workloads.SCALE, s.base_flag, status=s.status,
+                                           num_splits=kw.get("num_splits", 0), sparse=plans)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    H.assert_o_close(mo.cpu().numpy(), per_o.cpu().numpy(), f"multi {mode} o")
+    H.assert_lse_close(ml.cpu().numpy(), per_l.cpu().numpy(), f"multi {mode} lse")
+    if mode == "splits":
+        # a fixed split count gives the same chunks in both paths: bitwise equal
+        assert torch.equal(mo, per_o) and torch.equal(ml, per_l)
