@@ -292,7 +292,7 @@ int dcp_sparse_plan(dcp_layout layout, int32_t rank, int32_t batch, int32_t q_le
  * dcp_merge_heads -- recv [N][rows][v_dim + 4] (device; block r came from rank
  *   r, rows = B * q_len * H/N records) -> o [rows][v_dim] fp32, lse [rows] fp32
  *   (nullable), the exact merge in lse_base (that of the packed lse).  Parts
- *   with lse = -inf have zero weight and are not read. */
+ *   with lse = -inf have zero weight and do not enter the result. */
 int dcp_pack_heads(int32_t n_stripes, int64_t rows, int32_t n_heads, int32_t v_dim,
                    const float* o_r, const float* lse_r, void* send, void* stream);
 int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* recv,

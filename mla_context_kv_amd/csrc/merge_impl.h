@@ -8,7 +8,9 @@
 //
 // With m = max_r lse_r: w_r = base^(lse_r - m), o = sum_r w_r o_r / sum_r w_r,
 // lse = m + log_base(sum_r w_r).  Parts with lse = -inf have weight zero and
-// their o is never read; if all parts are empty, o = 0 and lse = -inf.
+// their o does not enter the result, whatever it holds (up to 8 parts it is
+// read and selected away, above that it is not read); if all parts are
+// empty, o = 0 and lse = -inf.
 //
 // HBM-bound: per row it reads N lse values and N*v_dim floats once and
 // writes v_dim + 1 floats, with 16-byte coalesced accesses.
@@ -111,6 +113,61 @@ __device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src,
   }
 }
 
+// The same merge for at most kMax parts and v4 <= 128, with every load in
+// flight at once: lane k < n holds part k's lse, and each lane loads its two
+// 16-byte column slices of every part before the max is known.  One memory
+// round trip instead of two.  A part of weight zero is read but selected
+// away (never multiplied in), so whatever its buffer holds -- an empty
+// stripe's unwritten output, NaN -- does not reach the result.
+template <int kMax, class Src>
+__device__ __forceinline__ void merge_row_at_once(int32_t N, int32_t v4, const Src& src, int32_t in_base2,
+                                                  int32_t out_base2, float4* __restrict__ o_row,
+                                                  float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int c0 = lane, c1 = 64 + lane;
+  const bool in0 = c0 < v4, in1 = c1 < v4;
+  const float x = lane < N ? src.lse(lane) : -INFINITY;
+  float4 a[kMax], b[kMax];
+#pragma unroll
+  for (int k = 0; k < kMax; ++k) {
+    a[k] = b[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < N) {
+      if (in0) a[k] = src.o4(k, c0);
+      if (in1) b[k] = src.o4(k, c1);
+    }
+  }
+  const float to2 = in_base2 ? 1.0f : kLog2e;
+  const float m = wave_max(x);
+  if (m == -INFINITY) {
+    if (in0) o_row[c0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (in1) o_row[c1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse_out && lane == 0) *lse_out = -INFINITY;
+    return;
+  }
+  const float e = x == -INFINITY ? 0.f : exp2f((x - m) * to2);
+  const float wsum = wave_sum(e);
+  const float w = e / wsum;
+  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0;
+#pragma unroll
+  for (int k = 0; k < kMax; ++k) {
+    if (k < N) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+      if (wk != 0.f) {
+        r0.x += wk * a[k].x; r0.y += wk * a[k].y; r0.z += wk * a[k].z; r0.w += wk * a[k].w;
+        r1.x += wk * b[k].x; r1.y += wk * b[k].y; r1.z += wk * b[k].z; r1.w += wk * b[k].w;
+      }
+    }
+  }
+  if (in0) o_row[c0] = r0;
+  if (in1) o_row[c1] = r1;
+  if (lse_out && lane == 0) {
+    const float lw2 = log2f(wsum);
+    const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
+    *lse_out = m_out + (out_base2 ? lw2 : lw2 * kLn2);
+  }
+}
+constexpr int kAtOnceParts = 8;
+
 // fp32 parts: part r of the row at o_parts[r * stride * v4 ...], lse at
 // lse_parts[r * stride]
 struct Fp32Parts {
@@ -127,7 +184,11 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
                                               const float* __restrict__ lse_parts, int32_t in_base2,
                                               int32_t out_base2, float4* __restrict__ o_row,
                                               float* __restrict__ lse_out) {
-  merge_row(N, v4, Fp32Parts{o_parts, lse_parts, stride, v4}, in_base2, out_base2, o_row, lse_out);
+  const Fp32Parts src{o_parts, lse_parts, stride, v4};
+  if (N <= kAtOnceParts && v4 <= 128)
+    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, o_row, lse_out);
+  else
+    merge_row(N, v4, src, in_base2, out_base2, o_row, lse_out);
 }
 
 // Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at

@@ -1058,52 +1058,6 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
   return DCP_OK;
 }
 
-// Merge of the n <= kSpecParts chunk partials of one row, every load issued
-// at once: the lse of each part (lane k < n holds part k's) and the lane's two
-// 16-byte column slices of every part.  The chunk partials are always written
-// (an empty chunk writes o = 0, lse = -inf), so reading a part of weight zero
-// is harmless: one memory round trip instead of two.
-constexpr int kSpecParts = 8;
-__device__ __forceinline__ void merge_chunks_at_once(int32_t n, int64_t stride, const float4* __restrict__ o_parts,
-                                                     const float* __restrict__ lse_parts, int32_t out_base2,
-                                                     float4* __restrict__ o_row, float* __restrict__ lse_out) {
-  constexpr int v4 = kDV / 4;                       // 128: two slices per lane
-  const int lane = threadIdx.x & 63;
-  const float x = lane < n ? lse_parts[(int64_t)lane * stride] : -INFINITY;
-  float4 a[kSpecParts], b[kSpecParts];
-#pragma unroll
-  for (int k = 0; k < kSpecParts; ++k) {
-    if (k < n) {
-      a[k] = o_parts[(int64_t)k * stride * v4 + lane];
-      b[k] = o_parts[(int64_t)k * stride * v4 + 64 + lane];
-    }
-  }
-  const float m = wave_max(x);
-  if (m == -INFINITY) {
-    o_row[lane] = o_row[64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane == 0) *lse_out = -INFINITY;
-    return;
-  }
-  const float e = x == -INFINITY ? 0.f : exp2f(x - m);
-  const float wsum = wave_sum(e);
-  const float w = e / wsum;
-  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0;
-#pragma unroll
-  for (int k = 0; k < kSpecParts; ++k) {
-    if (k < n) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-      r0.x += wk * a[k].x; r0.y += wk * a[k].y; r0.z += wk * a[k].z; r0.w += wk * a[k].w;
-      r1.x += wk * b[k].x; r1.y += wk * b[k].y; r1.z += wk * b[k].z; r1.w += wk * b[k].w;
-    }
-  }
-  o_row[lane] = r0;
-  o_row[64 + lane] = r1;
-  if (lane == 0) {
-    const float l2 = m + log2f(wsum);
-    *lse_out = out_base2 ? l2 : l2 * kLn2;
-  }
-}
-
 // Merge of each request's chunks (one wavefront per output row): requests cut
 // into one chunk were written by the attention kernel itself and are left
 // alone; the chunks partition the request's rows, so their partials merge
@@ -1123,13 +1077,8 @@ chunk_combine_kernel(Params p) {
   const RankPtrs& rk = p.rk[ri];
   constexpr int v4 = kDV / 4;
   const int64_t out = (int64_t)b * p.M + m;
-  const float4* parts = reinterpret_cast<const float4*>(p.ws_o) + (c0 * p.M + m) * v4;
-  if (n <= kSpecParts)
-    merge_chunks_at_once(n, p.M, parts, p.ws_lse + c0 * p.M + m, p.out_base2,
-                         reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
-  else
-    merge_one_row(n, p.M, v4, parts, p.ws_lse + c0 * p.M + m, 1, p.out_base2,
-                  reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
+  merge_one_row(n, p.M, v4, reinterpret_cast<const float4*>(p.ws_o) + (c0 * p.M + m) * v4, p.ws_lse + c0 * p.M + m,
+                1, p.out_base2, reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
 }
 
 template <int RB, bool kLogit>
