@@ -200,20 +200,23 @@ __device__ __forceinline__ int32_t wave_max_i(int32_t v) {
 }
 __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-// Work list of one stripe call.  Request b's local rows (what its last query
+// Work list of one launch.  Request b's local rows (what its last query
 // sees, from the first row its first query's window reaches, aligned down to
-// a tile) make tiles_b tiles of 32; the request is cut into n_b >= 1 chunks of
-// cs_b = ceil(tiles_b / n_b) tiles (an empty request gets one empty chunk,
-// which writes its zero output).  Requests of all the ranks of a launch are
-// listed rank by rank (request v = request v % B of rank slot v / B).  With
-// forced_splits = s: n_b = number of
-// chunks of ceil(tiles_b / s) tiles.  Otherwise the chunks are balanced over
-// the whole batch: n_b = ceil(tiles_b / C) for the smallest of a few
-// candidate chunk lengths C that keeps the total under target_chunks (the
-// last candidate, ceil(total / (target - B)), always does).  Chunks are
-// numbered request by request; chunk c is this workgroup's (every wave finds
-// it with wave-wide scans; the workgroup of chunk 0 also writes the table the
-// chunk combine reads).
+// a tile; or its selected entries) make tiles_b tiles of 32; the request is
+// cut into n_b >= 1 chunks of cs_b = ceil(tiles_b / n_b) tiles (an empty
+// request gets one empty chunk, which writes its zero output).  Requests of
+// all the ranks of a launch are listed rank by rank (request v = request
+// v % B of rank slot v / B).  With forced_splits = s: n_b = number of chunks
+// of ceil(tiles_b / s) tiles.  Otherwise the chunks are balanced over the
+// whole batch, n_b = ceil(tiles_b / C):
+//  * fewer requests than target_chunks: C is the smallest of a few candidate
+//    lengths that keeps the total under target_chunks (the last candidate,
+//    ceil(total / (target - B)), always does), so the grid is one round;
+//  * otherwise C = ceil(total / target), the mean share of a compute unit
+//    (capped for row groups), at most target + B chunks.
+// Chunks are numbered request by request; chunk c is this workgroup's (every
+// wave finds it with wave-wide scans; the workgroup of chunk 0 also writes
+// the table the chunk combine reads).
 struct WorkItem {
   int32_t b, k, n, cs, rows;        // request, chunk of it, its chunks, chunk length (tiles), rows
   int32_t ft;                       // the request's first tile
