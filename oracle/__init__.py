@@ -10,7 +10,8 @@ What it computes, and where the pages define it:
 
 * ``layout``    -- which rank owns a global token position, the compact local
   row it is stored at, the per-rank token counts of an interval, and the
-  paged physical slot, and the prefill-to-decode token relayout plan.  The striping is produced by *simulating* the
+  paged physical slot, the prefill-to-decode token relayout plan and a rank's
+  share of a global sparse selection.  The striping is produced by *simulating* the
   round-robin hand-out of tokens (page "DCP", section "core abstraction",
   idea one; page "PCP/DCP", sections 5 and 6), not by the closed forms; the
   closed forms are what the tests pin the simulation against.
@@ -20,7 +21,10 @@ What it computes, and where the pages define it:
   attention restricted to one stripe returning a locally normalised output and
   its log-sum-exp (page "DCP", idea two), and the exact LSE merge (page "DCP",
   "theory": merge identity and max-shifted form; SGLang DCP docs, "MLA decode
-  dataflow").
+  dataflow"); the variants that keep the merge exact (sliding window, logit
+  softcap, attention sink, position bias, sparse attention over a global
+  top-k; page "DCP", conditions for merging) and the packed head-return
+  exchange (page "DCP", "merge: All-to-All").
 
 Every function is pinned by a CPU test against something other than itself:
 values the pages print (``tests/golden``), closed forms, brute force on tiny
