@@ -1,0 +1,22 @@
+"""bench.py's contract that needs no GPU: it measures one GPU and says so."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+
+
+def test_bench_help_lists_the_modes():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0
+    for flag in ("--workload", "--op", "--multi", "--parts", "--topk", "--softcap", "--window", "--sinks"):
+        assert flag in r.stdout
