@@ -46,12 +46,18 @@ def parse():
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unsharded-baseline", action="store_true",
+                    help="time only the oracle's striped attention + merge, not also its unsharded attention")
     ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return"],
                     help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout; "
                          "head-return: pack by head owner + the owners' merges")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="MiB of scratch written between timed steps so the KV is not served from the memory-side "
+                         "cache (-1: 1024 when the workload's KV is under 1 GiB, else 0); with a flush the step time "
+                         "is the mean of the HIP-event step times")
     ap.add_argument("--multi", action="store_true",
                     help="all N stripes in one dcp_stripe_attn_multi launch (then the merge)")
     ap.add_argument("--topk", type=int, default=0,
@@ -249,10 +255,16 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
 
+    flush_mib = args.flush_mib
+    if flush_mib < 0:
+        flush_mib = 1024 if float(lens.sum()) * ROW_BYTES < (1 << 30) else 0
+    scratch = torch.empty((flush_mib << 20) // 4, dtype=torch.float32, device=dev) if flush_mib > 0 else None
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(float(k))              # evicts the KV from the caches, outside the step's events
         step(evs[k])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
@@ -272,6 +284,8 @@ def main():
     merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
     step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
     ms_per_step = wall_s * 1e3 / args.steps
+    if scratch is not None:
+        ms_per_step = float(step_ev_ms.mean())        # the flushes between steps are not step time
 
     # ---- algorithmic work
     local = counts.astype(np.int64)                                  # rows per (request, rank)
@@ -319,6 +333,7 @@ def main():
         except Exception:
             threads = os.cpu_count() or 1
         cpu_s = 0.0
+        full_s = 0.0
         sample_bytes = 0.0
         for qt, kvt, S in sample:
             qb, kvb = qt.double().numpy(), kvt.double().numpy()
@@ -328,11 +343,18 @@ def main():
             OA.lse_merge(np.stack([p[0] for p in parts]), np.stack([OA.to_base(p[1], w.lse_base) for p in parts]),
                          w.lse_base)
             cpu_s += time.perf_counter() - t1
+            if not args.no_unsharded_baseline:
+                t2 = time.perf_counter()
+                OA.full_attention(qb, kvb, S, workloads.SCALE, chunk=65536)      # the unsharded definition
+                full_s += time.perf_counter() - t2
             sample_bytes += S * ROW_BYTES
         cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
                "kind": "oracle", "seconds": round(cpu_s, 3),
                "sample": f"{len(sample)} of {w.B} requests ({int(sum(s[2] for s in sample))} tokens, {w.H} heads, "
                          f"q_len {w.q_len}): all {N} stripe attentions + LSE merge in float64 NumPy"}
+        if full_s > 0:
+            cpu["unsharded_seconds"] = round(full_s, 3)
+            cpu["unsharded_value"] = round(sample_bytes / full_s / 1e9, 4)
 
     out = {
         "metric": "us/decode-step and KV GB/s (% HBM peak) for stripe attn+merge, K3 shape, 1 GPU",
@@ -362,6 +384,9 @@ def main():
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
+        "event_step_us_median": round(float(np.median(step_ev_ms)) * 1e3, 1),
+        "event_step_us_min": round(float(step_ev_ms.min()) * 1e3, 1),
+        "flush_mib_between_steps": flush_mib,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if secondary else measured_traffic(w.name),
