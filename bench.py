@@ -65,6 +65,10 @@ def parse():
                          "on every rank)")
     ap.add_argument("--parts", type=int, default=0,
                     help="k > 0: every rank writes k unmerged parts per request and one merge folds all N*k")
+    ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
+                    help="2: the per-rank calls alternate between two streams, each with its own workspace, so "
+                         "one rank's launch starts on the compute units the previous one leaves idle at its end "
+                         "(the step time then has no per-launch split)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -102,6 +106,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the per-rank stripe kernels of all N stripes and the merge run on a "
               f"single MI355X; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if args.streams > 1 and args.multi:
+        print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -175,7 +182,8 @@ def main():
         need = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_multi_workspace(multi_arr, N, ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspaces = [torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) for _ in range(args.streams)]
+    streams = [stream] + [torch.cuda.Stream(dev) for _ in range(args.streams - 1)]   # default priority
     plans = None
     if args.topk > 0:
         # a global selection: k distinct visible positions per query token
@@ -203,7 +211,8 @@ def main():
         a.sinks = sinks.data_ptr() if sinks is not None and r == N - 1 else None
         a.q, a.pool = q.data_ptr(), sp.pools[r].data_ptr()
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        ws_r = workspaces[r % args.streams]
+        a.workspace, a.workspace_bytes = ws_r.data_ptr(), ws_r.numel()
         a.o, a.lse, a.status = o_parts[r * K].data_ptr(), lse_parts[r * K].data_ptr(), status.data_ptr()
     refs = [ctypes.byref(a) for a in attn_args]
     if multi_arr is not None:
@@ -229,18 +238,32 @@ def main():
             if events is not None:
                 events[N + 1].record(stream)
             return
-        for r in range(N):
+        two = len(streams) > 1
+        if two:
             if events is not None:
+                events[0].record(stream)
+            # fork: the second stream starts after everything queued before the step
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            streams[1].wait_event(fork)
+        for r in range(N):
+            s_r = streams[r % len(streams)]
+            sh_r = s_r.cuda_stream
+            if events is not None and not two:
                 events[r].record(stream)
             if plans is not None:
                 rc = L.dcp_sparse_plan(lay, r, w.B, w.q_len, args.topk, topk.data_ptr(), sp.seq_len.data_ptr(),
                                        plans[r][0].data_ptr(), plans[r][1].data_ptr(), plans[r][2].data_ptr(),
-                                       int(plans[r][0].shape[1]), sh)
+                                       int(plans[r][0].shape[1]), sh_r)
                 if rc != 0:
                     raise RuntimeError(f"dcp_sparse_plan: {dcp.strerror(rc)}")
-            rc = L.dcp_stripe_attn(refs[r], sh)
+            rc = L.dcp_stripe_attn(refs[r], sh_r)
             if rc != 0:
                 raise RuntimeError(f"dcp_stripe_attn: {dcp.strerror(rc)}")
+        if two:
+            join = torch.cuda.Event()
+            join.record(streams[1])
+            stream.wait_event(join)
         if events is not None:
             events[N].record(stream)
         rc = L.dcp_lse_merge(*merge_call)
@@ -280,7 +303,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+    if args.streams > 1:
+        # overlapping calls have no per-launch span: the stripe part of the step over N
+        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / N] * N for k in range(args.steps)])
+    else:
+        per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
     merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
     step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
     ms_per_step = wall_s * 1e3 / args.steps
@@ -322,7 +349,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
-                     or args.multi)
+                     or args.multi or args.streams > 1)
     cpu = None
     if sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk):
         from oracle import attention as OA
@@ -380,7 +407,8 @@ def main():
                       if (args.window or args.softcap or args.sinks) else {}),
                    **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {}),
                    **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {}),
-                   **({"one_launch_for_all_stripes": True} if args.multi else {})},
+                   **({"one_launch_for_all_stripes": True} if args.multi else {}),
+                   **({"streams": args.streams} if args.streams > 1 else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
@@ -392,7 +420,9 @@ def main():
                      "traffic": None if secondary else measured_traffic(w.name),
                      "kernel": ("one dcp_stripe_attn_multi launch: all stripes" if args.multi else
                                 (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
-                                 if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")),
+                                 if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")
+                                + (" (two streams: the step's stripe time over N, calls overlapping)"
+                                   if args.streams > 1 else "")),
                      "bytes_per_launch": int(stripe_bytes.sum() if args.multi else stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

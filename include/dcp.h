@@ -178,7 +178,9 @@ int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim,
  *             and the chunk table; a second kernel on the same stream merges
  *             the chunks of every request that has more than one.  Its
  *             contents need no initialisation.  Calls that overlap in time
- *             must not share a workspace.
+ *             must not share a workspace; with a workspace each, calls on
+ *             different streams may run at the same time (the library keeps
+ *             no other state between calls).
  * o    [B][q_len][H][v_dim] fp32 device out: o_r, normalised inside the stripe.
  * lse  [B][q_len][H] fp32 device out: lse_r in the chosen base.
  *      A query with no visible row in this stripe gets o = 0, lse = -inf

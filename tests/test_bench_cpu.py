@@ -18,5 +18,13 @@ def test_bench_help_lists_the_modes():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0
-    for flag in ("--workload", "--op", "--multi", "--parts", "--topk", "--softcap", "--window", "--sinks"):
+    for flag in ("--workload", "--op", "--multi", "--parts", "--topk", "--softcap", "--window", "--sinks",
+                 "--streams"):
         assert flag in r.stdout
+
+
+def test_two_streams_with_one_launch_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--streams", "2", "--multi"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--multi" in r.stderr
