@@ -16,7 +16,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("base", ["e", "2"])
-@pytest.mark.parametrize("N,rows,V", [(8, 6144, 512), (4, 37, 512), (1, 100, 512), (3, 5, 16), (16, 257, 512)])
+# part counts cover both merge bodies: up to 8 parts with every load at once, above that the generic body
+# (partial groups of 8, narrow rows, more parts than lanes)
+@pytest.mark.parametrize("N,rows,V", [(8, 6144, 512), (4, 37, 512), (1, 100, 512), (3, 5, 16), (16, 257, 512),
+                                      (9, 130, 512), (24, 64, 512), (32, 257, 512), (64, 64, 512), (20, 50, 16),
+                                      (65, 40, 512), (100, 33, 512)])
 def test_merge_matches_oracle(base, N, rows, V):
     dev = H.device()
     rng = np.random.default_rng(N * 1000 + rows)
@@ -74,7 +78,8 @@ def test_pack_heads_bit_exact(N, rows, H_, V):
 
 
 @pytest.mark.parametrize("base", ["e", "2"])
-@pytest.mark.parametrize("N,rows,V", [(8, 768, 512), (4, 37, 512), (3, 5, 16)])
+@pytest.mark.parametrize("N,rows,V", [(8, 768, 512), (4, 37, 512), (3, 5, 16), (16, 100, 512), (32, 40, 512),
+                                      (12, 9, 16), (72, 6, 512)])
 def test_merge_heads_matches_oracle(base, N, rows, V):
     dev = H.device()
     rng = np.random.default_rng(N + rows)
