@@ -69,6 +69,9 @@ def parse():
                     help="2: the per-rank calls alternate between two streams, each with its own workspace, so "
                          "one rank's launch starts on the compute units the previous one leaves idle at its end "
                          "(the step time then has no per-launch split)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (every call of it) in a HIP graph and time its replays (the step time "
+                         "then has no per-launch split)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -109,6 +112,9 @@ def main():
         sys.exit(2)
     if args.streams > 1 and args.multi:
         print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
+        sys.exit(2)
+    if args.graph and args.streams > 1:
+        print("--graph captures the one-stream step; it does not take --streams 2", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -222,7 +228,7 @@ def main():
     rows = w.B * M
     merge_call = (N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
 
-    def step(events=None):
+    def step(events=None, sh=sh):
         if multi_arr is not None:
             if events is not None:
                 events[0].record(stream)
@@ -232,7 +238,7 @@ def main():
             if events is not None:
                 for r in range(1, N + 1):
                     events[r].record(stream)
-            rc = L.dcp_lse_merge(*merge_call)
+            rc = L.dcp_lse_merge(*merge_call[:-1], sh)
             if rc != 0:
                 raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
             if events is not None:
@@ -247,8 +253,7 @@ def main():
             fork.record(stream)
             streams[1].wait_event(fork)
         for r in range(N):
-            s_r = streams[r % len(streams)]
-            sh_r = s_r.cuda_stream
+            sh_r = streams[r % len(streams)].cuda_stream if two else sh
             if events is not None and not two:
                 events[r].record(stream)
             if plans is not None:
@@ -266,7 +271,7 @@ def main():
             stream.wait_event(join)
         if events is not None:
             events[N].record(stream)
-        rc = L.dcp_lse_merge(*merge_call)
+        rc = L.dcp_lse_merge(*merge_call[:-1], sh)
         if rc != 0:
             raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
         if events is not None:
@@ -277,6 +282,19 @@ def main():
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
+    graph = None
+    if args.graph:
+        # every call of one step as one graph (the library allocates, clears
+        # and synchronises nothing inside a call); replays run on `stream`
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            step(sh=cap.cuda_stream)
+        stream.wait_stream(cap)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
 
     flush_mib = args.flush_mib
     if flush_mib < 0:
@@ -288,7 +306,13 @@ def main():
     for k in range(args.steps):
         if scratch is not None:
             scratch.fill_(float(k))              # evicts the KV from the caches, outside the step's events
-        step(evs[k])
+        if graph is not None:
+            evs[k][0].record(stream)
+            graph.replay()
+            evs[k][N].record(stream)
+            evs[k][N + 1].record(stream)
+        else:
+            step(evs[k])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
 
@@ -303,8 +327,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.streams > 1:
-        # overlapping calls have no per-launch span: the stripe part of the step over N
+    if args.streams > 1 or args.graph:
+        # overlapping calls, or one graph, have no per-launch span: the stripe part of the step over N
         per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / N] * N for k in range(args.steps)])
     else:
         per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
@@ -349,7 +373,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
-                     or args.multi or args.streams > 1)
+                     or args.multi or args.streams > 1 or args.graph)
     cpu = None
     if sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk):
         from oracle import attention as OA
@@ -408,7 +432,8 @@ def main():
                    **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {}),
                    **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {}),
                    **({"one_launch_for_all_stripes": True} if args.multi else {}),
-                   **({"streams": args.streams} if args.streams > 1 else {})},
+                   **({"streams": args.streams} if args.streams > 1 else {}),
+                   **({"hip_graph": True} if args.graph else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
         "merge_us": round(float(merge_ms.mean()) * 1e3, 1),
         "event_step_us": round(float(step_ev_ms.mean()) * 1e3, 1),
@@ -422,7 +447,9 @@ def main():
                                 (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
                                  if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")
                                 + (" (two streams: the step's stripe time over N, calls overlapping)"
-                                   if args.streams > 1 else "")),
+                                   if args.streams > 1 else "")
+                                + (" (one HIP graph per step: the step's time, merge included, over N)"
+                                   if args.graph else "")),
                      "bytes_per_launch": int(stripe_bytes.sum() if args.multi else stripe_bytes.mean())},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

@@ -19,7 +19,7 @@ def test_bench_help_lists_the_modes():
                        timeout=300)
     assert r.returncode == 0
     for flag in ("--workload", "--op", "--multi", "--parts", "--topk", "--softcap", "--window", "--sinks",
-                 "--streams"):
+                 "--streams", "--graph"):
         assert flag in r.stdout
 
 
@@ -28,3 +28,10 @@ def test_two_streams_with_one_launch_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "--multi" in r.stderr
+
+
+def test_graph_with_two_streams_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--graph", "--streams", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--graph" in r.stderr
