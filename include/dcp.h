@@ -16,7 +16,9 @@
  *    library never allocates or frees memory and keeps no state between calls.
  *  - bfloat16 data is passed as raw 16-bit storage (void*).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on `stream` and returns; nothing is synchronised.
+ *    enqueues kernel launches on `stream` and returns; nothing is
+ *    synchronised, and no call copies or clears memory with a runtime call,
+ *    so a sequence of calls can be captured into a HIP graph and replayed.
  *  - Return value: DCP_OK, or a negative error code.  On any error return
  *    nothing has been enqueued.  Argument errors (DCP_EINVAL,
  *    DCP_EUNSUPPORTED) are detected on the host before any HIP call.
