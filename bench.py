@@ -329,7 +329,9 @@ def main():
 
     if args.streams > 1 or args.graph:
         # overlapping calls, or one graph, have no per-launch span: the stripe part of the step over N
-        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / N] * N for k in range(args.steps)])
+        # (one launch of all stripes: the whole span is that launch's)
+        div = 1 if args.multi else N
+        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / div] * N for k in range(args.steps)])
     else:
         per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
     merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
@@ -443,7 +445,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if secondary else measured_traffic(w.name),
-                     "kernel": ("one dcp_stripe_attn_multi launch: all stripes" if args.multi else
+                     "kernel": ("one dcp_stripe_attn_multi launch: all stripes"
+                                + (" (in one HIP graph with the merge: the step's time)" if args.graph else "")
+                                if args.multi else
                                 (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
                                  if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")
                                 + (" (two streams: the step's stripe time over N, calls overlapping)"
