@@ -35,3 +35,15 @@ def test_graph_with_two_streams_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "--graph" in r.stderr
+
+
+def test_hbm_traffic_record_matches_the_kernel_sources():
+    # the headline's measured HBM bytes are reported only while the kernel
+    # sources are the ones the counters were taken on: a kernel change needs
+    # a fresh pair of FETCH_SIZE / WRITE_SIZE passes and a new record
+    sys.path.insert(0, ROOT)
+    import bench
+    got = bench.measured_traffic("k3")
+    assert got is not None, "profiles/stripe_attn_k3_hbm_bytes.md does not match the current kernel sources"
+    assert 1.0e9 < got < 1.5e9                     # one K3 stripe call: 1.21 GB of KV plus partials
+    assert bench.measured_traffic("dsv3") is None  # the record covers the workload it was taken on only
