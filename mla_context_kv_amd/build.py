@@ -71,7 +71,28 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_abi_client(verbose)
     return LIB
+
+
+ABI_CLIENT_SRC = os.path.join(ROOT, "tests", "abi_client.c")
+ABI_CLIENT = os.path.join(ROOT, "tests", "abi_client")
+
+
+def build_abi_client(verbose: bool = True) -> str:
+    """Compile the plain C client of the C ABI (host code only: gcc against
+    the HIP runtime and libdcp.so, found through its run path)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-O2", "-Wall", "-std=c11", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           f"-I{INCLUDE}", ABI_CLIENT_SRC, "-o", ABI_CLIENT,
+           f"-L{rocm}/lib", "-lamdhip64", f"-L{PKG}", "-ldcp", f"-Wl,-rpath,{rocm}/lib",
+           "-Wl,-rpath,$ORIGIN/../mla_context_kv_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling the C ABI client failed:\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {ABI_CLIENT}")
+    return ABI_CLIENT
 
 
 if __name__ == "__main__":
