@@ -83,6 +83,17 @@ def parse():
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md")
 
 
+def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1):
+    """Algorithmic bytes of each rank's dcp_stripe_attn call: its latent rows
+    (local_rows [B, N]: rows of request b on rank r, each read once), the
+    queries (B x M rows of 576 bf16) and its outputs (o_r fp32 x 512 and lse_r,
+    or `parts` unmerged parts of them).  Returns one value per rank."""
+    local_rows = np.asarray(local_rows, dtype=np.int64)
+    q_bytes = B * M * ROW_BYTES
+    out_bytes = parts * B * M * (512 + 1) * 4
+    return local_rows.sum(axis=0) * ROW_BYTES + q_bytes + out_bytes
+
+
 def measured_traffic(workload: str):
     """HBM bytes of one dcp_stripe_attn call from the committed counter record,
     or None when there is none for this workload or the kernel sources changed
@@ -364,7 +375,7 @@ def main():
     kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: one stripe-attention launch (its algorithmic bytes: the
     # stripe's latent rows, the queries, and its (o_r, lse_r))
-    stripe_bytes = local.sum(axis=0) * ROW_BYTES + q_bytes + part_bytes          # per rank
+    stripe_bytes = stripe_call_bytes(local, w.B, M, K)                            # per rank
     launch_ms = per_stripe_ms.mean(axis=0)                                        # per rank
     if args.multi:
         # one launch for all stripes: its bytes over its duration

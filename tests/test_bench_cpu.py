@@ -47,3 +47,22 @@ def test_hbm_traffic_record_matches_the_kernel_sources():
     assert got is not None, "profiles/stripe_attn_k3_hbm_bytes.md does not match the current kernel sources"
     assert 1.0e9 < got < 1.5e9                     # one K3 stripe call: 1.21 GB of KV plus partials
     assert bench.measured_traffic("dsv3") is None  # the record covers the workload it was taken on only
+
+
+def test_k3_call_bytes_from_the_oracle_counts():
+    # the roofline numerator: per rank, the rows the oracle's striping hands
+    # that rank (every K3 request has 131072 tokens, 8 stripes), the queries
+    # and the outputs; the K3 mean is the figure the traffic record compares to
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from oracle import layout as OL
+    B, S, N, H = 64, 131072, 8, 96
+    per_req = OL.local_counts(S, N, 1)                       # rows of one request on each rank
+    local = np.tile(np.asarray(per_req, dtype=np.int64), (B, 1))
+    got = bench.stripe_call_bytes(local, B, H)
+    assert list(per_req) == [S // N] * N
+    expect = B * (S // N) * 1152 + B * H * 1152 + B * H * 513 * 4
+    assert (got == expect).all() and int(got.mean()) == 1227644928
+    # four unmerged parts per request write four times the outputs
+    assert (bench.stripe_call_bytes(local, B, H, 4) - got == 3 * B * H * 513 * 4).all()
