@@ -48,9 +48,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unsharded-baseline", action="store_true",
                     help="time only the oracle's striped attention + merge, not also its unsharded attention")
-    ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return"],
+    ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return", "stream"],
                     help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout; "
-                         "head-return: pack by head owner + the owners' merges")
+                         "head-return: pack by head owner + the owners' merges; stream: the streaming-read probe "
+                         "(measured HBM read peak) in every load mode")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="step: skip the streaming-read probe that gives the measured HBM peak")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the step (0 = none)")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (on the last rank)")
@@ -139,6 +142,9 @@ def main():
         return
     if args.op == "head-return":
         run_head_return(args)
+        return
+    if args.op == "stream":
+        run_stream(args)
         return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
@@ -387,38 +393,22 @@ def main():
 
     secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
                      or args.multi or args.streams > 1 or args.graph)
+    # ---- measured HBM read peak: the streaming-read probe over the same pools,
+    # one launch per stripe's pool, in the step's back-to-back pattern
+    probe = None
+    if not args.no_probe:
+        probe = probe_pools(args, sp.pools, N, stream, dev)
+
+    # ---- parity of the last timed step's outputs against the oracle
+    check = sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk)
     cpu = None
-    if sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk):
-        from oracle import attention as OA
-        from oracle import layout as OL
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-        except Exception:
-            threads = os.cpu_count() or 1
-        cpu_s = 0.0
-        full_s = 0.0
-        sample_bytes = 0.0
-        for qt, kvt, S in sample:
-            qb, kvb = qt.double().numpy(), kvt.double().numpy()
-            t1 = time.perf_counter()
-            lists = OL.stripe_positions(S, N, I)
-            parts = [OA.stripe_attention(qb, kvb, S, lists[r], workloads.SCALE, chunk=65536) for r in range(N)]
-            OA.lse_merge(np.stack([p[0] for p in parts]), np.stack([OA.to_base(p[1], w.lse_base) for p in parts]),
-                         w.lse_base)
-            cpu_s += time.perf_counter() - t1
-            if not args.no_unsharded_baseline:
-                t2 = time.perf_counter()
-                OA.full_attention(qb, kvb, S, workloads.SCALE, chunk=65536)      # the unsharded definition
-                full_s += time.perf_counter() - t2
-            sample_bytes += S * ROW_BYTES
-        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-               "kind": "oracle", "seconds": round(cpu_s, 3),
-               "sample": f"{len(sample)} of {w.B} requests ({int(sum(s[2] for s in sample))} tokens, {w.H} heads, "
-                         f"q_len {w.q_len}): all {N} stripe attentions + LSE merge in float64 NumPy"}
-        if full_s > 0:
-            cpu["unsharded_seconds"] = round(full_s, 3)
-            cpu["unsharded_value"] = round(sample_bytes / full_s / 1e9, 4)
+    parity = None
+    if check:
+        host_out = (o.cpu().numpy(), lse.cpu().numpy(), o_parts.cpu().numpy(), lse_parts.cpu().numpy())
+        slot_bad = slot_map_mismatches(lay, lens[:len(sample)], sp.tables, N, I, P, dev)
+        cpu, parity = cpu_oracle_leg(args, w, sample, N, I, host_out)
+        parity["slot_map_mismatches"] = slot_bad
+        parity["ok"] = parity["ok"] and slot_bad == 0
 
     out = {
         "metric": "us/decode-step and KV GB/s (% HBM peak) for stripe attn+merge, K3 shape, 1 GPU",
@@ -467,9 +457,205 @@ def main():
                                    if args.graph else "")),
                      "bytes_per_launch": int(stripe_bytes.sum() if args.multi else stripe_bytes.mean())},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "step_algorithmic_bytes": int(kv_bytes + N * q_bytes + 2 * N * part_bytes + w.B * M * (512 + 1) * 4),
+        "device": device_ids(dev),
         "setup_s": round(setup_s, 1),
     }
+    if probe is not None:
+        peak = probe["hot_gbs"]
+        out["roofline"]["measured_peak"] = round(peak, 1)
+        out["roofline"]["frac_of_measured"] = round(achieved / peak, 4)
+        out["roofline"]["measured_peak_probe"] = probe
     print(json.dumps(out), flush=True)
+    if parity is not None and not parity["ok"]:
+        print("parity check against the oracle FAILED", file=sys.stderr)
+        sys.exit(3)
+
+
+def device_ids(dev):
+    """GPU and software identifiers of the run."""
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "hip_runtime": torch.version.hip, "rocm": rocm, "torch": torch.__version__}
+
+
+def probe_pools(args, pools, N, stream, dev):
+    """The streaming-read probe (16-byte direct-to-LDS non-temporal loads, the
+    stripe kernel's loader without compute) over each stripe's pool, N launches
+    per step like the step's N attention launches, warm-up then timed steps;
+    returns the mean rate of the timed launches and that of the first step."""
+    import torch
+    from mla_context_kv_amd import probe as PR
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    mode = "lds1"
+    grid = PR.grid_for(mode, cus)
+    sink = PR.make_sink(mode, grid, dev)
+    per = pools[0].numel() * pools[0].element_size()
+    sh = stream.cuda_stream
+    for _ in range(args.warmup):
+        for r in range(N):
+            PR.stream(pools[r], per, mode, grid, sink, sh)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    got = 0
+    for k in range(args.steps):
+        for r in range(N):
+            evs[k][r].record(stream)
+            got = PR.stream(pools[r], per, mode, grid, sink, sh)
+        evs[k][N].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+    gbs = got / (ms * 1e-3) / 1e9
+    return {"mode": PR.MODE_NOTES[mode], "bytes_per_launch": got, "launches": int(ms.size),
+            "hot_gbs": float(gbs.mean()), "first_step_gbs": round(float(gbs[0].mean()), 1),
+            "us_per_launch": round(float(ms.mean()) * 1e3, 1)}
+
+
+def slot_map_mismatches(lay, lens, tables, N, I, P, dev):
+    """Positions of the given requests whose (owner, row, slot) from
+    dcp_slot_map differ from the oracle's simulated hand-out, over every rank."""
+    from mla_context_kv_amd import dcp, stripes
+    from oracle import layout as OL
+    pos, req = stripes.positions_and_requests(lens, dev)
+    pos_h, req_h = pos.cpu().numpy(), req.cpu().numpy()
+    bad = 0
+    for r in range(N):
+        own, row, slot = dcp.dcp_slot_map(lay, r, pos, req, tables[r])
+        o_ref, r_ref, s_ref = OL.slot_map(pos_h, req_h, N, I, P, r, tables[r].cpu().numpy())
+        bad += int(((own.cpu().numpy() != o_ref) | (row.cpu().numpy() != r_ref)
+                    | (slot.cpu().numpy() != s_ref)).sum())
+    return bad
+
+
+O_ABS, O_REL, LSE_ABS = 4e-3, 1e-2, 2e-3        # |o - o_ref| <= 4e-3 + 1e-2 |o_ref|, |lse - lse_ref| <= 2e-3
+
+
+def cpu_oracle_leg(args, w, sample, N, I, host_out):
+    """The float64 oracle on the sampled requests, timed on every core of this
+    process's affinity mask (BLAS threads pinned to that count): its striped
+    attention + merge (the timed baseline) and its unsharded attention beside
+    it.  Outside the timed calls, every sampled request's merged (o, lse) and
+    every rank's (o_r, lse_r) from the GPU's last step are checked against the
+    oracle's, elementwise, at the parity bar."""
+    from contextlib import nullcontext
+    from oracle import attention as OA
+    from oracle import layout as OL
+    from mla_context_kv_amd import workloads
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except ImportError:                      # threadpoolctl missing: BLAS keeps its own count
+        limiter = nullcontext()
+    o_g, lse_g, op_g, lp_g = host_out
+    cpu_s = full_s = 0.0
+    sample_bytes = 0.0
+    worst_excess_o = worst_stripe_excess_o = -np.inf
+    worst_abs_o = worst_lse = worst_stripe_lse = 0.0
+    with limiter:
+        for b, (qt, kvt, S) in enumerate(sample):
+            qb, kvb = qt.double().numpy(), kvt.double().numpy()
+            t1 = time.perf_counter()
+            lists = OL.stripe_positions(S, N, I)
+            parts = [OA.stripe_attention(qb, kvb, S, lists[r], workloads.SCALE, chunk=65536) for r in range(N)]
+            o_m, lse_m = OA.lse_merge(np.stack([p[0] for p in parts]),
+                                      np.stack([OA.to_base(p[1], w.lse_base) for p in parts]), w.lse_base)
+            cpu_s += time.perf_counter() - t1
+            if not args.no_unsharded_baseline:
+                t2 = time.perf_counter()
+                OA.full_attention(qb, kvb, S, workloads.SCALE, chunk=65536)      # the unsharded definition
+                full_s += time.perf_counter() - t2
+            sample_bytes += S * ROW_BYTES
+            # parity of this request (not timed)
+            d = np.abs(o_g[b] - o_m)
+            worst_excess_o = max(worst_excess_o, float((d - (O_ABS + O_REL * np.abs(o_m))).max()))
+            worst_abs_o = max(worst_abs_o, float(d.max()))
+            worst_lse = max(worst_lse, float(np.abs(lse_g[b] - lse_m).max()))
+            for r in range(N):
+                po, pl = parts[r][0], OA.to_base(parts[r][1], w.lse_base)
+                seen = np.isfinite(pl)
+                if (np.isfinite(lp_g[r, b]) != seen).any():
+                    worst_stripe_lse = float("inf")            # an empty stripe must be empty on both sides
+                    continue
+                if seen.any():
+                    ds = np.abs(op_g[r, b] - po)[seen]
+                    worst_stripe_excess_o = max(worst_stripe_excess_o,
+                                                float((ds - (O_ABS + O_REL * np.abs(po[seen]))).max()))
+                    worst_stripe_lse = max(worst_stripe_lse, float(np.abs(lp_g[r, b] - pl)[seen].max()))
+    cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+           "kind": "oracle", "seconds": round(cpu_s, 3),
+           "sample": f"{len(sample)} of {w.B} requests ({int(sum(s[2] for s in sample))} tokens, {w.H} heads, "
+                     f"q_len {w.q_len}): all {N} stripe attentions + LSE merge in float64 NumPy, "
+                     f"BLAS threads pinned to the {cores} cores of the process affinity mask"}
+    if full_s > 0:
+        cpu["unsharded_seconds"] = round(full_s, 3)
+        cpu["unsharded_value"] = round(sample_bytes / full_s / 1e9, 4)
+    ok = worst_excess_o <= 0 and worst_lse <= LSE_ABS and worst_stripe_excess_o <= 0 and worst_stripe_lse <= LSE_ABS
+    parity = {"requests_checked": len(sample), "of_requests": w.B, "stripes_checked": N,
+              "max_abs_o": worst_abs_o, "max_excess_o": worst_excess_o, "max_abs_lse": worst_lse,
+              "stripe_max_excess_o": worst_stripe_excess_o, "stripe_max_abs_lse": worst_stripe_lse,
+              "bar": f"|o-o_ref| <= {O_ABS} + {O_REL}|o_ref|, |lse-lse_ref| <= {LSE_ABS} (lse base {w.lse_base})",
+              "ok": bool(ok)}
+    return cpu, parity
+
+
+def run_stream(args):
+    """The streaming-read probe alone, in every load mode: per mode, N launches
+    per step each reading one K3-sized stripe pool (1.208 GB; 9.66 GB per step
+    in all), warm-up then timed steps, mean rate of the timed launches and
+    that of the first timed step."""
+    import torch
+    from mla_context_kv_amd import probe as PR
+    dev = torch.device("cuda:0")
+    w = workloads_k3()
+    N = w.N
+    per = w.B * (w.S // w.N) * ROW_BYTES                        # one stripe's KV at K3
+    buf = torch.zeros((N, per // 2), dtype=torch.int16, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    res = {}
+    for mode in ("lds1", "lds4", "reg"):
+        grid = PR.grid_for(mode, cus)
+        sink = PR.make_sink(mode, grid, dev)
+        for _ in range(args.warmup):
+            for r in range(N):
+                PR.stream(buf[r], per, mode, grid, sink, sh)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        got = 0
+        for k in range(args.steps):
+            for r in range(N):
+                evs[k][r].record(stream)
+                got = PR.stream(buf[r], per, mode, grid, sink, sh)
+            evs[k][N].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+        gbs = got / (ms * 1e-3) / 1e9
+        res[mode] = {"what": PR.MODE_NOTES[mode], "grid": grid, "hot_gbs": round(float(gbs.mean()), 1),
+                     "first_step_gbs": round(float(gbs[0].mean()), 1), "min_us": round(float(ms.min()) * 1e3, 1),
+                     "mean_us": round(float(ms.mean()) * 1e3, 1), "max_us": round(float(ms.max()) * 1e3, 1)}
+    best = max(v["hot_gbs"] for v in res.values())
+    out = {"metric": "streaming HBM read GB/s (measured peak), K3-sized stripe pools, 1 GPU",
+           "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(float(np.mean([v["mean_us"] for v in res.values()])) * N / 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": "streaming read", "bytes_per_launch": per, "launches_per_step": N},
+           "modes": res, "frac_of_spec": round(best / HBM_PEAK_GBS, 4), "device": device_ids(dev)}
+    print(json.dumps(out), flush=True)
+
+
+def workloads_k3():
+    from mla_context_kv_amd import workloads
+    return workloads.WORKLOADS["k3"]
 
 
 def run_head_return(args):

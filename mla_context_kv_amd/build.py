@@ -1,7 +1,9 @@
 """Build libdcp.so (HIP kernels for gfx950 + the C ABI of include/dcp.h) in-tree.
 
 Every .hip file under csrc/ is compiled to an object with hipcc for gfx950 and
-linked into mla_context_kv_amd/libdcp.so.  Packed-FP32 instructions are
+linked into mla_context_kv_amd/libdcp.so.  The streaming-read probe under
+probe/ (a measurement tool, not part of the attention path) is linked into its
+own library, mla_context_kv_amd/libdcp_probe.so.  Packed-FP32 instructions are
 disabled for all device code.
 """
 
@@ -17,6 +19,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libdcp_probe.so")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdcp.so")
@@ -43,7 +47,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD_DIR, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
@@ -55,22 +59,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every kernel source and link libdcp.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    if not srcs:
-        raise RuntimeError("no HIP sources found")
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libdcp.so failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every kernel source, link libdcp.so and libdcp_probe.so; returns libdcp's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
+    if not srcs or not probe_srcs:
+        raise RuntimeError("no HIP sources found")
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     build_abi_client(verbose)
     return LIB
 

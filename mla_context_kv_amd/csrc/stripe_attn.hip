@@ -330,7 +330,14 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
     }
     const int32_t incl = carry + x, excl = incl - nb;
     if (write_table && b < Bv) {
-      p.table[b] = nb;
+      // Device lengths beyond the page table's capacity can ask for more
+      // chunks than the workspace has slots: such chunks have no workgroup,
+      // so the request is flagged (its output is unspecified) and its table
+      // entry is cut to the slots that exist -- the combine never reads past
+      // the workspace.
+      const int32_t fit = incl <= p.slots ? nb : max(p.slots - excl, 0);
+      if (fit != nb) flag_range(p.status);
+      p.table[b] = fit;
       p.table[Bv + b] = excl;
     }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(b < Bv && excl <= c && c < incl);
@@ -1076,6 +1083,7 @@ chunk_combine_kernel(Params p) {
   const int32_t n = p.table[v];
   if (n <= 1) return;
   const int64_t c0 = p.table[Bv + v];
+  if (c0 + n > p.slots) return;        // (never written so: the table is cut to the slots)
   const int32_t ri = v / p.B, b = v - ri * p.B;
   const RankPtrs& rk = p.rk[ri];
   constexpr int v4 = kDV / 4;
@@ -1198,3 +1206,4 @@ extern "C" int dcp_stripe_attn_multi_workspace(const dcp_attn_args* args, int32_
 extern "C" int dcp_stripe_attn_multi(const dcp_attn_args* args, int32_t n, void* stream) {
   return run(args, n, stream);
 }
+

@@ -295,16 +295,10 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
         raise ValueError("sinks must hold one value per head")
     if bias_slopes is not None and bias_slopes.numel() != H:
         raise ValueError("bias_slopes must hold one value per head")
-    need = ctypes.c_size_t(0)
-    _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
-    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
     a.q = _ptr(q, torch.bfloat16, "q", dev)
     a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
     a.block_table = _ptr(block_table, torch.int32, "block_table", dev)
     a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
-    a.workspace = _ptr(workspace, None, "workspace", dev) if workspace is not None else None
-    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.o = _ptr(o, torch.float32, "o", dev)
     a.lse = _ptr(lse, torch.float32, "lse", dev)
     a.status = _ptr(status, torch.int32, "status", dev)
@@ -318,6 +312,14 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
         a.sparse_bits = _ptr(bits, torch.int32, "sparse bits", dev)
         a.sparse_count = _ptr(count, torch.int32, "sparse count", dev)
         a.sparse_stride = int(rows.shape[1])
+    # the size query sees every field the call will see (a sparse selection
+    # sizes the plan by its stride, not by the page table)
+    need = ctypes.c_size_t(0)
+    _check(lib().dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)), "dcp_stripe_attn_workspace")
+    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace, None, "workspace", dev) if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
     return o, lse
 

@@ -13,6 +13,8 @@ must be caught.
 """
 
 import math
+import os
+import re
 
 import numpy as np
 import pytest
@@ -25,6 +27,37 @@ TILE, ROW_SLOTS, CHUNKS = 32, 73, 72
 TILE_SLOTS = TILE * ROW_SLOTS
 STAGES, MAX_RB = 4, 3
 LAST_BASE = TILE_SLOTS - 64
+
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "mla_context_kv_amd", "csrc", "stripe_attn.hip")
+
+
+def kernel_constants():
+    """The integer constexpr constants of the kernel source, evaluated from
+    their definitions (integer literals and earlier constants combined with
+    + - * / and parentheses)."""
+    src = open(KERNEL_SRC).read()
+    env = {}
+    for name, expr in re.findall(r"constexpr\s+int\s+(k\w+)\s*=\s*([^;]+);", src):
+        e = re.sub(r"//.*", "", expr).strip()
+        if not re.fullmatch(r"[\w\s+\-*/()]+", e):
+            continue
+        e = e.replace("/", "//")
+        try:
+            env[name] = int(eval(e, {"__builtins__": {}}, dict(env)))
+        except (NameError, SyntaxError):
+            pass
+    return env
+
+
+def test_replay_constants_are_the_kernels():
+    """The replay below re-types the kernel's tile geometry and plan limits;
+    a kernel edit that changes any of them without a mirror edit here fails."""
+    k = kernel_constants()
+    assert k["kTile"] == TILE and k["kRowSlots"] == ROW_SLOTS and k["kChunks"] == CHUNKS
+    assert k["kTileSlots"] == TILE_SLOTS and k["kLastBase"] == LAST_BASE
+    assert k["kStages"] == STAGES and k["kMaxRB"] == MAX_RB
+    assert k["kTileInsts"] == TILE_INSTS and k["kGroupChunkTiles"] == GROUP_CHUNK
 
 
 TILE_INSTS = -(-TILE_SLOTS // 64)                 # 37
@@ -139,6 +172,43 @@ def test_work_list_fits_the_grid_and_partitions_every_request():
                     # no chunk longer than the mean share of a compute unit (nor the group cap)
                     cap = cdiv(int(tiles.sum()), target)
                     assert max(cs for (_, _, _, cs) in wl) <= (min(cap, GROUP_CHUNK) if mgroups > 1 else cap)
+
+
+def chunk_table(tiles, forced, target, slots, mgroups=1, plant=None):
+    """The chunk table the kernel writes (chunks of request b, first chunk of
+    b): a request whose chunks would run past the workspace's slots is cut
+    to the slots that exist."""
+    wl = work_list(tiles, forced, target, mgroups)
+    n = {}
+    for (b, k, nb, cs) in wl:
+        n[b] = nb
+    table, excl, flagged = [], 0, False
+    for b in range(len(tiles)):
+        nb = n[b]
+        incl = excl + nb
+        fit = nb if (incl <= slots or plant == "no_table_clamp") else max(slots - excl, 0)
+        flagged |= fit != nb
+        table.append((fit, excl))
+        excl = incl
+    return table, flagged
+
+
+def test_chunk_table_never_points_past_the_workspace():
+    """Device lengths past the page table's capacity (the plan sizes the
+    workspace from the table) on the capped row-group path: the table is cut
+    to the slots, so the combine reads inside the workspace, and the call is
+    flagged; within capacity nothing is cut."""
+    B, cols, P, M = 256, 256, 64, 384                  # 4 row groups of 96 rows: capped chunks
+    W, mgroups, slots, forced, target = plan(B, M, cols, P)
+    assert mgroups > 1 and target <= B
+    fits = [cdiv(cols * P, TILE)] * B                  # every request at the table's capacity
+    table, flagged = chunk_table(fits, forced, target, slots, mgroups)
+    assert not flagged and all(c0 + n <= slots for n, c0 in table)
+    over = [8 * cdiv(cols * P, TILE)] * B               # lengths 8x the capacity
+    table, flagged = chunk_table(over, forced, target, slots, mgroups)
+    assert flagged and all(c0 + n <= slots for n, c0 in table if n > 0)
+    table, _ = chunk_table(over, forced, target, slots, mgroups, plant="no_table_clamp")
+    assert any(c0 + n > slots for n, c0 in table)      # what the clamp prevents
 
 
 def count_rows(x, N, I, r):
