@@ -13,7 +13,9 @@
  * Conventions shared by every entry point:
  *  - Pointers named as device pointers must point to device memory (or
  *    memory the device can read/write); the caller owns all buffers.  The
- *    library never allocates or frees memory and keeps no state between calls.
+ *    library never allocates or frees memory and keeps no state between calls,
+ *    except the fixed scratch buffer of dcp_stripe_attn_noalloc (one per GPU,
+ *    held until the process ends).
  *  - bfloat16 data is passed as raw 16-bit storage (void*).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues kernel launches on `stream` and returns; nothing is
@@ -44,6 +46,7 @@ extern "C" {
 #define DCP_EUNSUPPORTED (-2)  /* shape outside what the kernels are built for */
 #define DCP_EHIP (-3)          /* a HIP call or kernel launch failed */
 #define DCP_ERANGE (-4)        /* device data out of range (stored into *status) */
+#define DCP_ESCRATCH (-5)      /* needs more scratch than dcp_stripe_attn_noalloc's fixed buffer */
 
 /* Token-to-rank layout.
  * n_stripes  N >= 1: DCP size (number of stripes / ranks).
@@ -316,6 +319,23 @@ int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* 
  * 1 <= n <= 16 (n > 16: DCP_EUNSUPPORTED). */
 int dcp_stripe_attn_multi_workspace(const dcp_attn_args* args, int32_t n, size_t* bytes);
 int dcp_stripe_attn_multi(const dcp_attn_args* args, int32_t n, void* stream);
+
+/* dcp_stripe_attn_noalloc -- dcp_stripe_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and results
+ * as dcp_stripe_attn (bit for bit), except that args->workspace and
+ * args->workspace_bytes are ignored: the chunk partials and chunk table go to
+ * a fixed scratch buffer the library holds in device memory, one per GPU,
+ * of dcp_stripe_attn_noalloc_max_bytes() bytes (64 MiB) -- every GPU the
+ * library's kernels are loaded on holds it until the process ends.  A shape
+ * whose workspace (dcp_stripe_attn_workspace) exceeds that size returns
+ * DCP_ESCRATCH before any HIP call.  The call allocates and frees nothing;
+ * the buffer needs no clearing (every byte a call reads was written by that
+ * call's kernels).  All calls on one GPU share its buffer: calls that overlap
+ * in time on one GPU (other streams, other threads) race and must not be
+ * made; calls ordered on one stream are safe. */
+int dcp_stripe_attn_noalloc(const dcp_attn_args* args, void* stream);
+size_t dcp_stripe_attn_noalloc_max_bytes(void);
 
 /* dcp_lse_merge -- exact merge of N stripes' partial results.
  * Page "DCP", "merge operator and numerical stability"; SGLang DCP docs,

@@ -8,6 +8,7 @@ extern "C" const char* dcp_strerror(int code) {
     case DCP_EUNSUPPORTED: return "DCP_EUNSUPPORTED: shape not supported by the kernels";
     case DCP_EHIP: return "DCP_EHIP: HIP call or kernel launch failed";
     case DCP_ERANGE: return "DCP_ERANGE: device data out of range";
+    case DCP_ESCRATCH: return "DCP_ESCRATCH: the shape needs more scratch than the fixed no-allocation buffer holds";
     default: return "unknown dcp status code";
   }
 }

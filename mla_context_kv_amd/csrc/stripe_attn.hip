@@ -49,6 +49,8 @@
 //    the bias uses the row's GLOBAL position); an attention sink adds one
 //    zero-valued logit per head to the denominator of the request's first
 //    chunk -- the caller gives it to one rank only.
+#include <mutex>
+
 #include "dcp_common.h"
 #include "merge_impl.h"
 
@@ -1207,3 +1209,51 @@ extern "C" int dcp_stripe_attn_multi(const dcp_attn_args* args, int32_t n, void*
   return run(args, n, stream);
 }
 
+// ---- dcp_stripe_attn_noalloc: the same call with a fixed scratch buffer in
+// place of the caller's workspace, for callers that cannot allocate.  The
+// buffer is a file-scope device array: each GPU the library's kernels load on
+// holds its own copy (kNoAllocScratchBytes) until the process ends.  Host code
+// never uses the array's name as an address: its device address is looked up
+// once per device with hipGetSymbolAddress and kept.
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// device address of this device's copy of `scratch` (nullptr on a HIP error)
+void* scratch_address(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t dcp_stripe_attn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int dcp_stripe_attn_noalloc(const dcp_attn_args* args, void* stream) {
+  Plan pl;
+  const int rc = make_plan(args, 1, &pl);
+  if (rc != DCP_OK) return rc;
+  if (pl.ws_bytes > kNoAllocScratchBytes) return DCP_ESCRATCH;
+  dcp_attn_args a = *args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (pl.ws_bytes > 0) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return DCP_EHIP;
+    void* ptr = scratch_address(dev);
+    if (ptr == nullptr) return DCP_EHIP;
+    a.workspace = ptr;
+    a.workspace_bytes = kNoAllocScratchBytes;
+  }
+  return run(&a, 1, stream);
+}

@@ -25,6 +25,7 @@ DCP_EINVAL = -1
 DCP_EUNSUPPORTED = -2
 DCP_EHIP = -3
 DCP_ERANGE = -4
+DCP_ESCRATCH = -5
 
 HEAD_DIM = 576
 V_DIM = 512
@@ -89,6 +90,8 @@ _SIGNATURES = {
     "dcp_kv_write": (ctypes.c_int, [dcp_layout, _I32, _VP, _I32, _I64, _VP, _VP, _VP, _I32, _I32, _VP, _I64, _VP, _VP]),
     "dcp_stripe_attn_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
+    "dcp_stripe_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _VP]),
+    "dcp_stripe_attn_noalloc_max_bytes": (ctypes.c_size_t, []),
     "dcp_stripe_attn_multi_workspace": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _I32,
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn_multi": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _I32, _VP]),
@@ -321,6 +324,35 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.workspace = _ptr(workspace, None, "workspace", dev) if workspace is not None else None
     a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dcp_stripe_attn(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn")
+    return o, lse
+
+
+def dcp_stripe_attn_noalloc(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Tensor,
+                            block_table: torch.Tensor, seq_len: torch.Tensor, scale: float, lse_base: int = 0,
+                            num_splits: int = 0, o: torch.Tensor = None, lse: torch.Tensor = None,
+                            status: Optional[torch.Tensor] = None):
+    """dcp_stripe_attn through the entry point that allocates nothing (the
+    library's fixed per-GPU scratch buffer replaces the workspace).  o and lse
+    must be given, so the call allocates nothing on this side either."""
+    dev = q.device
+    if q.dim() != 4 or pool.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("q must be [B, q_len, H, 576], pool [pages, P, 576], block_table [B, cols]")
+    B, q_len, H, D = q.shape
+    if o is None or lse is None:
+        raise ValueError("o and lse are required")
+    if o.numel() != B * q_len * H * V_DIM or lse.numel() != B * q_len * H:
+        raise ValueError("o / lse have the wrong size")
+    if block_table.shape[0] != B or seq_len.numel() != B or pool.shape[1] != lay.page_size:
+        raise ValueError("block_table and seq_len need one row per request, pool [pages, page_size, 576]")
+    a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, None, o, lse, status)
+    a.q = _ptr(q, torch.bfloat16, "q", dev)
+    a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
+    a.block_table = _ptr(block_table, torch.int32, "block_table", dev)
+    a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
+    a.o = _ptr(o, torch.float32, "o", dev)
+    a.lse = _ptr(lse, torch.float32, "lse", dev)
+    a.status = _ptr(status, torch.int32, "status", dev)
+    _check(lib().dcp_stripe_attn_noalloc(ctypes.byref(a), _stream(dev)), "dcp_stripe_attn_noalloc")
     return o, lse
 
 
