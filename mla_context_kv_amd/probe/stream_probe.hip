@@ -71,8 +71,9 @@ stream_lds_kernel(const char* __restrict__ src, int64_t tiles, uint32_t* __restr
   for (int64_t t = 0; t < kStages - 1; ++t) issue(t);
   uint32_t acc = 0;
   for (int64_t it = 0; it < n; ++it) {
-    // piece it has landed (the loads of the later pieces may still be in flight)
-    const int64_t later = n - 1 - it;
+    // piece it has landed (the loads of the later pieces already issued,
+    // at most kStages - 2 of them, may still be in flight)
+    const int64_t later = n - 1 - it < kStages - 2 ? n - 1 - it : kStages - 2;
     if (later >= 2) wait_vm_then_barrier<kTwo>();
     else if (later == 1) wait_vm_then_barrier<kMy>();
     else wait_vm_then_barrier<0>();
