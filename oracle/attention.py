@@ -273,6 +273,20 @@ def unpack_merge(recv: np.ndarray, base: str = "e"):
     return lse_merge(o_parts, lse_parts, base)
 
 
+def merge_bf16_parts(o_parts: np.ndarray, lse_parts: np.ndarray, base: str = "e"):
+    """Exact merge of partial results whose outputs travel in bfloat16 and
+    whose LSE travels in float32: each part's o is rounded to bf16 (nearest,
+    ties to even), its lse to float32, then merged in float64.  Page "DCP",
+    "unification with online softmax": the split of a stripe's rows into
+    chunks is the same monoid as the split across stripes, so the chunk
+    partials merge with the same identity; page "MLA 的 DCP", section 5: the
+    partial payload is (512 + 4) x 2 bytes per (row, head), i.e. bf16 o.
+    o_parts [P, ..., V], lse_parts [P, ...] in ``base``."""
+    o16 = bf16_bits_to_float(to_bf16_bits(np.asarray(o_parts, dtype=np.float64).astype(np.float32)))
+    l32 = np.asarray(lse_parts, dtype=np.float64).astype(np.float32).astype(np.float64)
+    return lse_merge(o16, l32, base)
+
+
 # ---- sparse attention with a global top-k selection -------------------------
 #
 # Page "DCP", "conditions for merging and where they fail": sparse attention

@@ -600,3 +600,41 @@ def test_sparse_stripes_merge_to_the_global_selection(N, I):
     parts = [A.sparse_attention(q, kv, S, topk, SCALE, positions=pos) for pos in L.stripe_positions(S, N, I)]
     o, lse = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     assert np.allclose(o, o_full, rtol=1e-12, atol=1e-14) and np.allclose(lse, l_full, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("S,N,k", [(300, 1, 4), (999, 3, 5), (2048, 8, 4), (77, 4, 16)])
+def test_bf16_chunk_partials_merge_within_half_an_ulp(S, N, k):
+    # a stripe's rows cut into k contiguous chunks (as the kernel cuts them),
+    # each chunk's (o, lse) with o rounded to bf16 and lse to float32, merged:
+    # a convex combination of the rounded parts, so within 2^-8 of the largest
+    # |o| of a part (half a bf16 ulp, relative) of the stripe's exact o; the
+    # lse is exact up to float32
+    rng = np.random.default_rng(S + 7 * N + k)
+    H, q_len = 4, 2
+    q, kv = rand_case(rng, S, H, q_len)
+    for r in range(N):
+        pos = L.stripe_positions(S, N, 1)[r]
+        o_ref, l_ref = A.stripe_attention(q, kv, S, pos, SCALE)
+        cs = -(-len(pos) // k)
+        parts = [A.stripe_attention(q, kv, S, pos[c * cs:(c + 1) * cs], SCALE) for c in range(k)]
+        o_p = np.stack([p[0] for p in parts])
+        l_p = np.stack([p[1] for p in parts])
+        o, lse = A.merge_bf16_parts(o_p, l_p)
+        bound = 2.0 ** -8 * np.abs(o_p).max(axis=0) + 1e-12
+        assert (np.abs(o - o_ref) <= bound).all()
+        assert np.allclose(lse, l_ref, rtol=0, atol=1e-5)
+        # without the rounding the same merge is the stripe itself
+        o_x, l_x = A.lse_merge(o_p, l_p)
+        assert np.allclose(o_x, o_ref, rtol=1e-12, atol=1e-13) and np.allclose(l_x, l_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_single_part_is_its_rounding():
+    # one part (and an empty part: o = 0, lse = -inf) merge to the part's own bf16 value
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((1, 5, V))
+    l = rng.standard_normal((1, 5))
+    got, lse = A.merge_bf16_parts(np.concatenate([o, np.zeros_like(o)]),
+                                  np.concatenate([l, np.full_like(l, -np.inf)]))
+    want = A.bf16_bits_to_float(A.to_bf16_bits(o[0].astype(np.float32)))
+    assert np.array_equal(got, want)
+    assert np.array_equal(lse, l[0].astype(np.float32).astype(np.float64))
