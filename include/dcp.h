@@ -179,9 +179,11 @@ int dcp_relayout(dcp_layout layout, int32_t rank, int32_t row_dim,
  *             shorter than k tiles).
  * workspace, workspace_bytes  device scratch of at least the size
  *             dcp_stripe_attn_workspace() reports for these arguments (0 only
- *             for num_splits = 1).  It holds each chunk's partial (o, lse)
- *             and the chunk table; a second kernel on the same stream merges
- *             the chunks of every request that has more than one.  Its
+ *             for num_splits = 1).  It holds each chunk's partial (o as
+ *             bfloat16, rounded to nearest even, and its lse as float32) and
+ *             the chunk table; a second kernel on the same stream merges the
+ *             chunks of every request that has more than one.  (A request
+ *             cut into one chunk writes o_r directly, without the rounding.)  Its
  *             contents need no initialisation.  Calls that overlap in time
  *             must not share a workspace; with a workspace each, calls on
  *             different streams may run at the same time (the library keeps

@@ -191,6 +191,32 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
     merge_row(N, v4, src, in_base2, out_base2, o_row, lse_out);
 }
 
+// bf16 parts (the chunk partials of a stripe): part r of the row's o at
+// o[r * stride * v4 ...] as 4 bf16 per 8-byte unit, its lse at l[r * stride];
+// widened to fp32 in registers (a bf16 is the top half of a float32)
+struct Bf16Parts {
+  const uint2* __restrict__ o;
+  const float* __restrict__ l;
+  int64_t stride;
+  int32_t v4;
+  __device__ float lse(int r) const { return l[(int64_t)r * stride]; }
+  __device__ float4 o4(int r, int c) const {
+    const uint2 u = o[(int64_t)r * stride * v4 + c];
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+
+__device__ __forceinline__ void merge_bf16_row(int32_t N, int64_t stride, int32_t v4, const uint2* __restrict__ o_parts,
+                                               const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
+                                               float4* __restrict__ o_row, float* __restrict__ lse_out) {
+  const Bf16Parts src{o_parts, lse_parts, stride, v4};
+  if (N <= kAtOnceParts && v4 <= 128)
+    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, o_row, lse_out);
+  else
+    merge_row(N, v4, src, in_base2, out_base2, o_row, lse_out);
+}
+
 // Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at
 // lse_parts[r * rows + i].  XCD-aware order: the dispatcher sends block i to
 // XCD i % 8, so giving each XCD a contiguous range of rows keeps a request's

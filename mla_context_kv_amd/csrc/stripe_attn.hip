@@ -157,7 +157,7 @@ struct Params {
   int32_t sparse;                   // every rank has a sparse selection
   float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
-  float* ws_o;                      // chunk partials [slots][M][512], lse2 [slots][M]
+  uint16_t* ws_o;                   // chunk partials: o as bf16 [slots][M][512], lse2 fp32 [slots][M]
   float* ws_lse;
   int32_t* table;                   // chunks per request [nr*B], first chunk of each request [nr*B]
   int32_t* status;
@@ -915,10 +915,11 @@ stripe_attn_kernel(Params p) {
   }
   lds_barrier();
   if (!pv_wave) return;
-  float* out_base;
-  if (direct) out_base = rk.o + out_row0 * kDV;
-  else out_base = p.ws_o + (int64_t)chunk * p.M * kDV;
-  out_base += cgrp * kWaveCols * 32;
+  // a request's only chunk (or an unmerged part) stores o itself in fp32; the
+  // chunks of a request with several store their partial o as bf16 (rounded
+  // to nearest even), merged by the chunk combine
+  float* const out_base = direct ? rk.o + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
+  uint16_t* const part_base = direct ? nullptr : p.ws_o + (int64_t)chunk * p.M * kDV + cgrp * kWaveCols * 32;
   {
     // Normalise and store this wave's 128 columns of each row block.  The
     // accumulator layout gives a lane 16-byte pieces of 4 different 128-byte
@@ -946,7 +947,16 @@ stripe_attn_kernel(Params p) {
         const int r = 2 * i + half;
         const float4 v = *reinterpret_cast<const float4*>(stage + r * kEpiPitch + 4 * n);
         const int Rr = row0 + rb * 32 + r;
-        if (Rr < p.M) *reinterpret_cast<float4*>(out_base + (int64_t)Rr * kDV + 4 * n) = v;
+        if (Rr < p.M) {
+          if (direct) {
+            *reinterpret_cast<float4*>(out_base + (int64_t)Rr * kDV + 4 * n) = v;
+          } else {
+            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            typedef float f32x4_t __attribute__((ext_vector_type(4)));
+            const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
+            *reinterpret_cast<bf16x4_t*>(part_base + (int64_t)Rr * kDV + 4 * n) = h;
+          }
+        }
       }
       lds_wait();   // the next block overwrites the slice
     }
@@ -1060,7 +1070,7 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
   pl->combine = pl->forced != 1 && !a->partials;
   // chunk partials (o, base-2 lse) and the chunk table
   if (pl->combine) {
-    const size_t part = (size_t)pl->slots * M * (kDV + 1) * sizeof(float);
+    const size_t part = (size_t)pl->slots * M * (kDV * sizeof(uint16_t) + sizeof(float));
     pl->table_off = (part + 255) & ~(size_t)255;
     pl->ws_bytes = pl->table_off + (size_t)2 * pl->Bv * sizeof(int32_t);
   } else {
@@ -1090,8 +1100,8 @@ chunk_combine_kernel(Params p) {
   const RankPtrs& rk = p.rk[ri];
   constexpr int v4 = kDV / 4;
   const int64_t out = (int64_t)b * p.M + m;
-  merge_one_row(n, p.M, v4, reinterpret_cast<const float4*>(p.ws_o) + (c0 * p.M + m) * v4, p.ws_lse + c0 * p.M + m,
-                1, p.out_base2, reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
+  merge_bf16_row(n, p.M, v4, reinterpret_cast<const uint2*>(p.ws_o) + (c0 * p.M + m) * v4, p.ws_lse + c0 * p.M + m,
+                 1, p.out_base2, reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
 }
 
 template <int RB, bool kLogit>
@@ -1149,8 +1159,8 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
   prm.sparse = a->sparse_rows != nullptr;
   prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
-  prm.ws_o = pl.combine ? (float*)a->workspace : nullptr;
-  prm.ws_lse = pl.combine ? prm.ws_o + (size_t)pl.slots * M * kDV : nullptr;
+  prm.ws_o = pl.combine ? (uint16_t*)a->workspace : nullptr;
+  prm.ws_lse = pl.combine ? reinterpret_cast<float*>(prm.ws_o + (size_t)pl.slots * M * kDV) : nullptr;
   prm.table = pl.combine ? (int32_t*)((char*)a->workspace + pl.table_off) : nullptr;
   prm.status = a->status;
   for (int32_t i = 0; i < n; ++i) {

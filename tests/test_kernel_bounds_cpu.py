@@ -369,6 +369,6 @@ def test_plan_matches_library_workspace():
         n = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
         W, mg, slots, forced, target = plan(B, q_len * H_, cols, P, num_splits=ns)
-        part = slots * q_len * H_ * 513 * 4
+        part = slots * q_len * H_ * (512 * 2 + 4)       # bf16 o and float32 lse per chunk partial row
         want = 0 if forced == 1 else cdiv(part, 256) * 256 + 2 * B * 4
         assert n.value == want
