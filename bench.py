@@ -68,6 +68,10 @@ def parse():
                          "on every rank)")
     ap.add_argument("--parts", type=int, default=0,
                     help="k > 0: every rank writes k unmerged parts per request and one merge folds all N*k")
+    ap.add_argument("--records", action="store_true",
+                    help="every rank writes its (o_r, lse_r) as bf16 records (+ fp32 lse) in head-owner order -- "
+                         "the head-return all-to-all send buffer -- and one dcp_merge_heads over all owners' rows "
+                         "folds the N ranks' records")
     ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
                     help="2: the per-rank calls alternate between two streams, each with its own workspace, so "
                          "one rank's launch starts on the compute units the previous one leaves idle at its end "
@@ -86,14 +90,15 @@ def parse():
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md")
 
 
-def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1):
+def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1, out_row_bytes: int = (512 + 1) * 4):
     """Algorithmic bytes of each rank's dcp_stripe_attn call: its latent rows
     (local_rows [B, N]: rows of request b on rank r, each read once), the
     queries (B x M rows of 576 bf16) and its outputs (o_r fp32 x 512 and lse_r,
-    or `parts` unmerged parts of them).  Returns one value per rank."""
+    or `parts` unmerged parts of them; out_row_bytes per (row, head): 2052, or
+    1032 for a bf16 record).  Returns one value per rank."""
     local_rows = np.asarray(local_rows, dtype=np.int64)
     q_bytes = B * M * ROW_BYTES
-    out_bytes = parts * B * M * (512 + 1) * 4
+    out_bytes = parts * B * M * out_row_bytes
     return local_rows.sum(axis=0) * ROW_BYTES + q_bytes + out_bytes
 
 
@@ -126,6 +131,9 @@ def main():
         sys.exit(2)
     if args.streams > 1 and args.multi:
         print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
+        sys.exit(2)
+    if args.records and args.parts:
+        print("--records writes each rank's merged o_r as records; it does not take --parts", file=sys.stderr)
         sys.exit(2)
     if args.graph and args.streams > 1:
         print("--graph captures the one-stream step; it does not take --streams 2", file=sys.stderr)
@@ -181,8 +189,14 @@ def main():
 
     M = w.q_len * w.H
     K = max(args.parts, 1)                       # parts per rank (1: the rank's merged o_r)
-    o_parts = torch.empty((N * K, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
-    lse_parts = torch.empty((N * K, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    if args.records:
+        # rank r's records: [owner d][B * q_len][H / N][516]; the merge output
+        # is in the same owner order
+        recs = torch.empty((N, N, w.B * w.q_len, w.H // N, 516), dtype=torch.int16, device=dev)
+        o_parts = lse_parts = None
+    else:
+        o_parts = torch.empty((N * K, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
+        lse_parts = torch.empty((N * K, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -195,6 +209,7 @@ def main():
         a = dcp._attn_args(lay, r, q, sp.pools[r], sp.tables[r], sp.seq_len, workloads.SCALE, base,
                            args.parts if args.parts > 0 else args.splits, None, None, None, None,
                            partials=1 if args.parts > 0 else 0)
+        a.out_records = 1 if args.records else 0
         need = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
@@ -236,14 +251,26 @@ def main():
         a.block_table, a.seq_len = sp.tables[r].data_ptr(), sp.seq_len.data_ptr()
         ws_r = workspaces[r % args.streams]
         a.workspace, a.workspace_bytes = ws_r.data_ptr(), ws_r.numel()
-        a.o, a.lse, a.status = o_parts[r * K].data_ptr(), lse_parts[r * K].data_ptr(), status.data_ptr()
+        if args.records:
+            a.o, a.lse = recs[r].data_ptr(), None
+        else:
+            a.o, a.lse = o_parts[r * K].data_ptr(), lse_parts[r * K].data_ptr()
+        a.status = status.data_ptr()
     refs = [ctypes.byref(a) for a in attn_args]
     if multi_arr is not None:
         for r, a in enumerate(attn_args):
             multi_arr[r] = a
     sh = stream.cuda_stream
     rows = w.B * M
-    merge_call = (N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh)
+
+    def merge(sh_m):
+        if args.records:
+            rc = L.dcp_merge_heads(N, rows, 512, recs.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh_m)
+        else:
+            rc = L.dcp_lse_merge(N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(),
+                                 lse.data_ptr(), sh_m)
+        if rc != 0:
+            raise RuntimeError(f"merge: {dcp.strerror(rc)}")
 
     def step(events=None, sh=sh):
         if multi_arr is not None:
@@ -255,9 +282,7 @@ def main():
             if events is not None:
                 for r in range(1, N + 1):
                     events[r].record(stream)
-            rc = L.dcp_lse_merge(*merge_call[:-1], sh)
-            if rc != 0:
-                raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
+            merge(sh)
             if events is not None:
                 events[N + 1].record(stream)
             return
@@ -288,9 +313,7 @@ def main():
             stream.wait_event(join)
         if events is not None:
             events[N].record(stream)
-        rc = L.dcp_lse_merge(*merge_call[:-1], sh)
-        if rc != 0:
-            raise RuntimeError(f"dcp_lse_merge: {dcp.strerror(rc)}")
+        merge(sh)
         if events is not None:
             events[N + 1].record(stream)
 
@@ -368,7 +391,8 @@ def main():
         local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
     kv_bytes = float(local.sum()) * ROW_BYTES
     q_bytes = w.B * M * ROW_BYTES
-    part_bytes = K * w.B * M * (512 + 1) * 4                           # one stripe's (o_r, lse_r), or its K parts
+    out_row_bytes = 1032 if args.records else (512 + 1) * 4            # per (row, head): bf16 record or fp32
+    part_bytes = K * w.B * M * out_row_bytes                           # one stripe's (o_r, lse_r), or its K parts
     vis = np.zeros(w.B)
     for t in range(w.q_len):
         seen = np.minimum(lens, lens - w.q_len + t + 1).clip(min=0)
@@ -381,7 +405,7 @@ def main():
     kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: one stripe-attention launch (its algorithmic bytes: the
     # stripe's latent rows, the queries, and its (o_r, lse_r))
-    stripe_bytes = stripe_call_bytes(local, w.B, M, K)                            # per rank
+    stripe_bytes = stripe_call_bytes(local, w.B, M, K, out_row_bytes)             # per rank
     launch_ms = per_stripe_ms.mean(axis=0)                                        # per rank
     if args.multi:
         # one launch for all stripes: its bytes over its duration
@@ -392,7 +416,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
-                     or args.multi or args.streams > 1 or args.graph)
+                     or args.multi or args.streams > 1 or args.graph or args.records)
     # ---- measured HBM read peak: the streaming-read probe over the same pools,
     # one launch per stripe's pool, in the step's back-to-back pattern
     probe = None
@@ -404,7 +428,10 @@ def main():
     cpu = None
     parity = None
     if check:
-        host_out = (o.cpu().numpy(), lse.cpu().numpy(), o_parts.cpu().numpy(), lse_parts.cpu().numpy())
+        if args.records:
+            host_out = records_to_host(recs, o, lse, w)
+        else:
+            host_out = (o.cpu().numpy(), lse.cpu().numpy(), o_parts.cpu().numpy(), lse_parts.cpu().numpy())
         slot_bad = slot_map_mismatches(lay, lens[:len(sample)], sp.tables, N, I, P, dev)
         cpu, parity = cpu_oracle_leg(args, w, sample, N, I, host_out)
         parity["slot_map_mismatches"] = slot_bad
@@ -433,6 +460,8 @@ def main():
                    **({"variant": {"window": args.window, "softcap": args.softcap, "sinks": bool(args.sinks)}}
                       if (args.window or args.softcap or args.sinks) else {}),
                    **({"unmerged_parts": K, "merged_parts": N * K} if args.parts > 0 else {}),
+                   **({"outputs": "bf16 records + fp32 lse in head-owner order, merged by dcp_merge_heads"}
+                      if args.records else {}),
                    **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {}),
                    **({"one_launch_for_all_stripes": True} if args.multi else {}),
                    **({"streams": args.streams} if args.streams > 1 else {}),
@@ -451,6 +480,7 @@ def main():
                                 if args.multi else
                                 (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
                                  if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")
+                                + (" (bf16 record outputs)" if args.records else "")
                                 + (" (two streams: the step's stripe time over N, calls overlapping)"
                                    if args.streams > 1 else "")
                                 + (" (one HIP graph per step: the step's time, merge included, over N)"
@@ -459,6 +489,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "step_algorithmic_bytes": int(kv_bytes + N * q_bytes + 2 * N * part_bytes + w.B * M * (512 + 1) * 4),
+        "outputs": "bf16 records" if args.records else "fp32",
         "device": device_ids(dev),
         "setup_s": round(setup_s, 1),
     }
@@ -471,6 +502,28 @@ def main():
     if parity is not None and not parity["ok"]:
         print("parity check against the oracle FAILED", file=sys.stderr)
         sys.exit(3)
+
+
+def records_to_host(recs, o, lse, w):
+    """Host copies in request order of a records step: the merged (o, lse),
+    written in head-owner order [N][B*q_len][H/N], and every rank's (o_r,
+    lse_r) decoded from its bf16 records."""
+    import torch
+    N = recs.shape[0]
+    Hl = w.H // N
+
+    def owner_to_request(x):                       # [N, B*q_len, Hl, ...] -> [B, q_len, H, ...]
+        x = x.reshape((N, w.B * w.q_len, Hl) + tuple(x.shape[3:]))
+        return x.permute((1, 0, 2) + tuple(range(3, x.dim()))).reshape((w.B, w.q_len, w.H) + tuple(x.shape[3:]))
+
+    o_h = owner_to_request(o.view(N, w.B * w.q_len, Hl, 512)).cpu().numpy()
+    lse_h = owner_to_request(lse.view(N, w.B * w.q_len, Hl)).cpu().numpy()
+    r_cpu = recs.cpu()
+    op = np.stack([owner_to_request(r_cpu[r, ..., :512].contiguous().view(torch.bfloat16).float()).numpy()
+                   for r in range(N)])
+    lp = np.stack([owner_to_request(r_cpu[r, ..., 512:514].contiguous().view(torch.float32)[..., 0]).numpy()
+                   for r in range(N)])
+    return o_h, lse_h, op, lp
 
 
 def device_ids(dev):

@@ -248,6 +248,7 @@ typedef struct dcp_attn_args {
   const uint32_t* sparse_bits;
   const int32_t* sparse_count;
   int32_t sparse_stride;
+  int32_t out_records;
 } dcp_attn_args;
 
 /* Unmerged parts (page "DCP", "unification with online softmax": the split
@@ -262,6 +263,23 @@ typedef struct dcp_attn_args {
  *           lse [k][B][q_len][H] (an empty part: o = 0, lse = -inf; the sink,
  *           if any, joins part 0).  No workspace.  dcp_lse_merge over the
  *           N*k parts of all ranks gives the merged result directly. */
+
+/* Packed records (page "MLA 的 DCP", section 5: the partial payload is
+ * (512 + 4) x 2 bytes per (row, head), the output in bf16 and the LSE; page
+ * "DCP", "merge: All-to-All": each rank sends head slice d to the rank that
+ * owns it):
+ * out_records  0: o and lse as above (float32).  1: `o` points to 16-bit
+ *           records in head-owner order [N][k][B][q_len][H / N][v_dim + 4]
+ *           (N = layout.n_stripes, k = num_splits with partials = 1, else 1;
+ *           n_heads must be a multiple of N): per (row, head) the v_dim output
+ *           values in bf16 (rounded to nearest even from the float32 result),
+ *           then the float32 lse (lse_base) in the next two slots, low half
+ *           first, then two zero slots -- the record of dcp_pack_heads, 8-byte
+ *           aligned.  Block d is the piece of the all-to-all send buffer for
+ *           owner d; the owner's dcp_merge_heads over the N (or N * k) blocks
+ *           it receives gives the merged result.  `lse` is not used (may be
+ *           NULL).  The float32 result is rounded once: the records equal
+ *           dcp_pack_heads of the float32 outputs. */
 
 /* Workspace bytes dcp_stripe_attn needs for `args` (pointers are not read). */
 int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);
@@ -314,8 +332,9 @@ int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* 
  * parallelism of all stripes at once).  Each args[i] is a complete
  * dcp_stripe_attn argument block for its rank (own pool, block_table, o, lse,
  * sinks, sparse selection); everything else -- layout, shapes, q, seq_len,
- * scale, base, num_splits, window, softcap, bias_slopes, partials and whether
- * a selection is given -- must be the same in all n (else DCP_EINVAL).  The
+ * scale, base, num_splits, window, softcap, bias_slopes, partials,
+ * out_records and whether a selection is given -- must be the same in all n
+ * (else DCP_EINVAL).  The
  * workspace of args[0] serves the launch; size it with
  * dcp_stripe_attn_multi_workspace.  Results equal n dcp_stripe_attn calls.
  * 1 <= n <= 16 (n > 16: DCP_EUNSUPPORTED). */

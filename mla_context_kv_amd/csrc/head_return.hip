@@ -74,10 +74,11 @@ merge_heads_kernel(int32_t N, int64_t rows, int32_t v4, const uint2* __restrict_
   const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
   if (row >= rows) return;
   const PackedParts src{recv + row * (v4 + 1), rows, v4};
+  const Fp32Out dst{o + row * v4, lse ? lse + row : nullptr};
   if (N <= kAtOnceParts && v4 <= 128)
-    merge_row_at_once<kAtOnceParts>(N, v4, src, base2, base2, o + row * v4, lse ? lse + row : nullptr);
+    merge_row_at_once<kAtOnceParts>(N, v4, src, base2, base2, dst);
   else
-    merge_row(N, v4, src, base2, base2, o + row * v4, lse ? lse + row : nullptr);
+    merge_row(N, v4, src, base2, base2, dst);
 }
 
 }  // namespace

@@ -37,6 +37,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Where a merged row goes: its v4 16-byte column slices (c) and its lse.
+// Fp32Out: o as float32 [v4 * 4] and lse as float32 (lse may be NULL).
+struct Fp32Out {
+  float4* __restrict__ o;
+  float* __restrict__ l;
+  __device__ void o4(int c, float4 v) const { o[c] = v; }
+  __device__ bool has_lse() const { return l != nullptr; }
+  __device__ void lse(float x) const { *l = x; }
+};
+// RecordOut: one packed record -- v4 * 4 bf16 values (round to nearest even),
+// then the float32 lse in the next two 16-bit slots and two zero slots (the
+// head-return record, 8-byte aligned).
+struct RecordOut {
+  uint2* __restrict__ rec;
+  int32_t v4;
+  __device__ void o4(int c, float4 v) const {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
+    rec[c] = __builtin_bit_cast(uint2, h);
+  }
+  __device__ bool has_lse() const { return true; }
+  __device__ void lse(float x) const { rec[v4] = make_uint2(__float_as_uint(x), 0u); }
+};
+
 // Merge of one row by one wavefront.  `src` gives part r's lse (src.lse(r))
 // and its 16-byte column slice c as four floats (src.o4(r, c)); the result
 // goes to o_row[0 .. v4) and *lse_out (when not NULL).  in_base2 / out_base2
@@ -45,10 +70,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // lane merges two 16-byte column slices, with the loads of 8 parts in flight
 // before their FMAs.  Parts of weight zero (lse = -inf, or an underflowed
 // weight) are never read.
-template <class Src>
+template <class Src, class Dst>
 __device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src, int32_t in_base2,
-                                          int32_t out_base2, float4* __restrict__ o_row,
-                                          float* __restrict__ lse_out) {
+                                          int32_t out_base2, const Dst& dst) {
   const int lane = threadIdx.x & 63;
   // weights are base^(lse_r - m): the difference is taken in the input base
   // (exact for nearby values) and only then scaled into base 2 for exp2
@@ -58,8 +82,8 @@ __device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src,
     if (r0 + lane < N) m = fmaxf(m, src.lse(r0 + lane));
   m = wave_max(m);
   if (m == -INFINITY) {
-    for (int c = lane; c < v4; c += 64) o_row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse_out && lane == 0) *lse_out = -INFINITY;
+    for (int c = lane; c < v4; c += 64) dst.o4(c, make_float4(0.f, 0.f, 0.f, 0.f));
+    if (dst.has_lse() && lane == 0) dst.lse(-INFINITY);
     return;
   }
   float wsum = 0.f;
@@ -102,14 +126,14 @@ __device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src,
         }
       }
     }
-    if (in0) o_row[c0] = a0;
-    if (in1) o_row[c1] = a1;
+    if (in0) dst.o4(c0, a0);
+    if (in1) dst.o4(c1, a1);
   }
-  if (lse_out && lane == 0) {
+  if (dst.has_lse() && lane == 0) {
     // lse = m + log_base(sum w), written in the output base
     const float lw2 = log2f(wsum);                          // log2 of the weight sum
     const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
-    *lse_out = m_out + (out_base2 ? lw2 : lw2 * kLn2);
+    dst.lse(m_out + (out_base2 ? lw2 : lw2 * kLn2));
   }
 }
 
@@ -119,10 +143,9 @@ __device__ __forceinline__ void merge_row(int32_t N, int32_t v4, const Src& src,
 // round trip instead of two.  A part of weight zero is read but selected
 // away (never multiplied in), so whatever its buffer holds -- an empty
 // stripe's unwritten output, NaN -- does not reach the result.
-template <int kMax, class Src>
+template <int kMax, class Src, class Dst>
 __device__ __forceinline__ void merge_row_at_once(int32_t N, int32_t v4, const Src& src, int32_t in_base2,
-                                                  int32_t out_base2, float4* __restrict__ o_row,
-                                                  float* __restrict__ lse_out) {
+                                                  int32_t out_base2, const Dst& dst) {
   const int lane = threadIdx.x & 63;
   const int c0 = lane, c1 = 64 + lane;
   const bool in0 = c0 < v4, in1 = c1 < v4;
@@ -139,9 +162,9 @@ __device__ __forceinline__ void merge_row_at_once(int32_t N, int32_t v4, const S
   const float to2 = in_base2 ? 1.0f : kLog2e;
   const float m = wave_max(x);
   if (m == -INFINITY) {
-    if (in0) o_row[c0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (in1) o_row[c1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse_out && lane == 0) *lse_out = -INFINITY;
+    if (in0) dst.o4(c0, make_float4(0.f, 0.f, 0.f, 0.f));
+    if (in1) dst.o4(c1, make_float4(0.f, 0.f, 0.f, 0.f));
+    if (dst.has_lse() && lane == 0) dst.lse(-INFINITY);
     return;
   }
   const float e = x == -INFINITY ? 0.f : exp2f((x - m) * to2);
@@ -158,12 +181,12 @@ __device__ __forceinline__ void merge_row_at_once(int32_t N, int32_t v4, const S
       }
     }
   }
-  if (in0) o_row[c0] = r0;
-  if (in1) o_row[c1] = r1;
-  if (lse_out && lane == 0) {
+  if (in0) dst.o4(c0, r0);
+  if (in1) dst.o4(c1, r1);
+  if (dst.has_lse() && lane == 0) {
     const float lw2 = log2f(wsum);
     const float m_out = (in_base2 == out_base2) ? m : (in_base2 ? m * kLn2 : m * kLog2e);
-    *lse_out = m_out + (out_base2 ? lw2 : lw2 * kLn2);
+    dst.lse(m_out + (out_base2 ? lw2 : lw2 * kLn2));
   }
 }
 constexpr int kAtOnceParts = 8;
@@ -185,10 +208,11 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
                                               int32_t out_base2, float4* __restrict__ o_row,
                                               float* __restrict__ lse_out) {
   const Fp32Parts src{o_parts, lse_parts, stride, v4};
+  const Fp32Out dst{o_row, lse_out};
   if (N <= kAtOnceParts && v4 <= 128)
-    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, o_row, lse_out);
+    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, dst);
   else
-    merge_row(N, v4, src, in_base2, out_base2, o_row, lse_out);
+    merge_row(N, v4, src, in_base2, out_base2, dst);
 }
 
 // bf16 parts (the chunk partials of a stripe): part r of the row's o at
@@ -207,14 +231,15 @@ struct Bf16Parts {
   }
 };
 
+template <class Dst>
 __device__ __forceinline__ void merge_bf16_row(int32_t N, int64_t stride, int32_t v4, const uint2* __restrict__ o_parts,
                                                const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
-                                               float4* __restrict__ o_row, float* __restrict__ lse_out) {
+                                               const Dst& dst) {
   const Bf16Parts src{o_parts, lse_parts, stride, v4};
   if (N <= kAtOnceParts && v4 <= 128)
-    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, o_row, lse_out);
+    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, dst);
   else
-    merge_row(N, v4, src, in_base2, out_base2, o_row, lse_out);
+    merge_row(N, v4, src, in_base2, out_base2, dst);
 }
 
 // Part r of row i: o at o_parts[(r * rows + i) * v4 ...], lse at

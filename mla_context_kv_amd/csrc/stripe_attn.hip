@@ -128,6 +128,7 @@ struct RankPtrs {
   const int32_t* bt;
   float* o;                         // final outputs (requests cut into one chunk)
   float* lse;
+  uint2* rec;                       // packed records in place of o and lse, nullable
   const float* sinks;               // [H] natural-log sink logits, nullable
   const int32_t* sp_rows;           // sparse selection: local rows [B][sp_stride]
   const uint32_t* sp_bits;          //   which query tokens selected each entry (bit t)
@@ -157,6 +158,7 @@ struct Params {
   int32_t sparse;                   // every rank has a sparse selection
   float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
+  int32_t records;                  // outputs as packed records (bf16 o + float32 lse) in rk.rec
   uint16_t* ws_o;                   // chunk partials: o as bf16 [slots][M][512], lse2 fp32 [slots][M]
   float* ws_lse;
   int32_t* table;                   // chunks per request [nr*B], first chunk of each request [nr*B]
@@ -179,6 +181,17 @@ __device__ __forceinline__ const int32_t* sp_count_of(const Params& p, int32_t r
   for (int i = 1; i < kMaxRanks; ++i)
     if (i < p.nr && ri == i) c = p.rk[i].sp_count;
   return c;
+}
+
+// Record of query row R (= t * H + h) of request b, part kk, in 8-byte units
+// (times kDV / 4 + 1): head-owner order [N][parts][B][q_len][H / N], so the
+// block for owner d is one contiguous piece of the all-to-all send buffer.
+__device__ __forceinline__ int64_t rec_index(const Params& p, int32_t kk, int32_t b, int32_t R) {
+  const int32_t t = R / p.H, h = R - t * p.H;
+  const int32_t Hl = p.H / p.N;
+  const int32_t d = h / Hl, j = h - d * Hl;
+  const int32_t K = p.partials > 0 ? p.partials : 1;
+  return ((((int64_t)d * K + kk) * p.B + b) * p.q_len + t) * Hl + j;
 }
 
 // 32-bit layout arithmetic (positions < 2^31: seq_len is int32)
@@ -908,8 +921,11 @@ stripe_attn_kernel(Params p) {
     if (half == 0) {
       inv_lds[wave * 32 + n] = inv;
       if (valid) {
-        if (direct) rk.lse[out_row0 + R] = p.out_base2 ? lse2 : lse2 * kLn2;
-        else p.ws_lse[(int64_t)chunk * p.M + R] = lse2;
+        const float lse_out = p.out_base2 ? lse2 : lse2 * kLn2;
+        if (!direct) p.ws_lse[(int64_t)chunk * p.M + R] = lse2;
+        else if (p.records) rk.rec[rec_index(p, p.partials > 0 ? wi.k : 0, b, R) * (kDV / 4 + 1) + kDV / 4] =
+            make_uint2(__float_as_uint(lse_out), 0u);
+        else rk.lse[out_row0 + R] = lse_out;
       }
     }
   }
@@ -918,7 +934,9 @@ stripe_attn_kernel(Params p) {
   // a request's only chunk (or an unmerged part) stores o itself in fp32; the
   // chunks of a request with several store their partial o as bf16 (rounded
   // to nearest even), merged by the chunk combine
-  float* const out_base = direct ? rk.o + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
+  float* const out_base = direct && !p.records ? rk.o + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
+  uint2* const rec_base = direct && p.records ? rk.rec + cgrp * kWaveCols * 8 : nullptr;
+  const int32_t rec_part = p.partials > 0 ? wi.k : 0;
   uint16_t* const part_base = direct ? nullptr : p.ws_o + (int64_t)chunk * p.M * kDV + cgrp * kWaveCols * 32;
   {
     // Normalise and store this wave's 128 columns of each row block.  The
@@ -948,8 +966,14 @@ stripe_attn_kernel(Params p) {
         const float4 v = *reinterpret_cast<const float4*>(stage + r * kEpiPitch + 4 * n);
         const int Rr = row0 + rb * 32 + r;
         if (Rr < p.M) {
-          if (direct) {
+          if (direct && !p.records) {
             *reinterpret_cast<float4*>(out_base + (int64_t)Rr * kDV + 4 * n) = v;
+          } else if (direct) {
+            // packed record: 4 bf16 (round to nearest even) per 8-byte unit
+            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            typedef float f32x4_t __attribute__((ext_vector_type(4)));
+            const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
+            rec_base[rec_index(p, rec_part, b, Rr) * (kDV / 4 + 1) + n] = __builtin_bit_cast(uint2, h);
           } else {
             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
             typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -984,6 +1008,8 @@ int check_args(const dcp_attn_args* a) {
   if (a->num_splits < 0) return DCP_EINVAL;
   if (a->partials != 0 && (a->partials != 1 || a->num_splits < 1)) return DCP_EINVAL;
   if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
+  if (a->out_records != 0 && a->out_records != 1) return DCP_EINVAL;
+  if (a->out_records && a->n_heads % a->layout.n_stripes != 0) return DCP_EINVAL;
   if ((a->softcap > 0.f || a->bias_slopes != nullptr) && !(a->scale > 0.f)) return DCP_EINVAL;
   if (a->sparse_rows != nullptr) {
     if (a->sparse_bits == nullptr || a->sparse_count == nullptr || a->sparse_stride < 1) return DCP_EINVAL;
@@ -1005,6 +1031,7 @@ bool same_launch(const dcp_attn_args& a, const dcp_attn_args& b) {
          a.n_heads == b.n_heads && a.q == b.q && a.seq_len == b.seq_len && a.scale == b.scale &&
          a.lse_base == b.lse_base && a.num_splits == b.num_splits && a.window == b.window &&
          a.softcap == b.softcap && a.partials == b.partials && a.bias_slopes == b.bias_slopes &&
+         a.out_records == b.out_records &&
          (a.sparse_rows == nullptr) == (b.sparse_rows == nullptr);
 }
 
@@ -1100,8 +1127,13 @@ chunk_combine_kernel(Params p) {
   const RankPtrs& rk = p.rk[ri];
   constexpr int v4 = kDV / 4;
   const int64_t out = (int64_t)b * p.M + m;
-  merge_bf16_row(n, p.M, v4, reinterpret_cast<const uint2*>(p.ws_o) + (c0 * p.M + m) * v4, p.ws_lse + c0 * p.M + m,
-                 1, p.out_base2, reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out);
+  const uint2* const parts = reinterpret_cast<const uint2*>(p.ws_o) + (c0 * p.M + m) * v4;
+  if (p.records)
+    merge_bf16_row(n, p.M, v4, parts, p.ws_lse + c0 * p.M + m, 1, p.out_base2,
+                   RecordOut{rk.rec + rec_index(p, 0, b, m) * (v4 + 1), v4});
+  else
+    merge_bf16_row(n, p.M, v4, parts, p.ws_lse + c0 * p.M + m, 1, p.out_base2,
+                   Fp32Out{reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out});
 }
 
 template <int RB, bool kLogit>
@@ -1129,7 +1161,7 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
   for (int32_t i = 0; i < n; ++i) {
     const dcp_attn_args& x = args[i];
     if (x.q == nullptr || x.pool == nullptr || x.block_table == nullptr || x.seq_len == nullptr ||
-        x.o == nullptr || x.lse == nullptr)
+        x.o == nullptr || (x.lse == nullptr && !x.out_records))
       return DCP_EINVAL;
   }
   if (pl.ws_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < pl.ws_bytes)) return DCP_EINVAL;
@@ -1159,6 +1191,7 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
   prm.sparse = a->sparse_rows != nullptr;
   prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
+  prm.records = a->out_records;
   prm.ws_o = pl.combine ? (uint16_t*)a->workspace : nullptr;
   prm.ws_lse = pl.combine ? reinterpret_cast<float*>(prm.ws_o + (size_t)pl.slots * M * kDV) : nullptr;
   prm.table = pl.combine ? (int32_t*)((char*)a->workspace + pl.table_off) : nullptr;
@@ -1168,8 +1201,9 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
     RankPtrs& r = prm.rk[i];
     r.pool = (const char*)x.pool;
     r.bt = x.block_table;
-    r.o = x.o;
-    r.lse = x.lse;
+    r.o = x.out_records ? nullptr : x.o;
+    r.lse = x.out_records ? nullptr : x.lse;
+    r.rec = x.out_records ? reinterpret_cast<uint2*>(x.o) : nullptr;
     r.sinks = x.sinks;
     r.sp_rows = x.sparse_rows;
     r.sp_bits = x.sparse_bits;

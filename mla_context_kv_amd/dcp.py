@@ -74,6 +74,7 @@ class dcp_attn_args(ctypes.Structure):
         ("sparse_bits", ctypes.c_void_p),
         ("sparse_count", ctypes.c_void_p),
         ("sparse_stride", ctypes.c_int32),
+        ("out_records", ctypes.c_int32),
     ]
 
 
@@ -266,14 +267,18 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
                     sinks: Optional[torch.Tensor] = None, partials: bool = False,
-                    bias_slopes: Optional[torch.Tensor] = None, sparse=None):
+                    bias_slopes: Optional[torch.Tensor] = None, sparse=None, records: bool = False):
     """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
 
     window / softcap / sinks / bias_slopes select the mergeable variants (sinks: fp32 [H], on one
     rank only; bias_slopes: fp32 [H], on every rank).  sparse = (rows, bits, count) from
     dcp_sparse_plan restricts the stripe to the rank's selected tokens.
     partials=True (with num_splits = k >= 1) returns the k unmerged parts instead:
-    o [k,B,q_len,H,512], lse [k,B,q_len,H]."""
+    o [k,B,q_len,H,512], lse [k,B,q_len,H].
+    records=True writes packed records in place of (o, lse), already in the head-return send
+    layout: returns (rec, None), rec int16 [N, (k,) B*q_len, H/N, 516] (N = lay.n_stripes) --
+    the bf16 output then the fp32 lse and two zero slots per (row, head), the record of
+    dcp_pack_heads; rec[d] goes to head owner d, whose dcp_merge_heads folds what it receives."""
     dev = q.device
     if q.dim() != 4 or pool.dim() != 3 or block_table.dim() != 2:
         raise ValueError("q must be [B, q_len, H, 576], pool [pages, P, 576], block_table [B, cols]")
@@ -286,14 +291,25 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     if partials and k < 1:
         raise ValueError("partials needs num_splits >= 1")
     lead = (k,) if partials else ()
-    if o is None:
-        o = torch.empty(lead + (B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty(lead + (B, q_len, H), dtype=torch.float32, device=dev)
-    if o.numel() != k * B * q_len * H * V_DIM or lse.numel() != k * B * q_len * H:
-        raise ValueError("o / lse have the wrong size")
+    if records:
+        N = int(lay.n_stripes)
+        if H % N:
+            raise ValueError("records need n_heads to be a multiple of n_stripes")
+        if o is None:
+            o = torch.empty((N,) + lead + (B * q_len, H // N, V_DIM + 4), dtype=torch.int16, device=dev)
+        if o.numel() != k * B * q_len * H * (V_DIM + 4):
+            raise ValueError("the record tensor has the wrong size")
+        lse = None
+    else:
+        if o is None:
+            o = torch.empty(lead + (B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty(lead + (B, q_len, H), dtype=torch.float32, device=dev)
+        if o.numel() != k * B * q_len * H * V_DIM or lse.numel() != k * B * q_len * H:
+            raise ValueError("o / lse have the wrong size")
     a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status,
                    window, softcap, 1 if partials else 0)
+    a.out_records = 1 if records else 0
     if sinks is not None and sinks.numel() != H:
         raise ValueError("sinks must hold one value per head")
     if bias_slopes is not None and bias_slopes.numel() != H:
@@ -302,7 +318,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
     a.block_table = _ptr(block_table, torch.int32, "block_table", dev)
     a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
-    a.o = _ptr(o, torch.float32, "o", dev)
+    a.o = _ptr(o, torch.int16 if records else torch.float32, "o", dev)
     a.lse = _ptr(lse, torch.float32, "lse", dev)
     a.status = _ptr(status, torch.int32, "status", dev)
     a.sinks = _ptr(sinks, torch.float32, "sinks", dev)
@@ -441,21 +457,33 @@ def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_
                           scale: float, lse_base: int = 0, num_splits: int = 0, o: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
                           window: int = 0, softcap: float = 0.0, sinks=None, bias_slopes=None, sparse=None,
-                          workspace: Optional[torch.Tensor] = None):
+                          workspace: Optional[torch.Tensor] = None, records: bool = False):
     """The stripe attentions of several ranks in one launch: ranks[i] with pools[i],
     block_tables[i] (and sinks[i], sparse[i] when given per rank, else None).  Returns
-    o [n, B, q_len, H, 512] and lse [n, B, q_len, H], equal to n dcp_stripe_attn calls."""
+    o [n, B, q_len, H, 512] and lse [n, B, q_len, H], equal to n dcp_stripe_attn calls.
+    records=True: returns (rec, None), rec int16 [n, N, B*q_len, H/N, 516], each rank's
+    records in head-owner order (see dcp_stripe_attn)."""
     dev = q.device
     n = len(ranks)
     B, q_len, H, D = q.shape
     if len(pools) != n or len(block_tables) != n:
         raise ValueError("one pool and one block table per rank")
-    if o is None:
-        o = torch.empty((n, B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((n, B, q_len, H), dtype=torch.float32, device=dev)
-    if o.shape[0] != n or lse.shape[0] != n:
-        raise ValueError("o / lse need one block per rank")
+    if records:
+        N = int(lay.n_stripes)
+        if H % N:
+            raise ValueError("records need n_heads to be a multiple of n_stripes")
+        if o is None:
+            o = torch.empty((n, N, B * q_len, H // N, V_DIM + 4), dtype=torch.int16, device=dev)
+        if o.shape[0] != n or o[0].numel() != B * q_len * H * (V_DIM + 4):
+            raise ValueError("the record tensor needs one block of [N, B*q_len, H/N, 516] per rank")
+        lse = None
+    else:
+        if o is None:
+            o = torch.empty((n, B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((n, B, q_len, H), dtype=torch.float32, device=dev)
+        if o.shape[0] != n or lse.shape[0] != n:
+            raise ValueError("o / lse need one block per rank")
     arr = (dcp_attn_args * n)()
     for i in range(n):
         a = _attn_args(lay, ranks[i], q, pools[i], block_tables[i], seq_len, scale, lse_base, num_splits,
@@ -464,8 +492,9 @@ def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_
         a.pool = _ptr(pools[i], torch.bfloat16, "pool", dev)
         a.block_table = _ptr(block_tables[i], torch.int32, "block_table", dev)
         a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
-        a.o = _ptr(o[i], torch.float32, "o", dev)
-        a.lse = _ptr(lse[i], torch.float32, "lse", dev)
+        a.o = _ptr(o[i], torch.int16 if records else torch.float32, "o", dev)
+        a.lse = None if records else _ptr(lse[i], torch.float32, "lse", dev)
+        a.out_records = 1 if records else 0
         a.status = _ptr(status, torch.int32, "status", dev)
         a.bias_slopes = _ptr(bias_slopes, torch.float32, "bias_slopes", dev)
         if sinks is not None and sinks[i] is not None:

@@ -100,10 +100,19 @@ def _args(lay=None, **kw):
     ("pool", None, dcp.DCP_EINVAL), ("seq_len", None, dcp.DCP_EINVAL), ("o", None, dcp.DCP_EINVAL),
     ("window", -1, dcp.DCP_EINVAL), ("softcap", -1.0, dcp.DCP_EINVAL), ("softcap", float("nan"), dcp.DCP_EINVAL),
     ("softcap", float("inf"), dcp.DCP_EINVAL), ("partials", 2, dcp.DCP_EINVAL), ("partials", -1, dcp.DCP_EINVAL),
+    ("out_records", 2, dcp.DCP_EINVAL), ("out_records", -1, dcp.DCP_EINVAL), ("lse", None, dcp.DCP_EINVAL),
 ])
 def test_stripe_attn_argument_errors(field, value, code):
     a = _args(**{field: value})
     assert L.dcp_stripe_attn(ctypes.byref(a), None) == code
+
+
+def test_records_need_whole_head_slices():
+    # records go out in head-owner order: n_heads must split evenly over the stripes
+    a = _args(out_records=1, n_heads=12)
+    assert L.dcp_stripe_attn(ctypes.byref(a), None) == dcp.DCP_EINVAL
+    nbytes = ctypes.c_size_t(0)
+    assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(nbytes)) == dcp.DCP_EINVAL
 
 
 def test_softcap_and_position_bias_need_a_positive_scale():

@@ -66,3 +66,30 @@ def test_k3_call_bytes_from_the_oracle_counts():
     assert (got == expect).all() and int(got.mean()) == 1227644928
     # four unmerged parts per request write four times the outputs
     assert (bench.stripe_call_bytes(local, B, H, 4) - got == 3 * B * H * 513 * 4).all()
+
+
+def test_records_to_host_reorders_owner_order_to_request_order():
+    # the records step leaves the merged result and every rank's records in
+    # head-owner order [owner][B*q_len][H/N]; the parity leg reads them back in
+    # request order [B][q_len][H]
+    import types
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    w = types.SimpleNamespace(B=2, q_len=3, H=8)
+    N, Hl = 4, 2
+    g = torch.Generator().manual_seed(5)
+    o_req = torch.randn((2, 3, 8, 512), generator=g)
+    lse_req = torch.randn((2, 3, 8), generator=g)
+    o_own = o_req.reshape(6, N, Hl, 512).permute(1, 0, 2, 3).contiguous()
+    l_own = lse_req.reshape(6, N, Hl).permute(1, 0, 2).contiguous()
+    recs = torch.zeros((N, N, 6, Hl, 516), dtype=torch.int16)
+    for r in range(N):
+        recs[r, ..., :512] = (o_own + r).to(torch.bfloat16).view(torch.int16)
+        recs[r, ..., 512:514] = (l_own + r).unsqueeze(-1).contiguous().view(torch.int16)
+    oh, lh, op, lp = bench.records_to_host(recs, o_own.reshape(-1, 512), l_own.reshape(-1), w)
+    assert np.array_equal(oh, o_req.numpy()) and np.array_equal(lh, lse_req.numpy())
+    for r in range(N):
+        assert np.array_equal(lp[r], (lse_req + r).numpy())
+        assert np.array_equal(op[r], (o_req + r).to(torch.bfloat16).float().numpy())
