@@ -81,6 +81,9 @@ def parse():
                          "then has no per-launch split)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
+    ap.add_argument("--power-seconds", type=float, default=4.0,
+                    help="after the timed region, loop the step this long while amd-smi samples socket power and "
+                         "GFX clocks (0: off); reported as `power` in the JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -356,6 +359,17 @@ def main():
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
 
+    power = None
+    if args.power_seconds > 0:
+        def loop_step():
+            if scratch is not None:
+                scratch.fill_(0.0)
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+        power = sample_power(loop_step, args.power_seconds)
+
     if args.copy_calibration_mib > 0:
         # one plain elementwise pass of known size (reads n bytes, writes n
         # bytes) after the timed region: hardware byte counters of the
@@ -491,6 +505,7 @@ def main():
         "step_algorithmic_bytes": int(kv_bytes + N * q_bytes + 2 * N * part_bytes + w.B * M * (512 + 1) * 4),
         "outputs": "bf16 records" if args.records else "fp32",
         "device": device_ids(dev),
+        "power": power,
         "setup_s": round(setup_s, 1),
     }
     if probe is not None:
@@ -524,6 +539,70 @@ def records_to_host(recs, o, lse, w):
     lp = np.stack([owner_to_request(r_cpu[r, ..., 512:514].contiguous().view(torch.float32)[..., 0]).numpy()
                    for r in range(N)])
     return o_h, lse_h, op, lp
+
+
+def sample_power(loop_step, seconds: float, sync=None):
+    """Loop the step for `seconds` while `amd-smi metric --power --clock`
+    samples the socket power and the GFX clocks of every XCD (each sample
+    takes about a second).  None when amd-smi is missing or lists no GPU;
+    GPU 0 of amd-smi is taken as this device only when it lists one GPU."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    if sync is None:
+        import torch
+        sync = torch.cuda.synchronize
+    if shutil.which("amd-smi") is None:
+        return None
+
+    def query(extra):
+        try:
+            r = subprocess.run(["amd-smi"] + extra, capture_output=True, text=True, timeout=20)
+            return r.stdout if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+
+    listing = query(["list"]) or ""
+    n_gpus = len(re.findall(r"^GPU:\s*\d+", listing, re.M))
+    if n_gpus != 1:
+        return {"skipped": f"amd-smi lists {n_gpus} GPUs: cannot tell which one this process uses"}
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            txt = query(["metric", "-g", "0", "--power", "--clock"])
+            if txt is None:
+                continue
+            pw = re.findall(r"SOCKET_POWER:\s*(\d+)", txt)
+            gfx = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", txt)
+            if pw and gfx:
+                samples.append((time.perf_counter(), float(pw[0]), [float(x) for x in gfx]))
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        loop_step()
+        k += 1
+        if k % 64 == 0:
+            sync()
+    sync()
+    t_end = time.perf_counter()
+    stop.set()
+    th.join(timeout=30)
+    # samples taken while the loop ran, past its first half second (clocks settle)
+    use = [x for x in samples if t0 + 0.5 <= x[0] <= t_end]
+    if not use:
+        return {"skipped": "no amd-smi sample inside the loop"}
+    pw = np.array([x[1] for x in use])
+    clk = np.array([np.mean(x[2]) for x in use])
+    return {"tool": "amd-smi metric --power --clock", "loop_seconds": round(t_end - t0, 2), "steps": k,
+            "samples": len(use), "socket_w_mean": round(float(pw.mean()), 1), "socket_w_max": round(float(pw.max()), 1),
+            "gfx_mhz_mean": round(float(clk.mean()), 1), "gfx_mhz_min": round(float(clk.min()), 1),
+            "xcds": len(use[-1][2])}
 
 
 def device_ids(dev):
@@ -697,12 +776,24 @@ def run_stream(args):
                      "first_step_gbs": round(float(gbs[0].mean()), 1), "min_us": round(float(ms.min()) * 1e3, 1),
                      "mean_us": round(float(ms.mean()) * 1e3, 1), "max_us": round(float(ms.max()) * 1e3, 1)}
     best = max(v["hot_gbs"] for v in res.values())
+    power = None
+    if args.power_seconds > 0:
+        # the stripe kernel's own load mode, looped while power and clocks are sampled
+        grid = PR.grid_for("lds1", cus)
+        sink = PR.make_sink("lds1", grid, dev)
+
+        def loop_step():
+            for r in range(N):
+                PR.stream(buf[r], per, "lds1", grid, sink, sh)
+        power = sample_power(loop_step, args.power_seconds)
+        if isinstance(power, dict):
+            power["mode"] = "lds1"
     out = {"metric": "streaming HBM read GB/s (measured peak), K3-sized stripe pools, 1 GPU",
            "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(float(np.mean([v["mean_us"] for v in res.values()])) * N / 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
            "config": {"workload": "streaming read", "bytes_per_launch": per, "launches_per_step": N},
-           "modes": res, "frac_of_spec": round(best / HBM_PEAK_GBS, 4), "device": device_ids(dev)}
+           "modes": res, "frac_of_spec": round(best / HBM_PEAK_GBS, 4), "device": device_ids(dev), "power": power}
     print(json.dumps(out), flush=True)
 
 

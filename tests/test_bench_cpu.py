@@ -93,3 +93,26 @@ def test_records_to_host_reorders_owner_order_to_request_order():
     for r in range(N):
         assert np.array_equal(lp[r], (lse_req + r).numpy())
         assert np.array_equal(op[r], (o_req + r).to(torch.bfloat16).float().numpy())
+
+
+def test_power_sampler_parses_amd_smi(tmp_path, monkeypatch):
+    # a stand-in amd-smi on PATH printing the layout of `amd-smi list` and of
+    # `amd-smi metric --power --clock` (socket power, then one CLK line per XCD)
+    sys.path.insert(0, ROOT)
+    import bench
+    xcds = "".join(f"        GFX_{i}:\n            CLK: {1500 + 10 * i} MHz\n            MIN_CLK: 500 MHz\n"
+                   for i in range(8))
+    metric = f"GPU: 0\n    POWER:\n        SOCKET_POWER: 1400 W\n    CLOCK:\n{xcds}        MEM_0:\n            CLK: 2000 MHz\n"
+    (tmp_path / "metric.txt").write_text(metric)
+    tool = tmp_path / "amd-smi"
+    tool.write_text("#!/bin/sh\nif [ \"$1\" = list ]; then printf 'GPU: 0\\n    BDF: 0000:a4:00.0\\n'; "
+                    f"else cat {tmp_path / 'metric.txt'}; fi\n")
+    tool.chmod(0o755)
+    monkeypatch.setenv("PATH", f"{tmp_path}:{os.environ['PATH']}")
+    import time
+    got = bench.sample_power(lambda: time.sleep(0.005), 1.5, sync=lambda: None)
+    assert got["samples"] >= 1 and got["socket_w_mean"] == 1400.0 and got["xcds"] == 8
+    assert got["gfx_mhz_mean"] == 1535.0 and got["gfx_mhz_min"] == 1535.0
+    # two GPUs listed: the sampler cannot tell which is this process's
+    tool.write_text("#!/bin/sh\nprintf 'GPU: 0\\nGPU: 1\\n'\n")
+    assert "skipped" in bench.sample_power(lambda: None, 0.1, sync=lambda: None)
