@@ -82,6 +82,7 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB} and {PROBE_LIB}")
     build_abi_client(verbose)
+    build_sanitized(verbose)
     return LIB
 
 
@@ -103,6 +104,61 @@ def build_abi_client(verbose: bool = True) -> str:
     if verbose:
         print(f"built {ABI_CLIENT}")
     return ABI_CLIENT
+
+
+# The host-side argument checks of the C ABI, built with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (each sanitizer flag is
+# given to the host compilation alone; the GPU code is built as usual) and
+# linked with a C driver that calls every entry point with arguments the
+# library must reject or answer on the host.  Runs on the CPU (tests/).
+SAN_HOST_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_DRIVER_SRC = os.path.join(ROOT, "tests", "abi_errors.c")
+SAN_DRIVER = os.path.join(ROOT, "tests", "abi_errors_san")
+
+
+def llvm_tool(name: str) -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    exe = os.path.join(rocm, "lib", "llvm", "bin", name)
+    if not os.path.exists(exe):
+        raise RuntimeError(f"{exe} not found")
+    return exe
+
+
+def _compile_sanitized(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, "san_" + os.path.basename(src) + ".o")
+    flags = [f for f in COMMON_FLAGS if f != "-O3"]
+    cmd = [hipcc(), *flags, *SAN_HOST_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} with host sanitizers failed:\n{r.stdout}{r.stderr}")
+    return obj
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """The ABI error-path driver against a copy of the library whose host code
+    carries AddressSanitizer and UndefinedBehaviorSanitizer."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile_sanitized, srcs))
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    sanitize = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+    drv = os.path.join(BUILD_DIR, "abi_errors.o")
+    r = subprocess.run([llvm_tool("clang"), "-std=c11", "-O1", "-Wall", *sanitize, "-D__HIP_PLATFORM_AMD__",
+                        f"-I{rocm}/include", f"-I{INCLUDE}", "-c", SAN_DRIVER_SRC, "-o", drv],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling the sanitized ABI driver failed:\n{r.stdout}{r.stderr}")
+    r = subprocess.run([llvm_tool("clang++"), *sanitize, "-o", SAN_DRIVER, drv, *objs, f"-L{rocm}/lib",
+                        "-lamdhip64", f"-Wl,-rpath,{rocm}/lib"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the sanitized ABI driver failed:\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {SAN_DRIVER}")
+    return SAN_DRIVER
 
 
 if __name__ == "__main__":

@@ -58,6 +58,7 @@ inline int launch_status() {
   return e == hipSuccess ? DCP_OK : DCP_EHIP;
 }
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (no overflow near INT64_MAX)
+inline int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 
 }  // namespace dcp

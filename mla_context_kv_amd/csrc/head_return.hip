@@ -92,6 +92,7 @@ extern "C" int dcp_pack_heads(int32_t n_stripes, int64_t rows, int32_t n_heads, 
   if (v_dim < 4 || v_dim % 4 != 0) return DCP_EINVAL;
   if (rows == 0) return DCP_OK;
   if (o_r == nullptr || lse_r == nullptr || send == nullptr) return DCP_EINVAL;
+  if (rows > INT64_MAX / n_heads / (v_dim / 4)) return DCP_EUNSUPPORTED;   // (row, head, 4 values) count in 64 bits
   const int64_t total = rows * n_heads * (v_dim / 4);
   int64_t g = ceil_div(total, kPackThreads);
   g = g < 1 ? 1 : (g > 65536 ? 65536 : g);

@@ -1035,6 +1035,12 @@ bool same_launch(const dcp_attn_args& a, const dcp_attn_args& b) {
          (a.sparse_rows == nullptr) == (b.sparse_rows == nullptr);
 }
 
+// a * b for a, b >= 0, or INT64_MAX when the product does not fit
+int64_t mul_or_max(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
   if (args == nullptr || pl == nullptr || n < 1) return DCP_EINVAL;
   if (n > kMaxRanks) return DCP_EUNSUPPORTED;
@@ -1051,6 +1057,8 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
                                           : (int64_t)args[i].bt_cols * args[i].layout.page_size;
     max_rows = m > max_rows ? m : max_rows;
   }
+  // the kernel indexes query rows and workgroups in 32 bits
+  if (M > 0x7fffffff) return DCP_EUNSUPPORTED;
   pl->Bv = (int64_t)n * a->batch;
   // query rows per workgroup: up to 3 blocks of 32; above 96 rows the rows
   // are cut into groups (the workgroups of one group run side by side on
@@ -1069,12 +1077,12 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
     // unmerged parts: exactly num_splits per request, some possibly empty
     pl->forced = a->num_splits;
     pl->target = 0;
-    pl->slots = pl->Bv * a->num_splits;
+    pl->slots = mul_or_max(pl->Bv, a->num_splits);
   } else if (a->num_splits > 0) {
     // a fixed number of chunks per request
     pl->forced = (int32_t)(a->num_splits < tiles_max ? a->num_splits : tiles_max);
     pl->target = 0;
-    pl->slots = pl->Bv * pl->forced;
+    pl->slots = mul_or_max(pl->Bv, pl->forced);
   } else {
     // balanced chunks: one workgroup per compute unit, in one round when the
     // requests are fewer than the compute units; otherwise chunks of the mean
@@ -1089,11 +1097,11 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
     pl->slots = pl->target > pl->Bv ? pl->target : pl->target + pl->Bv;
     if (pl->target <= pl->Bv && pl->mgroups > 1) {
       // chunks capped at kGroupChunkTiles tiles: at most that share of every request, plus one
-      const int64_t capped = pl->Bv * (ceil_div(tiles_max, kGroupChunkTiles) + 1);
+      const int64_t capped = mul_or_max(pl->Bv, ceil_div(tiles_max, kGroupChunkTiles) + 1);
       pl->slots = capped > pl->slots ? capped : pl->slots;
     }
   }
-  if (pl->slots * pl->mgroups > 0x7fffffff || pl->Bv > 0x7fffffff / 2) return DCP_EUNSUPPORTED;
+  if (mul_or_max(pl->slots, pl->mgroups) > 0x7fffffff || pl->Bv > 0x7fffffff / 2) return DCP_EUNSUPPORTED;
   pl->combine = pl->forced != 1 && !a->partials;
   // chunk partials (o, base-2 lse) and the chunk table
   if (pl->combine) {
