@@ -235,6 +235,7 @@ __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 
 struct WorkItem {
   int32_t b, k, n, cs, rows;        // request, chunk of it, its chunks, chunk length (tiles), rows
   int32_t ft;                       // the request's first tile
+  int32_t S;                        // the request's global length
   bool live;
 };
 
@@ -243,36 +244,39 @@ __device__ __forceinline__ int32_t first_row(const Params& p, int32_t S, int32_t
   return p.window > 0 ? count_rows(S - p.q_len + 1 - p.window, p.N, p.I, rank) : 0;
 }
 
-// What the chunks of (virtual) request v cover: its local rows on its rank
-// (the selected entries with a sparse selection) and the tile of the first
-// row any query sees.
-__device__ __forceinline__ int32_t req_rows(const Params& p, int32_t v) {
+// What the chunks of (virtual) request v cover, from one load of its global
+// length S (and of its count with a sparse selection): its local rows on its
+// rank (the selected entries with a sparse selection), the tile of the first
+// row any query sees, and the tiles from there on.
+struct ReqShape {
+  int32_t S, rows, ft, tiles;
+};
+__device__ __forceinline__ ReqShape req_shape(const Params& p, int32_t v) {
   const int32_t ri = v / p.B, b = v - ri * p.B;
-  return p.sparse ? sp_count_of(p, ri)[b] : count_rows(p.seq_len[b], p.N, p.I, rank_id(p, ri));
-}
-__device__ __forceinline__ int32_t req_first_tile(const Params& p, int32_t v) {
-  const int32_t ri = v / p.B, b = v - ri * p.B;
-  return p.sparse ? 0 : first_row(p, p.seq_len[b], rank_id(p, ri)) / 32;
-}
-__device__ __forceinline__ int32_t req_tiles(const Params& p, int32_t v) {
-  const int32_t rows = req_rows(p, v);
-  return rows > 0 ? cdiv(rows, 32) - req_first_tile(p, v) : 0;
+  ReqShape r;
+  r.S = p.seq_len[b];
+  r.rows = p.sparse ? sp_count_of(p, ri)[b] : count_rows(r.S, p.N, p.I, rank_id(p, ri));
+  r.ft = p.sparse ? 0 : first_row(p, r.S, rank_id(p, ri)) / 32;
+  r.tiles = r.rows > 0 ? cdiv(r.rows, 32) - r.ft : 0;
+  return r;
 }
 
 // Unmerged parts: chunk c is part c % k of request c / k (k = partials); a
 // request of t tiles has parts of ceil(t / k) tiles, the last ones empty when
 // t < k (an empty part writes o = 0, lse = -inf: zero weight in the merge).
 __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
-  WorkItem w{0, 0, 0, 0, 0, 0, false};
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
   const int32_t k = p.partials;
   w.b = c / k;
   w.live = w.b < p.nr * p.B;
   if (!w.live) return w;
   w.k = c - w.b * k;
   w.n = k;
-  w.rows = req_rows(p, w.b);
-  w.ft = req_first_tile(p, w.b);
-  const int32_t t = w.rows > 0 ? cdiv(w.rows, 32) - w.ft : 0;
+  const ReqShape rs = req_shape(p, w.b);
+  w.rows = rs.rows;
+  w.ft = rs.ft;
+  w.S = rs.S;
+  const int32_t t = rs.tiles;
   w.cs = t > 0 ? cdiv(t, k) : 0;
   return w;
 }
@@ -280,14 +284,19 @@ __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
 __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
   const int lane = threadIdx.x & 63;
   const int32_t Bv = p.nr * p.B;                  // requests of all ranks in the launch
-  // tiles of request b (from its first tile on); the first 256 requests'
-  // are loaded once (all loads in flight together) and kept in registers
+  // length, rows, first tile and tiles of request b; the first 256
+  // requests' are loaded once (all loads in flight together) and kept in
+  // registers, so the chunk that is found needs no second round trip
   constexpr int kCached = 4;
-  int32_t tiles_c[kCached];
+  int32_t tiles_c[kCached], rows_c[kCached], ft_c[kCached], s_c[kCached];
 #pragma unroll
   for (int j = 0; j < kCached; ++j) {
     const int32_t b = 64 * j + lane;
-    tiles_c[j] = b < Bv ? req_tiles(p, b) : 0;
+    const ReqShape r = b < Bv ? req_shape(p, b) : ReqShape{0, 0, 0, 0};
+    tiles_c[j] = r.tiles;
+    rows_c[j] = r.rows;
+    ft_c[j] = r.ft;
+    s_c[j] = r.S;
   }
   auto tiles_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
     const int32_t b = b0 + lane;
@@ -297,7 +306,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? tiles_c[j] : r;
       return r;
     }
-    return b < Bv ? req_tiles(p, b) : 0;
+    return b < Bv ? req_shape(p, b).tiles : 0;
   };
   int32_t C = 1;
   if (p.forced_splits == 0) {
@@ -327,7 +336,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       }
     }
   }
-  WorkItem w{0, 0, 0, 0, 0, 0, false};
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
   int32_t carry = 0;
   for (int32_t b0 = 0; b0 < Bv; b0 += 64) {
     const int32_t b = b0 + lane;
@@ -362,8 +371,23 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       w.b = b0 + l;
       w.k = c - __builtin_amdgcn_readlane(excl, l);
       w.n = __builtin_amdgcn_readlane(nb, l);
-      w.rows = req_rows(p, w.b);
-      w.ft = req_first_tile(p, w.b);
+      if (b0 < 64 * kCached) {
+        int32_t rr = rows_c[0], ff = ft_c[0], ss = s_c[0];
+#pragma unroll
+        for (int j = 1; j < kCached; ++j) {
+          rr = b0 == 64 * j ? rows_c[j] : rr;
+          ff = b0 == 64 * j ? ft_c[j] : ff;
+          ss = b0 == 64 * j ? s_c[j] : ss;
+        }
+        w.rows = __builtin_amdgcn_readlane(rr, l);
+        w.ft = __builtin_amdgcn_readlane(ff, l);
+        w.S = __builtin_amdgcn_readlane(ss, l);
+      } else {
+        const ReqShape r = req_shape(p, w.b);
+        w.rows = r.rows;
+        w.ft = r.ft;
+        w.S = r.S;
+      }
       const int32_t tl = __builtin_amdgcn_readlane(t, l);
       w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
       if (!write_table) break;
@@ -464,7 +488,7 @@ stripe_attn_kernel(Params p) {
   const bool direct = wi.n == 1 || p.partials > 0;
   const int64_t out_row0 = ((p.partials > 0 ? (int64_t)wi.k * p.B : 0) + b) * p.M;   // first output row
 
-  const int32_t S_b = p.seq_len[b];
+  const int32_t S_b = wi.S;
   const int32_t max_vis = wi.rows;     // rows the last query sees
   // sparse selection: the chunks run over entries of the request's list of
   // selected local rows; with several drafts each entry carries the drafts
@@ -516,7 +540,6 @@ stripe_attn_kernel(Params p) {
     // vector-memory operation -- all in-flight tile loads -- at each later use.
     asm volatile("" : "+v"(vpt));
   };
-  if (kAligned) load_page_table(pt_base);
   // base address of tile `it` (aligned path): its page, offset inside the page
   auto tile_base_of = [&](int it) -> const char* {
     const int32_t J = row_lo + it * kTile;
@@ -866,8 +889,11 @@ stripe_attn_kernel(Params p) {
         }
       }
     } else {
-      // the loader (and, with fewer than 3 row blocks, idle waves)
+      // the loader (and, with fewer than 3 row blocks, idle waves); only
+      // this wave reads the page table, so the others start their own loads
+      // without waiting for it
       __builtin_amdgcn_s_setprio(3);
+      if (kAligned) load_page_table(pt_base);
       // the per-lane byte offsets of a fast tile's loads are the same for
       // every tile: computed once, kept in registers
       uint32_t foff[kMyLoads];

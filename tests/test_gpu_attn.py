@@ -235,6 +235,8 @@ SPARSE = [
     (3, 96, 1, 8, 1, 64, [3000, 9, 700], "2", 256, 0, None),        # DSA-style decode, an almost empty request
     (2, 96, 4, 8, 1, 64, [2000, 300], "e", 64, 0, None),            # drafts with their own selections
     (2, 64, 2, 4, 64, 64, [5000, 129], "2", 500, 3, "sink+cap"),    # chunks, interleave 64, sink and softcap
+    (2, 16, 4, 2, 1, 64, [40, 300], "e", 2048, 2, None),            # q_len*K far past the page table: the
+                                                                     # workspace is sized from the selection
 ]
 
 
