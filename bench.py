@@ -40,18 +40,20 @@ FLOP_PER_ROW_QUERY = 2 * 576 + 2 * 512   # QK^T + PV per (query row, visible tok
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for k3 and long, 100 for the short workloads)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: 10, or 20)")
     ap.add_argument("--workload", default="k3", help="tiny | dsv3 | k3 | ragged | long")
     ap.add_argument("--interleave", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0, help="KV splits per request (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unsharded-baseline", action="store_true",
                     help="time only the oracle's striped attention + merge, not also its unsharded attention")
-    ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return", "stream"],
+    ap.add_argument("--op", default="step", choices=["step", "relayout", "head-return", "stream", "mfma"],
                     help="step: stripe attention + merge (the headline); relayout: prefill-to-decode relayout; "
                          "head-return: pack by head owner + the owners' merges; stream: the streaming-read probe "
-                         "(measured HBM read peak) in every load mode")
+                         "(measured HBM read peak) in every load mode; mfma: the MFMA probe (measured bf16 matrix "
+                         "peak with the stripe kernel's 32x32x16 instruction)")
     ap.add_argument("--no-probe", action="store_true",
                     help="step: skip the streaming-read probe that gives the measured HBM peak")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap of the step (0 = none)")
@@ -87,7 +89,15 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (the reference "
                          "kernel for scaling HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # timing protocol: 20 timed steps for the long-running shapes, 100 for the
+    # short ones (whose step is a few hundred microseconds)
+    short = args.op == "step" and args.workload not in ("k3", "long")
+    if args.steps is None:
+        args.steps = 100 if short else 20
+    if args.warmup is None:
+        args.warmup = 20 if short else 10
+    return args
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md")
@@ -156,6 +166,9 @@ def main():
         return
     if args.op == "stream":
         run_stream(args)
+        return
+    if args.op == "mfma":
+        run_mfma(args)
         return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
@@ -436,6 +449,10 @@ def main():
     probe = None
     if not args.no_probe:
         probe = probe_pools(args, sp.pools, N, stream, dev)
+    mfma_peak = None
+    if not args.no_probe and flops / max(kv_bytes, 1.0) > MFMA_BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3):
+        # above the spec ridge the step is MFMA-bound: its rate against the MFMA probe's
+        mfma_peak, _, _, _ = mfma_probe_steps(N, 5, 2, stream, dev)
 
     # ---- parity of the last timed step's outputs against the oracle
     check = sample is not None and not (args.window or args.softcap or args.sinks or args.parts or args.topk)
@@ -463,6 +480,8 @@ def main():
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        **({"mfma_measured_peak": round(mfma_peak, 1), "mfma_frac_of_measured": round(tflops / mfma_peak, 4)}
+           if mfma_peak else {}),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -794,6 +813,64 @@ def run_stream(args):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
            "config": {"workload": "streaming read", "bytes_per_launch": per, "launches_per_step": N},
            "modes": res, "frac_of_spec": round(best / HBM_PEAK_GBS, 4), "device": device_ids(dev), "power": power}
+    print(json.dumps(out), flush=True)
+
+
+MFMA_PROBE_ITERS = 1600          # about 200 us per launch at the clock a loaded chip holds
+
+
+def mfma_probe_steps(N, steps, warmup, stream, dev):
+    """N launches of the MFMA probe per step (the stripe step's pattern), one
+    workgroup of 8 waves per CU; returns (mean TFLOP/s of the timed launches,
+    that of the first timed step, mean launch microseconds, grid)."""
+    import torch
+    from mla_context_kv_amd import probe as PR
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = PR.make_mfma_sink(cus, dev)
+    sh = stream.cuda_stream
+    for _ in range(warmup):
+        for _ in range(N):
+            PR.mfma(cus, MFMA_PROBE_ITERS, sink, sh)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    flops = 0
+    for k in range(steps):
+        for r in range(N):
+            evs[k][r].record(stream)
+            flops = PR.mfma(cus, MFMA_PROBE_ITERS, sink, sh)
+        evs[k][N].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(steps)])
+    tf = flops / (ms * 1e-3) / 1e12
+    return float(tf.mean()), float(tf[0].mean()), float(ms.mean() * 1e3), cus
+
+
+def run_mfma(args):
+    """The MFMA probe alone: per step 8 launches of ~200 us, every SIMD
+    running 32x32x16 bf16 MFMAs on four independent accumulator chains (two
+    waves per SIMD, as in the stripe kernel), no memory traffic."""
+    import torch
+    from mla_context_kv_amd import probe as PR
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    N = 8
+    hot, first, us, grid = mfma_probe_steps(N, args.steps, args.warmup, stream, dev)
+    power = None
+    if args.power_seconds > 0:
+        sink = PR.make_mfma_sink(grid, dev)
+
+        def loop_step():
+            for _ in range(N):
+                PR.mfma(grid, MFMA_PROBE_ITERS, sink, stream.cuda_stream)
+        power = sample_power(loop_step, args.power_seconds)
+    out = {"metric": "bf16 MFMA TFLOP/s (measured peak), v_mfma_f32_32x32x16_bf16 on every SIMD, 1 GPU",
+           "value": round(hot, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(us * N / 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "mfma stream", "grid": grid, "waves_per_workgroup": 8, "chains_per_wave": 4,
+                      "iters": MFMA_PROBE_ITERS, "launches_per_step": N},
+           "first_step_tflops": round(first, 1), "launch_us": round(us, 1),
+           "frac_of_spec": round(hot / MFMA_BF16_PEAK_TFLOPS, 4), "device": device_ids(dev), "power": power}
     print(json.dumps(out), flush=True)
 
 

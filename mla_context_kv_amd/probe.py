@@ -1,5 +1,7 @@
 """ctypes binding of libdcp_probe.so: the streaming-read probe that measures
-the HBM read peak with the stripe kernel's own 16-byte direct-to-LDS load.
+the HBM read peak with the stripe kernel's own 16-byte direct-to-LDS load, and
+the MFMA probe that measures the bf16 matrix peak with its own MFMA
+instruction.
 
 A measurement tool only (bench.py uses it); the attention path never calls it.
 """
@@ -38,6 +40,11 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
         h.dcp_probe_block_threads.restype = ctypes.c_int
         h.dcp_probe_block_threads.argtypes = [ctypes.c_int32]
+        h.dcp_probe_mfma.restype = ctypes.c_int
+        h.dcp_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.c_void_p]
+        h.dcp_probe_mfma_block_threads.restype = ctypes.c_int
+        h.dcp_probe_mfma_block_threads.argtypes = []
         _h = h
     return _h
 
@@ -62,3 +69,18 @@ def stream(src: torch.Tensor, nbytes: int, mode: str, grid: int, sink: torch.Ten
     if rc != 0:
         raise RuntimeError(f"dcp_probe_stream returned {rc}")
     return int(got.value)
+
+
+def make_mfma_sink(grid: int, device) -> torch.Tensor:
+    return torch.empty(grid * lib().dcp_probe_mfma_block_threads(), dtype=torch.float32, device=device)
+
+
+def mfma(grid: int, iters: int, sink: torch.Tensor, stream_handle: int) -> int:
+    """Enqueue one MFMA-probe launch (8 waves per workgroup, 4 independent
+    32x32x16 bf16 chains per wave); returns its matrix FLOPs."""
+    flops = ctypes.c_int64(0)
+    rc = lib().dcp_probe_mfma(int(grid), int(iters), ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                              ctypes.c_void_p(stream_handle))
+    if rc != 0:
+        raise RuntimeError(f"dcp_probe_mfma returned {rc}")
+    return int(flops.value)

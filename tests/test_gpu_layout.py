@@ -247,3 +247,26 @@ def test_relayout_missing_page_is_skipped_and_flagged():
                        s_sl, d_sl)
     assert np.array_equal(pool.view(torch.int16).reshape(-1, D).cpu().numpy(), want)
     assert (s_sl < 0).sum() == 4                             # rank 1 owns 49, 53, 57, 61 of that page
+
+
+@pytest.mark.gpu
+def test_measurement_probes_run():
+    # the streaming-read and MFMA probes behind the measured peaks: one small
+    # launch each, counts as documented, every sink word written
+    import torch
+    from mla_context_kv_amd import probe as PR
+    dev = torch.device("cuda:0")
+    src = torch.arange(41 * 36864 // 4, dtype=torch.int32, device=dev)
+    for mode in ("lds1", "lds4", "reg"):
+        grid = 4
+        sink = PR.make_sink(mode, grid, dev)
+        sink.fill_(-1)
+        got = PR.stream(src, 40 * 36864 + 100, mode, grid, sink, torch.cuda.current_stream(dev).cuda_stream)
+        torch.cuda.synchronize()
+        assert got == 40 * 36864
+        assert not bool((sink == -1).all())
+    sink = PR.make_mfma_sink(2, dev)
+    flops = PR.mfma(2, 3, sink, torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert flops == 2 * 8 * 4 * 4 * 32 * 32 * 16 * 2          # 3 rounds run as 4 (pairs)
+    assert bool(torch.isfinite(sink).all())
