@@ -83,6 +83,9 @@ def parse():
                          "then has no per-launch split)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary measurement: the same step with all N stripes in one "
+                         "dcp_stripe_attn_multi launch")
     ap.add_argument("--power-seconds", type=float, default=4.0,
                     help="after the timed region, loop the step this long while amd-smi samples socket power and "
                          "GFX clocks (0: off); reported as `power` in the JSON line")
@@ -372,6 +375,47 @@ def main():
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
 
+    # ---- secondary variant: the same step with all N stripes in one launch
+    # (the N-fold parallelism of one GPU), timed the same way
+    one_launch = None
+    if not (args.no_secondary or args.multi or args.streams > 1 or args.graph or args.topk > 0):
+        arr2 = (dcp.dcp_attn_args * N)(*[dcp.dcp_attn_args.from_buffer_copy(a) for a in attn_args])
+        need2 = ctypes.c_size_t(0)
+        assert L.dcp_stripe_attn_multi_workspace(arr2, N, ctypes.byref(need2)) == 0
+        ws2 = torch.empty(max(need2.value, 16), dtype=torch.uint8, device=dev)
+        arr2[0].workspace, arr2[0].workspace_bytes = ws2.data_ptr(), ws2.numel()
+
+        def step2(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            rc = L.dcp_stripe_attn_multi(arr2, N, sh)
+            if rc != 0:
+                raise RuntimeError(f"dcp_stripe_attn_multi: {dcp.strerror(rc)}")
+            if ev is not None:
+                ev[1].record(stream)
+            merge(sh)
+            if ev is not None:
+                ev[2].record(stream)
+        for _ in range(max(2, args.warmup // 2)):
+            step2()
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            if scratch is not None:
+                scratch.fill_(float(k))
+            step2(ev2[k])
+        torch.cuda.synchronize()
+        st2 = np.array([ev2[k][0].elapsed_time(ev2[k][2]) for k in range(args.steps)])
+        la2 = np.array([ev2[k][0].elapsed_time(ev2[k][1]) for k in range(args.steps)])
+        if int(status.item()) != 0:
+            raise RuntimeError(f"device status {int(status.item())} after the one-launch step")
+        one_launch = {"what": "the same step with the N stripe attentions in one dcp_stripe_attn_multi launch, "
+                              "then the same merge (HIP-event step times)",
+                      "us_per_step": round(float(st2.mean()) * 1e3, 1),
+                      "us_per_step_median": round(float(np.median(st2)) * 1e3, 1),
+                      "launch_us": round(float(la2.mean()) * 1e3, 1), "ms": float(st2.mean())}
+        del ws2
+
     power = None
     if args.power_seconds > 0:
         def loop_step():
@@ -417,6 +461,11 @@ def main():
         first = np.clip(lens - w.q_len + 1 - args.window, 0, None)
         local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
     kv_bytes = float(local.sum()) * ROW_BYTES
+    if one_launch is not None:
+        ms2 = one_launch.pop("ms")
+        one_launch["value"] = round(kv_bytes / (ms2 * 1e-3) / 1e9, 2)
+        one_launch["unit"] = "GB/s"
+        one_launch["hbm_frac"] = round(kv_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     q_bytes = w.B * M * ROW_BYTES
     out_row_bytes = 1032 if args.records else (512 + 1) * 4            # per (row, head): bf16 record or fp32
     part_bytes = K * w.B * M * out_row_bytes                           # one stripe's (o_r, lse_r), or its K parts
@@ -525,6 +574,7 @@ def main():
         "outputs": "bf16 records" if args.records else "fp32",
         "device": device_ids(dev),
         "power": power,
+        "one_launch_for_all_stripes": one_launch,
         "setup_s": round(setup_s, 1),
     }
     if probe is not None:

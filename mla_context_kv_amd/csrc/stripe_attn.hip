@@ -67,6 +67,7 @@ constexpr int kKSteps = kD / 16;        // 36 MFMA k-steps for QK^T
 constexpr int kRowBytes = kD * 2;       // 1152
 constexpr int kWaves = 4;               // PV waves, one per SIMD
 constexpr int kNW = 8;                  // wavefronts per workgroup
+constexpr int kChunkGroup = 4;          // consecutive chunks kept on one XCD
 constexpr int kLoaderWaveId = 3;
 constexpr int kWaveCols = kDV / kWaves / 32;   // 4 value-column blocks of 32 per wave
 constexpr int kMaxRB = 3;               // query-row blocks of 32 per workgroup
@@ -471,13 +472,20 @@ stripe_attn_kernel(Params p) {
   const bool pv_wave = wave >= 4;
   const int cgrp = wave - 4;           // PV wave: value columns 128*cgrp .. +127
 
-  // ---- work item: XCD-aware block order (the dispatcher sends block i to XCD
-  // i % 8, so consecutive logical items share an XCD and its L2)
-  int id = blockIdx.x;
-  const int G = gridDim.x;
-  if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
-  const int mg = id % p.mgroups;
-  const int32_t chunk = id / p.mgroups;
+  // ---- work item: XCD-aware block order.  The dispatcher sends block i to
+  // XCD i % 8.  Groups of kChunkGroup consecutive chunks go to the XCDs in
+  // turn (chunk c to XCD (c / kChunkGroup) % 8): the live chunks (numbered
+  // first; a plan may hold more slots than a call's lengths fill) spread over
+  // every XCD, while a request's neighbouring chunks share an XCD and its L2
+  // (its queries are read there once).  The row groups of one chunk are
+  // consecutive blocks of that XCD, so they run side by side and share each
+  // KV tile through its L2.  (The plan makes the slot count a multiple of
+  // 8 * kChunkGroup, so the map is a bijection.)
+  const int bid = blockIdx.x;
+  const int bx = bid & 7, bk = bid >> 3;
+  const int mg = bk % p.mgroups;
+  const int bj = bk / p.mgroups;                 // this block's chunk is the bj-th on its XCD
+  const int32_t chunk = ((bj / kChunkGroup) * 8 + bx) * kChunkGroup + bj % kChunkGroup;
   const WorkItem wi = p.partials > 0 ? part_work(p, chunk)
                                       : find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
   if (!wi.live) return;                // past the last chunk (the same in every wave)
@@ -1127,6 +1135,10 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
       pl->slots = capped > pl->slots ? capped : pl->slots;
     }
   }
+  // a multiple of 8 * kChunkGroup slots: the kernel's block order hands
+  // groups of kChunkGroup chunks to the 8 XCDs in turn
+  if (pl->slots > 0x7fffffff) return DCP_EUNSUPPORTED;
+  pl->slots = ceil_div(pl->slots, 8 * kChunkGroup) * 8 * kChunkGroup;
   if (mul_or_max(pl->slots, pl->mgroups) > 0x7fffffff || pl->Bv > 0x7fffffff / 2) return DCP_EUNSUPPORTED;
   pl->combine = pl->forced != 1 && !a->partials;
   // chunk partials (o, base-2 lse) and the chunk table

@@ -125,7 +125,7 @@ def test_stripe_attn_workspace_size_and_missing_workspace():
     a = _args(num_splits=3, bt_cols=100)
     n = ctypes.c_size_t(0)
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK
-    part = 3 * 2 * 16 * (512 * 2 + 4)                               # (o bf16, lse fp32) partial of every chunk slot
+    part = 32 * 16 * (512 * 2 + 4)      # (o bf16, lse fp32) partial of every chunk slot: 3 x 2, rounded up to 32
     assert n.value == -(-part // 256) * 256 + 2 * 2 * 4              # + the chunk table (count, first)
     a = _args(num_splits=1)
     assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(n)) == dcp.DCP_OK and n.value == 0
@@ -245,7 +245,7 @@ def test_multi_rank_launch_argument_errors():
     n = ctypes.c_size_t(0)
     assert L.dcp_stripe_attn_multi_workspace(arr, 3, ctypes.byref(n)) == dcp.DCP_OK
     # the three ranks' chunk slots: 2 requests each, 2 splits (the _args default)
-    assert n.value == -(-(3 * 2 * 2 * 16 * (512 * 2 + 4)) // 256) * 256 + 2 * 3 * 2 * 4
+    assert n.value == -(-(32 * 16 * (512 * 2 + 4)) // 256) * 256 + 2 * 3 * 2 * 4   # 3 x 2 x 2 slots -> 32
     assert L.dcp_stripe_attn_multi_workspace(arr, 0, ctypes.byref(n)) == dcp.DCP_EINVAL
     big = (dcp.dcp_attn_args * 17)(*[_args(rank=i % 8) for i in range(17)])
     assert L.dcp_stripe_attn_multi(big, 17, None) == dcp.DCP_EUNSUPPORTED

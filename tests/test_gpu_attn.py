@@ -145,7 +145,13 @@ def test_full_size_sampled(name, I):
     assert torch.isfinite(lse_f).all()
     lens = s.lens
     if name == "ragged":
-        picks = [0, 3, 6, int(np.argmax(lens)), int(np.argmin(np.abs(lens - 1500)))]
+        # the forced 1..7-token requests, the longest, one near 1500, and every 12th
+        picks = sorted(set(list(range(7)) + [int(np.argmax(lens)), int(np.argmin(np.abs(lens - 1500)))]
+                           + list(range(0, w.B, 12))))
+    elif name == "dsv3":
+        picks = list(range(w.B))                        # every request
+    elif name == "k3":
+        picks = list(range(0, w.B, 9)) + [w.B - 1]      # 8 of 64, first and last included
     else:
         picks = [0, w.B - 1]
     heads = None if w.H * w.q_len * max(int(lens[b]) for b in picks) < 2**26 else list(range(0, w.H, 7))

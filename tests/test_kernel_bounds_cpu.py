@@ -58,9 +58,11 @@ def test_replay_constants_are_the_kernels():
     assert k["kTileSlots"] == TILE_SLOTS and k["kLastBase"] == LAST_BASE
     assert k["kStages"] == STAGES and k["kMaxRB"] == MAX_RB
     assert k["kTileInsts"] == TILE_INSTS and k["kGroupChunkTiles"] == GROUP_CHUNK
+    assert k["kChunkGroup"] == CHUNK_GROUP
 
 
 TILE_INSTS = -(-TILE_SLOTS // 64)                 # 37
+CHUNK_GROUP = 4
 
 
 def load_slots():
@@ -98,7 +100,37 @@ def plan(B, M, bt_cols, P, cus=256, num_splits=0):
         slots = target if target > B else target + B
         if target <= B and mgroups > 1:
             slots = max(slots, B * (-(-tiles_max // GROUP_CHUNK) + 1))
+    slots = -(-slots // (8 * CHUNK_GROUP)) * 8 * CHUNK_GROUP   # groups of chunks go to the 8 XCDs in turn
     return W, mgroups, slots, forced, target
+
+
+def block_item(bid, mgroups):
+    """The kernel's block order: block bid runs on XCD bid % 8; it is row
+    group (bid // 8) % mgroups of the j-th chunk of that XCD, j = bid // 8 //
+    mgroups, and groups of CHUNK_GROUP consecutive chunks go to the XCDs in turn."""
+    bx, bk = bid & 7, bid >> 3
+    j = bk // mgroups
+    return ((j // CHUNK_GROUP) * 8 + bx) * CHUNK_GROUP + j % CHUNK_GROUP, bk % mgroups
+
+
+def test_block_order_is_a_bijection_that_spreads_live_chunks():
+    for slots in (32, 64, 256, 512, 416):
+        for mgroups in (1, 2, 3, 4):
+            items = [block_item(b, mgroups) for b in range(slots * mgroups)]
+            assert sorted(items) == [(c, g) for c in range(slots) for g in range(mgroups)]
+            # the row groups of a chunk sit on one XCD, in consecutive blocks of it
+            for c in range(slots):
+                bids = [b for b, it in enumerate(items) if it[0] == c]
+                assert len({b % 8 for b in bids}) == 1
+                assert sorted(b // 8 for b in bids) == list(range(min(b // 8 for b in bids),
+                                                                  min(b // 8 for b in bids) + mgroups))
+            # any number of live chunks (the first L) spreads over the 8 XCDs to
+            # within one group; a group of consecutive chunks shares an XCD
+            for live in (1, 7, 9, slots // 2, slots - 3):
+                per_xcd = np.bincount([b % 8 for b, it in enumerate(items) if it[0] < live], minlength=8)
+                assert per_xcd.max() - per_xcd.min() <= CHUNK_GROUP * mgroups
+            xcd_of = {it[0]: b % 8 for b, it in enumerate(items)}
+            assert all(xcd_of[c] == xcd_of[c - c % CHUNK_GROUP] for c in range(slots))
 
 
 def cdiv(a, b):
