@@ -79,6 +79,9 @@ constexpr int kMaxRB = 3;               // query-row blocks of 32 per workgroup
 constexpr int kTileInsts = (kTileSlots + 63) / 64;   // 37
 constexpr int kLastBase = kTileSlots - 64;
 constexpr int kStageBytes = kTileSlots * 16;    // 37,376
+// requests whose shapes a workgroup keeps in LDS (in the last tile stage, at
+// the start of the kernel)
+constexpr int kTableMax = 2304;
 constexpr int kStages = 4;
 // P^T rows: 4 chunks of 16 bytes, chunk kk*2 + lane half holding k-step kk;
 // chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16-byte
@@ -282,32 +285,16 @@ __device__ __forceinline__ WorkItem part_work(const Params& p, int32_t c) {
   return w;
 }
 
-__device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table) {
+// `tab` (nullable): every request's (tiles, rows, first tile, length) in
+// LDS, filled by the whole workgroup; without it (batches past its capacity)
+// each wave loads what it needs as it goes.
+__device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool write_table, const int4* tab) {
   const int lane = threadIdx.x & 63;
   const int32_t Bv = p.nr * p.B;                  // requests of all ranks in the launch
-  // length, rows, first tile and tiles of request b; the first 256
-  // requests' are loaded once (all loads in flight together) and kept in
-  // registers, so the chunk that is found needs no second round trip
-  constexpr int kCached = 4;
-  int32_t tiles_c[kCached], rows_c[kCached], ft_c[kCached], s_c[kCached];
-#pragma unroll
-  for (int j = 0; j < kCached; ++j) {
-    const int32_t b = 64 * j + lane;
-    const ReqShape r = b < Bv ? req_shape(p, b) : ReqShape{0, 0, 0, 0};
-    tiles_c[j] = r.tiles;
-    rows_c[j] = r.rows;
-    ft_c[j] = r.ft;
-    s_c[j] = r.S;
-  }
   auto tiles_of = [&](int32_t b0) -> int32_t {     // b0 = 64 * block
     const int32_t b = b0 + lane;
-    if (b0 < 64 * kCached) {
-      int32_t r = tiles_c[0];
-#pragma unroll
-      for (int j = 1; j < kCached; ++j) r = b0 == 64 * j ? tiles_c[j] : r;
-      return r;
-    }
-    return b < Bv ? req_shape(p, b).tiles : 0;
+    if (b >= Bv) return 0;
+    return tab != nullptr ? tab[b].x : req_shape(p, b).tiles;
   };
   int32_t C = 1;
   if (p.forced_splits == 0) {
@@ -372,17 +359,11 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       w.b = b0 + l;
       w.k = c - __builtin_amdgcn_readlane(excl, l);
       w.n = __builtin_amdgcn_readlane(nb, l);
-      if (b0 < 64 * kCached) {
-        int32_t rr = rows_c[0], ff = ft_c[0], ss = s_c[0];
-#pragma unroll
-        for (int j = 1; j < kCached; ++j) {
-          rr = b0 == 64 * j ? rows_c[j] : rr;
-          ff = b0 == 64 * j ? ft_c[j] : ff;
-          ss = b0 == 64 * j ? s_c[j] : ss;
-        }
-        w.rows = __builtin_amdgcn_readlane(rr, l);
-        w.ft = __builtin_amdgcn_readlane(ff, l);
-        w.S = __builtin_amdgcn_readlane(ss, l);
+      if (tab != nullptr) {
+        const int4 e = tab[w.b];
+        w.rows = e.y;
+        w.ft = e.z;
+        w.S = e.w;
       } else {
         const ReqShape r = req_shape(p, w.b);
         w.rows = r.rows;
@@ -392,6 +373,70 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       const int32_t tl = __builtin_amdgcn_readlane(t, l);
       w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
       if (!write_table) break;
+    }
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return w;
+}
+
+// Chunk classes of the many-request plan: chunks of about 2^(30 - key)
+// tiles, key 31 for an empty request.  The plan numbers chunks class by
+// class, longest first (and request by request inside a class), so the
+// longest chunks take the first blocks of the launch and the short ones fill
+// the compute units that free up later: a longest-first order for launches of
+// several rounds of workgroups.
+constexpr int kClasses = 32;
+static_assert(kTableMax * 16 + (1 + kClasses) * 4 <= kStageBytes, "request table and class counts fit one stage");
+__device__ __forceinline__ int32_t chunk_class(int32_t cs) { return cs > 0 ? 30 - (31 - __builtin_clz(cs)) : 31; }
+
+// The many-request plan (more requests than workgroups per round): chunks of
+// the mean per-CU share C, numbered in classes.  `tab` holds every request's
+// shape; `cls` [kClasses] the chunks of each class (filled by the workgroup).
+__device__ __forceinline__ WorkItem find_work_classes(const Params& p, int32_t c, const int4* tab,
+                                                      const int32_t* cls, int32_t C) {
+  const int lane = threadIdx.x & 63;
+  const int32_t Bv = p.nr * p.B;
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
+  // the class of chunk c, from the per-class counts
+  const int32_t cnt = lane < kClasses ? cls[lane] : 0;
+  int32_t x = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  const uint64_t in_class = __builtin_amdgcn_ballot_w64(x - cnt <= c && c < x);
+  if (in_class == 0) return w;                   // past the last chunk
+  const int key = __builtin_ctzll(in_class);
+  const int32_t r = c - (__builtin_amdgcn_readlane(x, key) - __builtin_amdgcn_readlane(cnt, key));
+  // the request of the class's r-th chunk, in request order
+  int32_t carry = 0;
+  for (int32_t b0 = 0; b0 < Bv; b0 += 64) {
+    const int32_t b = b0 + lane;
+    const int32_t t = b < Bv ? tab[b].x : 0;
+    const int32_t nb = max(cdiv(t, C), 1);
+    const int32_t cs = t > 0 ? cdiv(t, nb) : 0;
+    const int32_t mine = b < Bv && chunk_class(cs) == key ? nb : 0;
+    int32_t y = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t z = __shfl_up(y, d, 64);
+      if (lane >= d) y += z;
+    }
+    const int32_t incl = carry + y, excl = incl - mine;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(mine > 0 && excl <= r && r < incl);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      w.live = true;
+      w.b = b0 + l;
+      w.k = r - __builtin_amdgcn_readlane(excl, l);
+      w.n = __builtin_amdgcn_readlane(nb, l);
+      w.cs = __builtin_amdgcn_readlane(cs, l);
+      const int4 e = tab[w.b];
+      w.rows = e.y;
+      w.ft = e.z;
+      w.S = e.w;
+      return w;
     }
     carry = __builtin_amdgcn_readlane(incl, 63);
   }
@@ -486,8 +531,70 @@ stripe_attn_kernel(Params p) {
   const int mg = bk % p.mgroups;
   const int bj = bk / p.mgroups;                 // this block's chunk is the bj-th on its XCD
   const int32_t chunk = ((bj / kChunkGroup) * 8 + bx) * kChunkGroup + bj % kChunkGroup;
-  const WorkItem wi = p.partials > 0 ? part_work(p, chunk)
-                                      : find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0);
+  // Every request's shape, loaded once by the whole workgroup into the last
+  // tile stage (the loader first fills it after the loop's first barrier, and
+  // every wave is done with the table before that barrier).
+  const int32_t Bv = p.nr * p.B;
+  const int4* table = nullptr;
+  // many requests per round of workgroups: chunks of the mean per-CU share,
+  // numbered longest class first
+  const bool classes = p.partials == 0 && p.forced_splits == 0 && p.target_chunks <= Bv && Bv <= kTableMax;
+  int32_t C = 1;
+  if (p.partials == 0 && Bv <= kTableMax) {
+    int4* t = reinterpret_cast<int4*>(smem + (kStages - 1) * kStageBytes);
+    int32_t* const aux = reinterpret_cast<int32_t*>(t + kTableMax);   // [0] total tiles, [1 + key] chunks
+    if (classes) {
+      if (threadIdx.x < 1 + kClasses) aux[threadIdx.x] = 0;
+      __syncthreads();
+    }
+    int32_t mine = 0;
+    for (int v = threadIdx.x; v < Bv; v += 64 * kNW) {
+      const ReqShape r = req_shape(p, v);
+      t[v] = make_int4(r.tiles, r.rows, r.ft, r.S);
+      mine += r.tiles;
+    }
+    if (classes) {
+      mine = wave_sum_i(mine);
+      if (lane == 0) atomicAdd(&aux[0], mine);
+    }
+    __syncthreads();
+    table = t;
+    if (classes) {
+      C = max(cdiv(aux[0], p.target_chunks), 1);
+      if (p.mgroups > 1) C = min(C, kGroupChunkTiles);
+      for (int v = threadIdx.x; v < Bv; v += 64 * kNW) {
+        const int32_t tv = t[v].x;
+        const int32_t nb = max(cdiv(tv, C), 1);
+        atomicAdd(&aux[1 + chunk_class(tv > 0 ? cdiv(tv, nb) : 0)], nb);
+      }
+      __syncthreads();
+    }
+  }
+  WorkItem wi;
+  if (p.partials > 0) {
+    wi = part_work(p, chunk);
+  } else if (classes) {
+    const int32_t* const aux = reinterpret_cast<const int32_t*>(table + kTableMax);
+    wi = find_work_classes(p, chunk, table, aux + 1, C);
+    if (p.table != nullptr && mg == 0 && wave == 0 && lane == 0) {
+      // the chunk table the combine reads: each request's first chunk writes
+      // its entry (cut to the slots there are; chunks without a workgroup
+      // make the call flagged), and the workgroup of chunk 0 checks the count
+      if (wi.live && wi.k == 0) {
+        const int32_t fit = chunk + wi.n <= p.slots ? wi.n : p.slots - chunk;
+        if (fit != wi.n) flag_range(p.status);
+        p.table[wi.b] = fit;
+        p.table[Bv + wi.b] = chunk;
+      }
+      if (chunk == 0) {
+        int32_t tot = 0;
+        for (int key = 0; key < kClasses; ++key) tot += aux[1 + key];
+        if (tot > p.slots) flag_range(p.status);
+      }
+    }
+  } else {
+    wi = find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0, table);
+  }
   if (!wi.live) return;                // past the last chunk (the same in every wave)
   const int32_t ri = wi.b / p.B;       // rank slot of the launch
   const int b = wi.b - ri * p.B;       // request
@@ -1168,7 +1275,7 @@ chunk_combine_kernel(Params p) {
   const int32_t n = p.table[v];
   if (n <= 1) return;
   const int64_t c0 = p.table[Bv + v];
-  if (c0 + n > p.slots) return;        // (never written so: the table is cut to the slots)
+  if (c0 < 0 || c0 + n > p.slots) return;   // (never written so: entries are cut to the slots)
   const int32_t ri = v / p.B, b = v - ri * p.B;
   const RankPtrs& rk = p.rk[ri];
   constexpr int v4 = kDV / 4;

@@ -415,3 +415,29 @@ def test_multi_rank_launch_other_modes(mode):
     if mode == "splits":
         # a fixed split count gives the same chunks in both paths: bitwise equal
         assert torch.equal(mo, per_o) and torch.equal(ml, per_l)
+
+
+MANY = [
+    # B, H, N, P, max length, seed: more requests of all ranks than workgroups per round, so the
+    # plan cuts chunks of the mean per-CU share and numbers them longest class first
+    (48, 32, 8, 64, 6000, 1),      # one row group: 384 requests for 256 workgroups per round
+    (24, 128, 8, 64, 9000, 2),     # two row groups of 64 rows: 192 requests for 128 per round
+]
+
+
+@pytest.mark.parametrize("B,H_,N,P,smax,seed", MANY)
+def test_one_launch_many_requests_every_element(B, H_, N, P, smax, seed):
+    # log-uniform lengths with the shortest forced in (1..5, an empty stripe on most ranks)
+    rng = np.random.default_rng(seed)
+    lens = np.exp(rng.uniform(0, np.log(smax), B)).astype(np.int64).clip(1, smax)
+    lens[:5] = [1, 2, 3, 4, 5]
+    w, lens = custom(B, H_, 1, N, P, lens.tolist(), "2")
+    print(f"one launch, many requests B={B} H={H_} N={N} lens[:8]={lens[:8].tolist()}", flush=True)
+    s = H.make_setup(w, 1, lens=lens)
+    mo, ml = dcp.dcp_stripe_attn_multi(s.lay, list(range(N)), s.q, s.sp.pools, s.sp.tables, s.sp.seq_len,
+                                       workloads.SCALE, s.base_flag, status=s.status)
+    o, lse = dcp.dcp_lse_merge(mo, ml, s.base_flag)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    for b in range(B):
+        H.check_request(s, mo, ml, o, lse, b)

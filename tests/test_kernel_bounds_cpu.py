@@ -206,37 +206,78 @@ def test_work_list_fits_the_grid_and_partitions_every_request():
                     assert max(cs for (_, _, _, cs) in wl) <= (min(cap, GROUP_CHUNK) if mgroups > 1 else cap)
 
 
+def chunk_class(cs):
+    """The kernel's chunk class: chunks of about 2**(30 - key) tiles; 31 = empty."""
+    return 30 - (int(cs).bit_length() - 1) if cs > 0 else 31
+
+
+def class_order(tiles, target, mgroups=1):
+    """The many-request plan (target <= requests): the same chunks as
+    work_list, numbered class by class, longest class first, request by
+    request inside a class.  Returns [(b, k, n, cs)] in chunk order."""
+    wl = work_list(tiles, 0, target, mgroups)
+    per_req = {}
+    for (b, k, n, cs) in wl:
+        per_req.setdefault(b, []).append((b, k, n, cs))
+    out = []
+    for key in range(32):
+        for b in range(len(tiles)):
+            chunks = per_req[b]
+            if chunk_class(chunks[0][3]) == key:
+                out += chunks
+    return out
+
+
+def test_class_order_is_longest_first_and_keeps_requests_together():
+    rng = np.random.default_rng(9)
+    for trial in range(60):
+        B = int(rng.integers(257, 1200))
+        tiles = [int(x) for x in np.exp(rng.uniform(0, np.log(300), B)).astype(int)]
+        tiles[:7] = [0, 1, 2, 3, 0, 5, 6]
+        target = 256
+        order = class_order(tiles, target)
+        assert sorted(order) == sorted(work_list(tiles, 0, target))       # the same chunks
+        keys = [chunk_class(cs) for (_, _, _, cs) in order]
+        assert keys == sorted(keys)                                        # longest class first
+        # a request's chunks are consecutive, k = 0..n-1
+        pos = {}
+        for c, (b, k, n, cs) in enumerate(order):
+            pos.setdefault(b, []).append((c, k))
+        for b, ck in pos.items():
+            cs_ = [c for c, _ in ck]
+            assert cs_ == list(range(cs_[0], cs_[0] + len(cs_))) and [k for _, k in ck] == list(range(len(ck)))
+        assert len(order) <= target + B                                    # the plan's slot bound
+
+
 def chunk_table(tiles, forced, target, slots, mgroups=1, plant=None):
-    """The chunk table the kernel writes (chunks of request b, first chunk of
-    b): a request whose chunks would run past the workspace's slots is cut
-    to the slots that exist."""
-    wl = work_list(tiles, forced, target, mgroups)
-    n = {}
-    for (b, k, nb, cs) in wl:
-        n[b] = nb
-    table, excl, flagged = [], 0, False
-    for b in range(len(tiles)):
-        nb = n[b]
-        incl = excl + nb
-        fit = nb if (incl <= slots or plant == "no_table_clamp") else max(slots - excl, 0)
-        flagged |= fit != nb
-        table.append((fit, excl))
-        excl = incl
-    return table, flagged
+    """The chunk table the combine reads in the many-request plan: each
+    request's first chunk, if it has a workgroup (chunk index < slots), writes
+    (chunks cut to the slots there are, first chunk); the call is flagged when
+    the chunks outnumber the slots."""
+    order = class_order(tiles, target, mgroups)
+    table, flagged = {}, len(order) > slots
+    for c, (b, k, n, cs) in enumerate(order):
+        if k == 0 and c < slots:
+            fit = n if (c + n <= slots or plant == "no_table_clamp") else slots - c
+            flagged |= fit != n
+            table[b] = (fit, c)
+    return list(table.values()), flagged
 
 
 def test_chunk_table_never_points_past_the_workspace():
     """Device lengths past the page table's capacity (the plan sizes the
-    workspace from the table) on the capped row-group path: the table is cut
-    to the slots, so the combine reads inside the workspace, and the call is
-    flagged; within capacity nothing is cut."""
+    workspace from the table) on the capped row-group path: every entry the
+    combine can read is cut to the slots, so it reads inside the workspace,
+    and the call is flagged; within capacity nothing is cut.  (An entry no
+    workgroup writes is rejected by the combine's own range check.)"""
     B, cols, P, M = 256, 256, 64, 384                  # 4 row groups of 96 rows: capped chunks
     W, mgroups, slots, forced, target = plan(B, M, cols, P)
     assert mgroups > 1 and target <= B
     fits = [cdiv(cols * P, TILE)] * B                  # every request at the table's capacity
     table, flagged = chunk_table(fits, forced, target, slots, mgroups)
-    assert not flagged and all(c0 + n <= slots for n, c0 in table)
+    assert not flagged and len(table) == B and all(c0 + n <= slots for n, c0 in table)
     over = [8 * cdiv(cols * P, TILE)] * B               # lengths 8x the capacity
+    over[0] = 3 * GROUP_CHUNK                           # (so that one request's chunks straddle the last slot)
     table, flagged = chunk_table(over, forced, target, slots, mgroups)
     assert flagged and all(c0 + n <= slots for n, c0 in table if n > 0)
     table, _ = chunk_table(over, forced, target, slots, mgroups, plant="no_table_clamp")
