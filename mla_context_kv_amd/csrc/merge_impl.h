@@ -1,6 +1,7 @@
-// Exact LSE merge kernel shared by dcp_lse_merge (merge across stripes) and
-// the split-KV combine of dcp_stripe_attn (merge across the KV chunks of one
-// stripe).  Both are the same operation: the softmax numerator and
+// Exact LSE merge kernel of dcp_lse_merge (merge across stripes), and the wave
+// reductions and constants it shares with the split-KV combine of
+// dcp_stripe_attn (merge across the KV chunks of one stripe, whose bf16 body
+// sits beside the attention kernel).  Both are the same operation: the softmax numerator and
 // denominator are sums over a disjoint partition of the visible positions
 // (page "DCP" (zdszero), "theory": merge identity, merge operator and
 // numerical stability; the FlashAttention-style split inside a stripe is the
@@ -45,21 +46,6 @@ struct Fp32Out {
   __device__ void o4(int c, float4 v) const { o[c] = v; }
   __device__ bool has_lse() const { return l != nullptr; }
   __device__ void lse(float x) const { *l = x; }
-};
-// RecordOut: one packed record -- v4 * 4 bf16 values (round to nearest even),
-// then the float32 lse in the next two 16-bit slots and two zero slots (the
-// head-return record, 8-byte aligned).
-struct RecordOut {
-  uint2* __restrict__ rec;
-  int32_t v4;
-  __device__ void o4(int c, float4 v) const {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
-    rec[c] = __builtin_bit_cast(uint2, h);
-  }
-  __device__ bool has_lse() const { return true; }
-  __device__ void lse(float x) const { rec[v4] = make_uint2(__float_as_uint(x), 0u); }
 };
 
 // Merge of one row by one wavefront.  `src` gives part r's lse (src.lse(r))
@@ -209,33 +195,6 @@ __device__ __forceinline__ void merge_one_row(int32_t N, int64_t stride, int32_t
                                               float* __restrict__ lse_out) {
   const Fp32Parts src{o_parts, lse_parts, stride, v4};
   const Fp32Out dst{o_row, lse_out};
-  if (N <= kAtOnceParts && v4 <= 128)
-    merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, dst);
-  else
-    merge_row(N, v4, src, in_base2, out_base2, dst);
-}
-
-// bf16 parts (the chunk partials of a stripe): part r of the row's o at
-// o[r * stride * v4 ...] as 4 bf16 per 8-byte unit, its lse at l[r * stride];
-// widened to fp32 in registers (a bf16 is the top half of a float32)
-struct Bf16Parts {
-  const uint2* __restrict__ o;
-  const float* __restrict__ l;
-  int64_t stride;
-  int32_t v4;
-  __device__ float lse(int r) const { return l[(int64_t)r * stride]; }
-  __device__ float4 o4(int r, int c) const {
-    const uint2 u = o[(int64_t)r * stride * v4 + c];
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-  }
-};
-
-template <class Dst>
-__device__ __forceinline__ void merge_bf16_row(int32_t N, int64_t stride, int32_t v4, const uint2* __restrict__ o_parts,
-                                               const float* __restrict__ lse_parts, int32_t in_base2, int32_t out_base2,
-                                               const Dst& dst) {
-  const Bf16Parts src{o_parts, lse_parts, stride, v4};
   if (N <= kAtOnceParts && v4 <= 128)
     merge_row_at_once<kAtOnceParts>(N, v4, src, in_base2, out_base2, dst);
   else

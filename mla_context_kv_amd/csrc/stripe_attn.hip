@@ -1260,33 +1260,99 @@ int make_plan(const dcp_attn_args* args, int32_t n, Plan* pl) {
   return DCP_OK;
 }
 
-// Merge of each request's chunks (one wavefront per output row): requests cut
+// Merge of each request's chunks (one wavefront per output row, 16-byte
+// loads of the bf16 partials, 8 chunks in flight at once): requests cut
 // into one chunk were written by the attention kernel itself and are left
 // alone; the chunks partition the request's rows, so their partials merge
 // exactly like stripes (base-2 partial lse).
-__global__ void __launch_bounds__(64 * kMergeRowsPerBlock)
-chunk_combine_kernel(Params p) {
+constexpr int kCombineWaves = 4;       // wavefronts per block, one output row each
+constexpr int kCombineGroup = 8;       // chunk partials loaded at once
+
+__global__ void __launch_bounds__(64 * kCombineWaves) chunk_combine_kernel(Params p) {
   int64_t bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-  const int64_t row = bid * kMergeRowsPerBlock + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
   const int64_t Bv = (int64_t)p.nr * p.B;
+  const int64_t row = bid * kCombineWaves + (threadIdx.x >> 6);
   if (row >= Bv * p.M) return;
-  const int32_t v = (int32_t)(row / p.M), m = (int32_t)(row % p.M);
+  const int32_t v = (int32_t)(row / p.M), m = (int32_t)(row - (int64_t)v * p.M);
   const int32_t n = p.table[v];
-  if (n <= 1) return;
+  if (n <= 1) return;                        // one chunk: written by the attention kernel
   const int64_t c0 = p.table[Bv + v];
   if (c0 < 0 || c0 + n > p.slots) return;   // (never written so: entries are cut to the slots)
   const int32_t ri = v / p.B, b = v - ri * p.B;
   const RankPtrs& rk = p.rk[ri];
-  constexpr int v4 = kDV / 4;
   const int64_t out = (int64_t)b * p.M + m;
-  const uint2* const parts = reinterpret_cast<const uint2*>(p.ws_o) + (c0 * p.M + m) * v4;
-  if (p.records)
-    merge_bf16_row(n, p.M, v4, parts, p.ws_lse + c0 * p.M + m, 1, p.out_base2,
-                   RecordOut{rk.rec + rec_index(p, 0, b, m) * (v4 + 1), v4});
-  else
-    merge_bf16_row(n, p.M, v4, parts, p.ws_lse + c0 * p.M + m, 1, p.out_base2,
-                   Fp32Out{reinterpret_cast<float4*>(rk.o) + out * v4, rk.lse + out});
+  constexpr int v4 = kDV / 4;
+  // lane l takes values 8l .. 8l+7 (16 bytes of bf16) of each part,
+  // kCombineGroup parts in flight at once; the lse of parts r0 .. r0+63 sit
+  // one per lane (base 2).  The first group's loads go out with the lse's.
+  const float* const lse0 = p.ws_lse + c0 * p.M + m;
+  const uint4* const part0 = reinterpret_cast<const uint4*>(p.ws_o + (c0 * p.M + m) * kDV) + lane;
+  const int64_t part_stride = p.M * (kDV / 8);
+  float lp = lane < n ? lse0[(int64_t)lane * p.M] : -INFINITY;
+  uint4 x[kCombineGroup];
+#pragma unroll
+  for (int k = 0; k < kCombineGroup; ++k)
+    x[k] = k < n ? part0[k * part_stride] : make_uint4(0u, 0u, 0u, 0u);
+  float mx = lp;
+  for (int r0 = 64; r0 < n; r0 += 64)
+    if (r0 + lane < n) mx = fmaxf(mx, lse0[(int64_t)(r0 + lane) * p.M]);
+  mx = wave_max(mx);
+  // the exact merge: weights 2^(lse_k - max) / sum; parts of weight zero are
+  // selected away, whatever they hold
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse_out = -INFINITY;
+  if (mx != -INFINITY) {
+    float wsum = lp == -INFINITY ? 0.f : exp2f(lp - mx);
+    for (int r0 = 64; r0 < n; r0 += 64) {
+      const float l = r0 + lane < n ? lse0[(int64_t)(r0 + lane) * p.M] : -INFINITY;
+      wsum += l == -INFINITY ? 0.f : exp2f(l - mx);
+    }
+    wsum = wave_sum(wsum);
+    const float inv = 1.0f / wsum;
+    float w = lp == -INFINITY ? 0.f : exp2f(lp - mx) * inv;   // lane k: weight of part r0 + k
+    for (int g = 0; g < n; g += kCombineGroup) {
+      if (g > 0) {
+        if ((g & 63) == 0) {
+          lp = g + lane < n ? lse0[(int64_t)(g + lane) * p.M] : -INFINITY;
+          w = lp == -INFINITY ? 0.f : exp2f(lp - mx) * inv;
+        }
+#pragma unroll
+        for (int k = 0; k < kCombineGroup; ++k)
+          x[k] = g + k < n ? part0[(g + k) * part_stride] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < kCombineGroup; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (g + k) & 63));
+        if (g + k < n && wk != 0.f) {
+          const uint32_t u[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += wk * __uint_as_float(u[q] << 16);
+            acc[2 * q + 1] += wk * __uint_as_float(u[q] & 0xffff0000u);
+          }
+        }
+      }
+    }
+    const float lw2 = log2f(wsum);
+    lse_out = p.out_base2 ? mx + lw2 : (mx + lw2) * kLn2;
+  }
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  if (p.records) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    uint2* const rec = rk.rec + rec_index(p, 0, b, m) * (v4 + 1);
+    const bf16x4_t h0 = __builtin_convertvector((f32x4_t){acc[0], acc[1], acc[2], acc[3]}, bf16x4_t);
+    const bf16x4_t h1 = __builtin_convertvector((f32x4_t){acc[4], acc[5], acc[6], acc[7]}, bf16x4_t);
+    rec[2 * lane] = __builtin_bit_cast(uint2, h0);
+    rec[2 * lane + 1] = __builtin_bit_cast(uint2, h1);
+    if (lane == 0) rec[v4] = make_uint2(__float_as_uint(lse_out), 0u);
+  } else {
+    float4* const o = reinterpret_cast<float4*>(rk.o) + out * v4;
+    o[2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (lane == 0) rk.lse[out] = lse_out;
+  }
 }
 
 template <int RB, bool kLogit>
@@ -1376,8 +1442,8 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
   }
   if (r != DCP_OK || !pl.combine) return r;
   const int64_t rows = pl.Bv * M;
-  hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)ceil_div(rows, kMergeRowsPerBlock)),
-                     dim3(64 * kMergeRowsPerBlock), 0, s, prm);
+  hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)ceil_div(rows, kCombineWaves)),
+                     dim3(64 * kCombineWaves), 0, s, prm);
   return launch_status();
 }
 
