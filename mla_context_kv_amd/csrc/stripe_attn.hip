@@ -386,12 +386,14 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
 // the compute units that free up later: a longest-first order for launches of
 // several rounds of workgroups.
 constexpr int kClasses = 32;
-static_assert(kTableMax * 16 + (1 + kClasses) * 4 <= kStageBytes, "request table and class counts fit one stage");
 __device__ __forceinline__ int32_t chunk_class(int32_t cs) { return cs > 0 ? 30 - (31 - __builtin_clz(cs)) : 31; }
 
 // The many-request plan (more requests than workgroups per round): chunks of
-// the mean per-CU share C, numbered in classes.  `tab` holds every request's
-// shape; `cls` [kClasses] the chunks of each class (filled by the workgroup).
+// the mean per-CU share C, numbered by class (longest chunks first) and in
+// request order within a class.  `tab` holds every request's shape, `cls`
+// [kClasses] the chunks of each class (filled by the workgroup).  Each wave
+// finds chunk c itself, with one scan over the requests per 64 of them: the
+// form for a few hundred requests.
 __device__ __forceinline__ WorkItem find_work_classes(const Params& p, int32_t c, const int4* tab,
                                                       const int32_t* cls, int32_t C) {
   const int lane = threadIdx.x & 63;
@@ -439,6 +441,91 @@ __device__ __forceinline__ WorkItem find_work_classes(const Params& p, int32_t c
       return w;
     }
     carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return w;
+}
+
+// The same numbering found by the whole workgroup, for many requests (above
+// kBlockFind): each thread takes a contiguous run of requests, so one scan
+// over the threads finds the request of chunk c, where a wave alone would
+// scan 64 requests at a time.  Called by every thread of the workgroup (it
+// holds two barriers); aux[1 + key] holds the chunks of each class,
+// aux[kAuxWaves ..] and aux[kAuxFound ..] are scratch.
+constexpr int kBlockFind = 512;
+constexpr int kAuxWaves = 1 + kClasses;          // [kNW]: chunks of the class in each wave's runs
+constexpr int kAuxFound = kAuxWaves + kNW;       // [4]: request, chunk of it, its chunks, chunk length
+static_assert(kTableMax * 16 + (kAuxFound + 4) * 4 <= kStageBytes, "request table and its scratch fit one stage");
+__device__ __forceinline__ WorkItem find_work_block(const Params& p, int32_t c, const int4* tab, int32_t* aux,
+                                                    int32_t C) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t Bv = p.nr * p.B;
+  // the class of chunk c and its rank r in the class, from the per-class counts
+  const int32_t cnt = lane < kClasses ? aux[1 + lane] : 0;
+  int32_t x = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  const uint64_t in_class = __builtin_amdgcn_ballot_w64(x - cnt <= c && c < x);
+  const int key = in_class != 0 ? __builtin_ctzll(in_class) : -1;      // -1: past the last chunk
+  const int32_t r = key >= 0 ? c - (__builtin_amdgcn_readlane(x, key) - __builtin_amdgcn_readlane(cnt, key)) : 0;
+  // the chunks of class `key` in this thread's run of requests
+  const int32_t q = (Bv + 64 * kNW - 1) / (64 * kNW);
+  const int32_t v0 = (int32_t)threadIdx.x * q;
+  int32_t s = 0;
+  for (int32_t j = 0; j < q; ++j) {
+    const int32_t v = v0 + j;
+    if (v < Bv) {
+      const int32_t tv = tab[v].x;
+      const int32_t nb = max(cdiv(tv, C), 1);
+      if (chunk_class(tv > 0 ? cdiv(tv, nb) : 0) == key) s += nb;
+    }
+  }
+  int32_t incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) aux[kAuxWaves + wave] = incl;
+  if (threadIdx.x == 0) aux[kAuxFound] = -1;
+  __syncthreads();
+  int32_t excl = incl - s;
+  for (int w = 0; w < wave; ++w) excl += aux[kAuxWaves + w];
+  if (s > 0 && excl <= r && r < excl + s) {
+    // the one thread whose run holds chunk r of the class
+    int32_t acc = excl;
+    for (int32_t j = 0; j < q; ++j) {
+      const int32_t v = v0 + j;
+      if (v >= Bv) break;
+      const int32_t tv = tab[v].x;
+      const int32_t nb = max(cdiv(tv, C), 1);
+      const int32_t cs = tv > 0 ? cdiv(tv, nb) : 0;
+      if (chunk_class(cs) != key) continue;
+      if (r < acc + nb) {
+        aux[kAuxFound] = v;
+        aux[kAuxFound + 1] = r - acc;
+        aux[kAuxFound + 2] = nb;
+        aux[kAuxFound + 3] = cs;
+        break;
+      }
+      acc += nb;
+    }
+  }
+  __syncthreads();
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
+  const int32_t vf = aux[kAuxFound];
+  if (vf >= 0) {
+    w.live = true;
+    w.b = vf;
+    w.k = aux[kAuxFound + 1];
+    w.n = aux[kAuxFound + 2];
+    w.cs = aux[kAuxFound + 3];
+    const int4 e = tab[vf];
+    w.rows = e.y;
+    w.ft = e.z;
+    w.S = e.w;
   }
   return w;
 }
@@ -573,9 +660,10 @@ stripe_attn_kernel(Params p) {
   WorkItem wi;
   if (p.partials > 0) {
     wi = part_work(p, chunk);
-  } else if (classes) {
-    const int32_t* const aux = reinterpret_cast<const int32_t*>(table + kTableMax);
-    wi = find_work_classes(p, chunk, table, aux + 1, C);
+  } else if (__builtin_expect(classes, 0)) {   // (placed out of the way of the common path's code)
+    int32_t* const aux = reinterpret_cast<int32_t*>(smem + (kStages - 1) * kStageBytes) + 4 * kTableMax;
+    wi = Bv > kBlockFind ? find_work_block(p, chunk, table, aux, C)      // (uniform in the workgroup)
+                         : find_work_classes(p, chunk, table, aux + 1, C);
     if (p.table != nullptr && mg == 0 && wave == 0 && lane == 0) {
       // the chunk table the combine reads: each request's first chunk writes
       // its entry (cut to the slots there are; chunks without a workgroup

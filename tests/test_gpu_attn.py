@@ -422,6 +422,8 @@ MANY = [
     # plan cuts chunks of the mean per-CU share and numbers them longest class first
     (48, 32, 8, 64, 6000, 1),      # one row group: 384 requests for 256 workgroups per round
     (24, 128, 8, 64, 9000, 2),     # two row groups of 64 rows: 192 requests for 128 per round
+    (80, 32, 8, 64, 5000, 3),      # 640 requests: the workgroup-wide lookup (above 512 requests)
+    (72, 128, 8, 64, 3000, 4),     # 576 requests in two row groups, workgroup-wide lookup
 ]
 
 

@@ -249,6 +249,60 @@ def test_class_order_is_longest_first_and_keeps_requests_together():
         assert len(order) <= target + B                                    # the plan's slot bound
 
 
+def block_find(tiles, target, c, threads=512, plant=None):
+    """The workgroup-wide lookup of the many-request plan (above 512
+    requests): thread i takes the contiguous run of requests i*q .. i*q+q-1,
+    counts the chunks of chunk c's class in its run, and the one thread whose
+    prefix range holds c's rank in the class walks its run.  Returns
+    (b, k, n, cs) or None past the last chunk."""
+    B = len(tiles)
+    C = max(cdiv(int(sum(tiles)), target), 1)
+    nb = [max(cdiv(t, C), 1) for t in tiles]
+    cs = [cdiv(t, n) if t > 0 else 0 for t, n in zip(tiles, nb)]
+    key = [chunk_class(x) for x in cs]
+    counts = [sum(n for n, k in zip(nb, key) if k == kk) for kk in range(32)]
+    incl = np.cumsum(counts)
+    hit = [kk for kk in range(32) if incl[kk] - counts[kk] <= c < incl[kk]]
+    if not hit:
+        return None
+    kk = hit[0]
+    r = c - (incl[kk] - counts[kk])
+    q = cdiv(B, threads)
+    runs = [range(i * q, min(i * q + q, B)) for i in range(threads)]
+    s = [sum(nb[v] for v in run if key[v] == kk) for run in runs]
+    excl = 0
+    for i, run in enumerate(runs):
+        lo = excl + (1 if plant == "off_by_one" else 0)
+        if s[i] > 0 and lo <= r < excl + s[i]:
+            acc = excl
+            for v in run:
+                if key[v] != kk:
+                    continue
+                if r < acc + nb[v]:
+                    return (v, r - acc, nb[v], cs[v])
+                acc += nb[v]
+        excl += s[i]
+    return "lost"
+
+
+def test_block_find_is_the_class_order():
+    """Over random many-request batches (more requests than threads, fewer,
+    empty ones), the workgroup-wide lookup finds for every chunk the request
+    and chunk that the class order numbers there, and nothing past the end; a
+    planted off-by-one in the prefix test is caught."""
+    rng = np.random.default_rng(13)
+    for trial in range(24):
+        B = int(rng.integers(513, 2305)) if trial % 3 else int(rng.integers(257, 600))
+        tiles = [int(x) for x in np.exp(rng.uniform(0, np.log(400), B)).astype(int)]
+        tiles[:5] = [0, 1, 0, 3, 2]
+        order = class_order(tiles, 256)
+        for c in list(range(0, len(order), max(1, len(order) // 97))) + [len(order) - 1]:
+            assert block_find(tiles, 256, c) == order[c]
+        assert block_find(tiles, 256, len(order)) is None
+    bad = [block_find(tiles, 256, c, plant="off_by_one") for c in range(len(order))]
+    assert any(x != order[c] for c, x in enumerate(bad))
+
+
 def chunk_table(tiles, forced, target, slots, mgroups=1, plant=None):
     """The chunk table the combine reads in the many-request plan: each
     request's first chunk, if it has a workgroup (chunk index < slots), writes
