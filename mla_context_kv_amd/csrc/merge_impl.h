@@ -26,16 +26,38 @@ constexpr int kMergeRowsPerBlock = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Reductions over the wave's 64 lanes (every lane active), with a
+// wave-uniform result: shifts of 1, 2, 4 and 8 lanes inside each row of 16
+// leave each row's total in its lane 15, and the row broadcasts of lanes 15
+// and 31 gather them in lane 63 -- cross-lane data paths of the VALU (DPP),
+// where a shuffle through the LDS crossbar costs a round trip per step.  A
+// lane with no source (past the row start, or a row the step leaves alone)
+// reads the operation's identity.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_or(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), kCtrl,
+                                                    kRowMask, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-  return v;
+  const float id = -INFINITY;
+  v = fmaxf(v, dpp_or<0x111, 0xf>(id, v));   // row_shr:1
+  v = fmaxf(v, dpp_or<0x112, 0xf>(id, v));   // row_shr:2
+  v = fmaxf(v, dpp_or<0x114, 0xf>(id, v));   // row_shr:4
+  v = fmaxf(v, dpp_or<0x118, 0xf>(id, v));   // row_shr:8
+  v = fmaxf(v, dpp_or<0x142, 0xa>(id, v));   // row_bcast:15 into rows 1 and 3
+  v = fmaxf(v, dpp_or<0x143, 0xc>(id, v));   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  v += dpp_or<0x111, 0xf>(0.f, v);
+  v += dpp_or<0x112, 0xf>(0.f, v);
+  v += dpp_or<0x114, 0xf>(0.f, v);
+  v += dpp_or<0x118, 0xf>(0.f, v);
+  v += dpp_or<0x142, 0xa>(0.f, v);
+  v += dpp_or<0x143, 0xc>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Where a merged row goes: its v4 16-byte column slices (c) and its lse.

@@ -207,16 +207,22 @@ __device__ __forceinline__ int32_t count_rows(int32_t x, int32_t N, int32_t I, i
   return (x / round) * I + rem;
 }
 
-__device__ __forceinline__ int32_t wave_sum_i(int32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+// Inclusive prefix sum over the wave's 64 lanes (every lane active): shifts
+// of 1, 2, 4 and 8 lanes inside each row of 16, then each row's total carried
+// into the rows above it by the row broadcasts of lanes 15 and 31.  Cross-lane
+// data paths of the VALU (DPP), a few cycles each, where a shuffle through
+// the LDS crossbar waits on a memory round trip per step.
+__device__ __forceinline__ int32_t wave_scan_i(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2 and 3
   return v;
 }
-__device__ __forceinline__ int32_t wave_max_i(int32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
-  return v;
-}
+// the wave's total (every lane active), wave-uniform
+__device__ __forceinline__ int32_t wave_sum_i(int32_t v) { return __builtin_amdgcn_readlane(wave_scan_i(v), 63); }
 __device__ __forceinline__ int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // Work list of one launch.  Request b's local rows (what its last query
@@ -334,12 +340,7 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       if (p.forced_splits > 0) nb = t > 0 ? cdiv(t, cdiv(t, p.forced_splits)) : 1;
       else nb = max(cdiv(t, C), 1);
     }
-    int32_t x = nb;                                // inclusive scan over the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
-    }
+    const int32_t x = wave_scan_i(nb);             // inclusive scan over the wave
     const int32_t incl = carry + x, excl = incl - nb;
     if (write_table && b < Bv) {
       // Device lengths beyond the page table's capacity can ask for more
@@ -401,12 +402,7 @@ __device__ __forceinline__ WorkItem find_work_classes(const Params& p, int32_t c
   WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
   // the class of chunk c, from the per-class counts
   const int32_t cnt = lane < kClasses ? cls[lane] : 0;
-  int32_t x = cnt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int32_t x = wave_scan_i(cnt);
   const uint64_t in_class = __builtin_amdgcn_ballot_w64(x - cnt <= c && c < x);
   if (in_class == 0) return w;                   // past the last chunk
   const int key = __builtin_ctzll(in_class);
@@ -419,12 +415,7 @@ __device__ __forceinline__ WorkItem find_work_classes(const Params& p, int32_t c
     const int32_t nb = max(cdiv(t, C), 1);
     const int32_t cs = t > 0 ? cdiv(t, nb) : 0;
     const int32_t mine = b < Bv && chunk_class(cs) == key ? nb : 0;
-    int32_t y = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t z = __shfl_up(y, d, 64);
-      if (lane >= d) y += z;
-    }
+    const int32_t y = wave_scan_i(mine);
     const int32_t incl = carry + y, excl = incl - mine;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(mine > 0 && excl <= r && r < incl);
     if (hit != 0) {
@@ -461,12 +452,7 @@ __device__ __forceinline__ WorkItem find_work_block(const Params& p, int32_t c, 
   const int32_t Bv = p.nr * p.B;
   // the class of chunk c and its rank r in the class, from the per-class counts
   const int32_t cnt = lane < kClasses ? aux[1 + lane] : 0;
-  int32_t x = cnt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int32_t x = wave_scan_i(cnt);
   const uint64_t in_class = __builtin_amdgcn_ballot_w64(x - cnt <= c && c < x);
   const int key = in_class != 0 ? __builtin_ctzll(in_class) : -1;      // -1: past the last chunk
   const int32_t r = key >= 0 ? c - (__builtin_amdgcn_readlane(x, key) - __builtin_amdgcn_readlane(cnt, key)) : 0;
@@ -482,12 +468,7 @@ __device__ __forceinline__ WorkItem find_work_block(const Params& p, int32_t c, 
       if (chunk_class(tv > 0 ? cdiv(tv, nb) : 0) == key) s += nb;
     }
   }
-  int32_t incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
+  const int32_t incl = wave_scan_i(s);
   if (lane == 63) aux[kAuxWaves + wave] = incl;
   if (threadIdx.x == 0) aux[kAuxFound] = -1;
   __syncthreads();
