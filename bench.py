@@ -490,6 +490,15 @@ def main():
     else:
         achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
+    # the same launch's matrix rate: each rank's share of the step's FLOPs
+    # (in proportion to its latent rows) over its duration
+    rows_r = np.asarray(local, dtype=np.float64).sum(axis=0)
+    stripe_flops = flops * rows_r / max(rows_r.sum(), 1.0)
+    if args.multi:
+        achieved_tf = float(stripe_flops.sum() / (launch_ms[0] * 1e-3)) / 1e12
+    else:
+        achieved_tf = float(np.mean(stripe_flops / (launch_ms * 1e-3))) / 1e12
+    mfma_bound = flops / max(kv_bytes, 1.0) > MFMA_BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3)
 
     secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
                      or args.multi or args.streams > 1 or args.graph or args.records)
@@ -499,7 +508,7 @@ def main():
     if not args.no_probe:
         probe = probe_pools(args, sp.pools, N, stream, dev)
     mfma_peak = None
-    if not args.no_probe and flops / max(kv_bytes, 1.0) > MFMA_BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3):
+    if not args.no_probe and mfma_bound:
         # above the spec ridge the step is MFMA-bound: its rate against the MFMA probe's
         mfma_peak, _, _, _ = mfma_probe_steps(N, 5, 2, stream, dev)
 
@@ -582,6 +591,20 @@ def main():
         out["roofline"]["measured_peak"] = round(peak, 1)
         out["roofline"]["frac_of_measured"] = round(achieved / peak, 4)
         out["roofline"]["measured_peak_probe"] = probe
+    if mfma_bound:
+        # above the spec ridge (312.5 FLOP per byte) the launch is bound by the
+        # matrix cores: its rate against the bf16 MFMA peaks, with the memory
+        # view kept beside it
+        hbm_view = {k: out["roofline"].pop(k) for k in ("achieved", "peak", "unit", "frac", "measured_peak",
+                                                       "frac_of_measured", "measured_peak_probe")
+                    if k in out["roofline"]}
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(achieved_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           **({"measured_peak": round(mfma_peak, 1),
+                               "frac_of_measured": round(achieved_tf / mfma_peak, 4)} if mfma_peak else {}),
+                           "flops_per_launch": int(stripe_flops.sum() if args.multi else stripe_flops.mean()),
+                           **{k: v for k, v in out["roofline"].items() if k != "bound"},
+                           "hbm_view": hbm_view}
     print(json.dumps(out), flush=True)
     if parity is not None and not parity["ok"]:
         print("parity check against the oracle FAILED", file=sys.stderr)
