@@ -322,12 +322,21 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
       C = max(cdiv(total, target), 1);
       if (p.mgroups > 1) C = min(C, kGroupChunkTiles);
     } else {
-      C = max(cdiv(total, target), 1);
-      const int32_t T0 = chunks_for(C);
-      if (T0 > target) {
-        const int32_t C1 = cdiv(C * T0, target);
-        C = chunks_for(C1) <= target ? C1 : max(cdiv(total, target - Bv), 1);
+      // the shortest chunk length whose chunks fit one round of `target`
+      // workgroups: the count falls as the length grows, and the mean share
+      // of target - Bv units always fits (at most one extra chunk per
+      // request), so a bisection between the two finds it
+      int32_t lo = max(cdiv(total, target), 1);
+      if (chunks_for(lo) > target) {
+        int32_t hi = max(cdiv(total, target - Bv), 1);
+        ++lo;
+        while (lo < hi) {
+          const int32_t mid = lo + (hi - lo) / 2;
+          if (chunks_for(mid) <= target) hi = mid;
+          else lo = mid + 1;
+        }
       }
+      C = lo;
     }
   }
   WorkItem w{0, 0, 0, 0, 0, 0, 0, false};

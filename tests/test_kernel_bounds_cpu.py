@@ -155,10 +155,15 @@ def work_list(tiles, forced, target, mgroups=1):
                 C = min(C, GROUP_CHUNK)
         else:
             C = max(cdiv(total, target), 1)
-            T0 = chunks_for(C)
-            if T0 > target:
-                C1 = cdiv(C * T0, target)
-                C = C1 if chunks_for(C1) <= target else max(cdiv(total, target - B), 1)
+            if chunks_for(C) > target:               # the shortest length that fits one round, by bisection
+                lo, hi = C + 1, max(cdiv(total, target - B), 1)
+                while lo < hi:
+                    mid = lo + (hi - lo) // 2
+                    if chunks_for(mid) <= target:
+                        hi = mid
+                    else:
+                        lo = mid + 1
+                C = lo
         n = [max(cdiv(t, C), 1) for t in tiles]
     out = []
     for b, t in enumerate(tiles):
@@ -204,6 +209,25 @@ def test_work_list_fits_the_grid_and_partitions_every_request():
                     # no chunk longer than the mean share of a compute unit (nor the group cap)
                     cap = cdiv(int(tiles.sum()), target)
                     assert max(cs for (_, _, _, cs) in wl) <= (min(cap, GROUP_CHUNK) if mgroups > 1 else cap)
+
+
+def test_one_round_chunk_length_is_the_shortest_that_fits():
+    """Fewer requests than workgroups: the balanced list's chunk length is the
+    smallest whose chunk count fits one round (brute force over every
+    length), whatever the mix of short and long requests."""
+    rng = np.random.default_rng(17)
+    for trial in range(200):
+        B = int(rng.integers(1, 255))
+        tiles = [int(x) for x in np.rint(np.exp(rng.uniform(0, np.log(rng.choice([8, 300, 5000])), B)))]
+        if trial % 3 == 0:
+            tiles[: B // 2] = [1] * (B // 2)
+        target = 256
+        wl = work_list(tiles, 0, target)
+        count = lambda L: sum(max(cdiv(t, L), 1) for t in tiles)
+        best = next(L for L in range(1, max(tiles) + 2) if count(L) <= target)
+        assert len(wl) == count(best) <= target
+        # no chunk longer than that length
+        assert max(cs for (_, _, _, cs) in wl) <= best
 
 
 def chunk_class(cs):
