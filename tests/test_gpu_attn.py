@@ -424,6 +424,7 @@ MANY = [
     (24, 128, 8, 64, 9000, 2),     # two row groups of 64 rows: 192 requests for 128 per round
     (80, 32, 8, 64, 5000, 3),      # 640 requests: the workgroup-wide lookup (above 512 requests)
     (72, 128, 8, 64, 3000, 4),     # 576 requests in two row groups, workgroup-wide lookup
+    (320, 16, 8, 16, 400, 5),      # 2560 requests: past the LDS request table, every wave reads lengths itself
 ]
 
 
