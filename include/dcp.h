@@ -249,6 +249,7 @@ typedef struct dcp_attn_args {
   const int32_t* sparse_count;
   int32_t sparse_stride;
   int32_t out_records;
+  int32_t o_bf16;
 } dcp_attn_args;
 
 /* Unmerged parts (page "DCP", "unification with online softmax": the split
@@ -280,6 +281,15 @@ typedef struct dcp_attn_args {
  *           it receives gives the merged result.  `lse` is not used (may be
  *           NULL).  The float32 result is rounded once: the records equal
  *           dcp_pack_heads of the float32 outputs. */
+
+/* Outputs in bf16 (page "MLA 的 DCP", section 5: the partial a rank hands to
+ * the merge is (512 + 4) x 2 bytes per (row, head) -- the output in bf16
+ * beside its LSE):
+ * o_bf16  0: o is float32 as above.  1: `o` points to bf16 values in the same
+ *         layout ([B][q_len][H][v_dim], or [k][B][q_len][H][v_dim] with
+ *         partials = 1), each the float32 result rounded once to nearest
+ *         even; lse stays float32.  dcp_lse_merge_bf16 merges such parts.
+ *         With out_records = 1: DCP_EINVAL. */
 
 /* Workspace bytes dcp_stripe_attn needs for `args` (pointers are not read). */
 int dcp_stripe_attn_workspace(const dcp_attn_args* args, size_t* bytes);
@@ -370,6 +380,17 @@ size_t dcp_stripe_attn_noalloc_max_bytes(void);
 int dcp_lse_merge(int32_t n_stripes, int64_t rows, int32_t v_dim,
                   const float* o_parts, const float* lse_parts, int32_t lse_base,
                   float* o, float* lse, void* stream);
+
+/* dcp_lse_merge_bf16 -- the same exact merge over parts whose o is bf16 (the
+ * o_bf16 outputs of dcp_stripe_attn; page "MLA 的 DCP", section 5, bf16
+ * partials).  o_parts [N][rows][v_dim] bf16 (raw 16-bit values), lse_parts
+ * [N][rows] fp32 device; the bf16 values are widened exactly and every sum
+ * is float32.  o [rows][v_dim], lse [rows] fp32 device out (lse may be
+ * NULL).  v_dim % 8 == 0 (16-byte loads).  Zero-weight parts as in
+ * dcp_lse_merge. */
+int dcp_lse_merge_bf16(int32_t n_parts, int64_t rows, int32_t v_dim,
+                       const void* o_parts, const float* lse_parts, int32_t lse_base,
+                       float* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,4 +13,4 @@ extern "C" const char* dcp_strerror(int code) {
   }
 }
 
-extern "C" int dcp_abi_version(void) { return 8; }
+extern "C" int dcp_abi_version(void) { return 9; }

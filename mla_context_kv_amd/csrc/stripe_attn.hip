@@ -163,6 +163,7 @@ struct Params {
   float inv_scale;                  // 1 / scale: a natural-log logit term in raw-score units
   int32_t out_base2;
   int32_t records;                  // outputs as packed records (bf16 o + float32 lse) in rk.rec
+  int32_t o_bf16;                   // o (and unmerged parts) written as bf16, lse float32
   uint16_t* ws_o;                   // chunk partials: o as bf16 [slots][M][512], lse2 fp32 [slots][M]
   float* ws_lse;
   int32_t* table;                   // chunks per request [nr*B], first chunk of each request [nr*B]
@@ -1153,7 +1154,9 @@ stripe_attn_kernel(Params p) {
   // a request's only chunk (or an unmerged part) stores o itself in fp32; the
   // chunks of a request with several store their partial o as bf16 (rounded
   // to nearest even), merged by the chunk combine
-  float* const out_base = direct && !p.records ? rk.o + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
+  float* const out_base = direct && !p.records && !p.o_bf16 ? rk.o + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
+  uint16_t* const out16_base =
+      direct && p.o_bf16 ? reinterpret_cast<uint16_t*>(rk.o) + out_row0 * kDV + cgrp * kWaveCols * 32 : nullptr;
   uint2* const rec_base = direct && p.records ? rk.rec + cgrp * kWaveCols * 8 : nullptr;
   const int32_t rec_part = p.partials > 0 ? wi.k : 0;
   uint16_t* const part_base = direct ? nullptr : p.ws_o + (int64_t)chunk * p.M * kDV + cgrp * kWaveCols * 32;
@@ -1185,17 +1188,19 @@ stripe_attn_kernel(Params p) {
         const float4 v = *reinterpret_cast<const float4*>(stage + r * kEpiPitch + 4 * n);
         const int Rr = row0 + rb * 32 + r;
         if (Rr < p.M) {
-          if (direct && !p.records) {
+          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          typedef float f32x4_t __attribute__((ext_vector_type(4)));
+          if (direct && p.o_bf16) {
+            // o in bf16, 4 values (round to nearest even) per 8-byte store
+            const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
+            *reinterpret_cast<bf16x4_t*>(out16_base + (int64_t)Rr * kDV + 4 * n) = h;
+          } else if (direct && !p.records) {
             *reinterpret_cast<float4*>(out_base + (int64_t)Rr * kDV + 4 * n) = v;
           } else if (direct) {
             // packed record: 4 bf16 (round to nearest even) per 8-byte unit
-            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            typedef float f32x4_t __attribute__((ext_vector_type(4)));
             const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
             rec_base[rec_index(p, rec_part, b, Rr) * (kDV / 4 + 1) + n] = __builtin_bit_cast(uint2, h);
           } else {
-            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            typedef float f32x4_t __attribute__((ext_vector_type(4)));
             const bf16x4_t h = __builtin_convertvector((f32x4_t){v.x, v.y, v.z, v.w}, bf16x4_t);
             *reinterpret_cast<bf16x4_t*>(part_base + (int64_t)Rr * kDV + 4 * n) = h;
           }
@@ -1229,6 +1234,7 @@ int check_args(const dcp_attn_args* a) {
   if (a->window < 0 || !(a->softcap >= 0.f) || a->softcap == INFINITY) return DCP_EINVAL;
   if (a->out_records != 0 && a->out_records != 1) return DCP_EINVAL;
   if (a->out_records && a->n_heads % a->layout.n_stripes != 0) return DCP_EINVAL;
+  if (a->o_bf16 != 0 && (a->o_bf16 != 1 || a->out_records)) return DCP_EINVAL;
   if ((a->softcap > 0.f || a->bias_slopes != nullptr) && !(a->scale > 0.f)) return DCP_EINVAL;
   if (a->sparse_rows != nullptr) {
     if (a->sparse_bits == nullptr || a->sparse_count == nullptr || a->sparse_stride < 1) return DCP_EINVAL;
@@ -1250,7 +1256,7 @@ bool same_launch(const dcp_attn_args& a, const dcp_attn_args& b) {
          a.n_heads == b.n_heads && a.q == b.q && a.seq_len == b.seq_len && a.scale == b.scale &&
          a.lse_base == b.lse_base && a.num_splits == b.num_splits && a.window == b.window &&
          a.softcap == b.softcap && a.partials == b.partials && a.bias_slopes == b.bias_slopes &&
-         a.out_records == b.out_records &&
+         a.out_records == b.out_records && a.o_bf16 == b.o_bf16 &&
          (a.sparse_rows == nullptr) == (b.sparse_rows == nullptr);
 }
 
@@ -1417,8 +1423,16 @@ __global__ void __launch_bounds__(64 * kCombineWaves) chunk_combine_kernel(Param
     lse_out = p.out_base2 ? mx + lw2 : (mx + lw2) * kLn2;
   }
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  if (p.records) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  if (p.o_bf16) {
+    // o_r in bf16 (one 16-byte store per lane), lse in float32
+    const bf16x4_t h0 = __builtin_convertvector((f32x4_t){acc[0], acc[1], acc[2], acc[3]}, bf16x4_t);
+    const bf16x4_t h1 = __builtin_convertvector((f32x4_t){acc[4], acc[5], acc[6], acc[7]}, bf16x4_t);
+    uint4* const o16 = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(rk.o) + out * kDV);
+    const uint2 a0 = __builtin_bit_cast(uint2, h0), a1 = __builtin_bit_cast(uint2, h1);
+    o16[lane] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    if (lane == 0) rk.lse[out] = lse_out;
+  } else if (p.records) {
     uint2* const rec = rk.rec + rec_index(p, 0, b, m) * (v4 + 1);
     const bf16x4_t h0 = __builtin_convertvector((f32x4_t){acc[0], acc[1], acc[2], acc[3]}, bf16x4_t);
     const bf16x4_t h1 = __builtin_convertvector((f32x4_t){acc[4], acc[5], acc[6], acc[7]}, bf16x4_t);
@@ -1489,6 +1503,7 @@ int run(const dcp_attn_args* args, int32_t n, void* stream) {
   prm.inv_scale = a->scale > 0.f ? 1.0f / a->scale : 0.f;
   prm.out_base2 = a->lse_base;
   prm.records = a->out_records;
+  prm.o_bf16 = a->o_bf16;
   prm.ws_o = pl.combine ? (uint16_t*)a->workspace : nullptr;
   prm.ws_lse = pl.combine ? reinterpret_cast<float*>(prm.ws_o + (size_t)pl.slots * M * kDV) : nullptr;
   prm.table = pl.combine ? (int32_t*)((char*)a->workspace + pl.table_off) : nullptr;

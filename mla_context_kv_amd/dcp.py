@@ -75,6 +75,7 @@ class dcp_attn_args(ctypes.Structure):
         ("sparse_count", ctypes.c_void_p),
         ("sparse_stride", ctypes.c_int32),
         ("out_records", ctypes.c_int32),
+        ("o_bf16", ctypes.c_int32),
     ]
 
 
@@ -97,6 +98,7 @@ _SIGNATURES = {
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "dcp_stripe_attn_multi": (ctypes.c_int, [ctypes.POINTER(dcp_attn_args), _I32, _VP]),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "dcp_lse_merge_bf16": (ctypes.c_int, [_I32, _I64, _I32, _VP, _VP, _I32, _VP, _VP, _VP]),
     "dcp_pack_heads": (ctypes.c_int, [_I32, _I64, _I32, _I32, _VP, _VP, _VP, _VP]),
     "dcp_sparse_plan": (ctypes.c_int, [dcp_layout, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "dcp_merge_heads": (ctypes.c_int, [_I32, _I64, _I32, _VP, _I32, _VP, _VP, _VP]),
@@ -267,8 +269,10 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, window: int = 0, softcap: float = 0.0,
                     sinks: Optional[torch.Tensor] = None, partials: bool = False,
-                    bias_slopes: Optional[torch.Tensor] = None, sparse=None, records: bool = False):
-    """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]).
+                    bias_slopes: Optional[torch.Tensor] = None, sparse=None, records: bool = False,
+                    o_bf16: bool = False):
+    """One rank's stripe attention: returns (o_r fp32 [B,q_len,H,512], lse_r fp32 [B,q_len,H]);
+    with o_bf16=True o_r is bf16 (the float32 result rounded to nearest even) and lse_r float32.
 
     window / softcap / sinks / bias_slopes select the mergeable variants (sinks: fp32 [H], on one
     rank only; bias_slopes: fp32 [H], on every rank).  sparse = (rows, bits, count) from
@@ -291,6 +295,8 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     if partials and k < 1:
         raise ValueError("partials needs num_splits >= 1")
     lead = (k,) if partials else ()
+    if records and o_bf16:
+        raise ValueError("records already carry bf16 outputs: o_bf16 does not combine with them")
     if records:
         N = int(lay.n_stripes)
         if H % N:
@@ -302,7 +308,8 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
         lse = None
     else:
         if o is None:
-            o = torch.empty(lead + (B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+            o = torch.empty(lead + (B, q_len, H, V_DIM), dtype=torch.bfloat16 if o_bf16 else torch.float32,
+                            device=dev)
         if lse is None:
             lse = torch.empty(lead + (B, q_len, H), dtype=torch.float32, device=dev)
         if o.numel() != k * B * q_len * H * V_DIM or lse.numel() != k * B * q_len * H:
@@ -310,6 +317,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a = _attn_args(lay, rank, q, pool, block_table, seq_len, scale, lse_base, num_splits, workspace, o, lse, status,
                    window, softcap, 1 if partials else 0)
     a.out_records = 1 if records else 0
+    a.o_bf16 = 1 if o_bf16 else 0
     if sinks is not None and sinks.numel() != H:
         raise ValueError("sinks must hold one value per head")
     if bias_slopes is not None and bias_slopes.numel() != H:
@@ -318,7 +326,7 @@ def dcp_stripe_attn(lay: dcp_layout, rank: int, q: torch.Tensor, pool: torch.Ten
     a.pool = _ptr(pool, torch.bfloat16, "pool", dev)
     a.block_table = _ptr(block_table, torch.int32, "block_table", dev)
     a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
-    a.o = _ptr(o, torch.int16 if records else torch.float32, "o", dev)
+    a.o = _ptr(o, torch.int16 if records else (torch.bfloat16 if o_bf16 else torch.float32), "o", dev)
     a.lse = _ptr(lse, torch.float32, "lse", dev)
     a.status = _ptr(status, torch.int32, "status", dev)
     a.sinks = _ptr(sinks, torch.float32, "sinks", dev)
@@ -374,7 +382,8 @@ def dcp_stripe_attn_noalloc(lay: dcp_layout, rank: int, q: torch.Tensor, pool: t
 
 def dcp_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, lse_base: int = 0,
                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Exact merge over the leading (stripe) axis: o_parts [N, ..., V], lse_parts [N, ...]."""
+    """Exact merge over the leading (stripe) axis: o_parts [N, ..., V] (float32, or bfloat16
+    through dcp_lse_merge_bf16), lse_parts [N, ...] float32; o, lse float32."""
     dev = o_parts.device
     N = o_parts.shape[0]
     v_dim = o_parts.shape[-1]
@@ -385,11 +394,12 @@ def dcp_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, lse_base: int 
         o = torch.empty(o_parts.shape[1:], dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=dev)
-    rc = lib().dcp_lse_merge(int(N), int(rows), int(v_dim), _ptr(o_parts, torch.float32, "o_parts", dev),
-                             _ptr(lse_parts, torch.float32, "lse_parts", dev), int(lse_base),
-                             _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev),
-                             _stream(dev))
-    _check(rc, "dcp_lse_merge")
+    bf16 = o_parts.dtype == torch.bfloat16
+    fn = lib().dcp_lse_merge_bf16 if bf16 else lib().dcp_lse_merge
+    rc = fn(int(N), int(rows), int(v_dim), _ptr(o_parts, torch.bfloat16 if bf16 else torch.float32, "o_parts", dev),
+            _ptr(lse_parts, torch.float32, "lse_parts", dev), int(lse_base),
+            _ptr(o, torch.float32, "o", dev), _ptr(lse, torch.float32, "lse", dev), _stream(dev))
+    _check(rc, "dcp_lse_merge_bf16" if bf16 else "dcp_lse_merge")
     return o, lse
 
 
@@ -457,7 +467,8 @@ def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_
                           scale: float, lse_base: int = 0, num_splits: int = 0, o: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
                           window: int = 0, softcap: float = 0.0, sinks=None, bias_slopes=None, sparse=None,
-                          workspace: Optional[torch.Tensor] = None, records: bool = False):
+                          workspace: Optional[torch.Tensor] = None, records: bool = False,
+                          o_bf16: bool = False):
     """The stripe attentions of several ranks in one launch: ranks[i] with pools[i],
     block_tables[i] (and sinks[i], sparse[i] when given per rank, else None).  Returns
     o [n, B, q_len, H, 512] and lse [n, B, q_len, H], equal to n dcp_stripe_attn calls.
@@ -479,7 +490,7 @@ def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_
         lse = None
     else:
         if o is None:
-            o = torch.empty((n, B, q_len, H, V_DIM), dtype=torch.float32, device=dev)
+            o = torch.empty((n, B, q_len, H, V_DIM), dtype=torch.bfloat16 if o_bf16 else torch.float32, device=dev)
         if lse is None:
             lse = torch.empty((n, B, q_len, H), dtype=torch.float32, device=dev)
         if o.shape[0] != n or lse.shape[0] != n:
@@ -492,9 +503,10 @@ def dcp_stripe_attn_multi(lay: dcp_layout, ranks, q: torch.Tensor, pools, block_
         a.pool = _ptr(pools[i], torch.bfloat16, "pool", dev)
         a.block_table = _ptr(block_tables[i], torch.int32, "block_table", dev)
         a.seq_len = _ptr(seq_len, torch.int32, "seq_len", dev)
-        a.o = _ptr(o[i], torch.int16 if records else torch.float32, "o", dev)
+        a.o = _ptr(o[i], torch.int16 if records else (torch.bfloat16 if o_bf16 else torch.float32), "o", dev)
         a.lse = None if records else _ptr(lse[i], torch.float32, "lse", dev)
         a.out_records = 1 if records else 0
+        a.o_bf16 = 1 if o_bf16 else 0
         a.status = _ptr(status, torch.int32, "status", dev)
         a.bias_slopes = _ptr(bias_slopes, torch.float32, "bias_slopes", dev)
         if sinks is not None and sinks[i] is not None:

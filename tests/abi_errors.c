@@ -116,6 +116,17 @@ static void merges(void) {
   CHECK(dcp_lse_merge(8, 4, 512, NULL, FAKE, 0, FAKE, FAKE, NULL), DCP_EINVAL);
   CHECK(dcp_lse_merge(8, 0, 512, NULL, NULL, 0, NULL, NULL, NULL), DCP_OK);
   CHECK(dcp_lse_merge(8, INT64_MAX, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EUNSUPPORTED);
+  CHECK(dcp_lse_merge_bf16(0, 4, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, -1, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, 4, 508, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, 4, 512, FAKE, FAKE, 2, FAKE, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, 4, 512, FAKE, NULL, 0, FAKE, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, 4, 512, FAKE, FAKE, 0, NULL, FAKE, NULL), DCP_EINVAL);
+  CHECK(dcp_lse_merge_bf16(8, 0, 512, NULL, NULL, 0, NULL, NULL, NULL), DCP_OK);
+  CHECK(dcp_lse_merge_bf16(8, INT64_MAX, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EUNSUPPORTED);
+  CHECK(dcp_lse_merge_bf16(INT32_MAX, INT64_MAX / 8, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EUNSUPPORTED);
+  CHECK(dcp_lse_merge_bf16(INT32_MAX, ((int64_t)1 << 33) - 4, 512, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EUNSUPPORTED);
+  CHECK(dcp_lse_merge_bf16(2, 4, INT32_MAX - 3, FAKE, FAKE, 0, FAKE, FAKE, NULL), DCP_EINVAL);
   CHECK(dcp_pack_heads(8, 4, 12, 512, FAKE, FAKE, FAKE, NULL), DCP_EINVAL);
   CHECK(dcp_pack_heads(8, 4, 16, 510, FAKE, FAKE, FAKE, NULL), DCP_EINVAL);
   CHECK(dcp_pack_heads(8, 4, 16, 512, NULL, FAKE, FAKE, NULL), DCP_EINVAL);
@@ -155,7 +166,14 @@ static void stripe_attn_arguments(void) {
   BAD(softcap, -1.0f, DCP_EINVAL);
   BAD(partials, 2, DCP_EINVAL);
   BAD(out_records, 2, DCP_EINVAL);
+  BAD(o_bf16, 2, DCP_EINVAL);
+  BAD(o_bf16, -1, DCP_EINVAL);
 #undef BAD
+  /* bf16 outputs and records are two output forms: not both */
+  a = base_args();
+  a.out_records = 1;
+  a.o_bf16 = 1;
+  CHECK(dcp_stripe_attn(&a, NULL), DCP_EINVAL);
   /* splits need a workspace: rejected before launch when none (or too small) is given */
   a = base_args();
   a.num_splits = 3;
