@@ -1,19 +1,28 @@
 """Decode-step benchmark of DCP stripe attention + LSE merge on one MI355X.
 
-One step = the N per-rank dcp_stripe_attn launches, each at its real per-rank
+One step = the stripe attention of all N ranks, each at its real per-rank
 shape (all H query heads against that rank's stripe of every request), plus
-one dcp_lse_merge of the N partials, all on one stream with the inputs already
-resident in HBM.  Default workload: the Kimi-K3-shaped decode batch
-(B=64 requests x 131072 tokens, H=96, N=8 stripes, page 64, base-2 LSE).
+one merge of the N partials, on one stream with the inputs already resident
+in HBM.  By default the N stripe attentions run as one dcp_stripe_attn_multi
+launch -- on one GPU the ranks' attentions are independent work -- each rank
+writing o_r in bf16 (rounded once from the float32 result) and lse_r in
+float32, the partial payload the pages size at (512 + 4) x 2 bytes per (row,
+head); dcp_lse_merge_bf16 merges them into float32 (o, lse).  The per-rank
+form (N dcp_stripe_attn calls, the launch one rank runs on its own GPU, then
+the same merge) is timed beside it.  Default workload: the Kimi-K3-shaped
+decode batch (B=64 requests x 131072 tokens, H=96, N=8 stripes, page 64,
+base-2 LSE).
 
 Prints one JSON line: KV GB/s as `value`, microseconds per step, the roofline
-of the dominant kernel (the stripe attention, timed per launch with HIP events
-on its stream) and the float64 CPU oracle timed on a bounded sample of the
-same workload on this host's cores.
+of the dominant launch (timed with HIP events on its stream) and the float64
+CPU oracle timed on a bounded sample of the same workload on this host's
+cores, with the parity of the step's outputs against it.
 
-Secondary measurements (not the headline): --softcap / --window / --sinks time
-the same step with a mergeable variant switched on; --op relayout times the
-prefill-to-decode token relayout of the whole batch into the N ranks' pools.
+Other modes (not the headline): --per-rank times the per-rank form as the
+step; --o-fp32 keeps o_r in float32; --softcap / --window / --sinks time the
+step with a mergeable variant switched on; --op relayout / head-return /
+stream / mfma time the relayout, the head-return exchange and the two probes
+behind the measured peaks.
 """
 
 from __future__ import annotations
@@ -63,8 +72,12 @@ def parse():
                     help="MiB of scratch written between timed steps so the KV is not served from the memory-side "
                          "cache (-1: 1024 when the workload's KV is under 1 GiB, else 0); with a flush the step time "
                          "is the mean of the HIP-event step times")
+    ap.add_argument("--per-rank", action="store_true",
+                    help="time the per-rank form as the step: N dcp_stripe_attn calls (the launch one rank runs on "
+                         "its own GPU) then the merge; the default step runs the same N stripe attentions as one "
+                         "dcp_stripe_attn_multi launch (then the merge)")
     ap.add_argument("--multi", action="store_true",
-                    help="all N stripes in one dcp_stripe_attn_multi launch (then the merge)")
+                    help="the one-launch form (the default; kept for older command lines)")
     ap.add_argument("--topk", type=int, default=0,
                     help="k > 0: sparse attention over a global top-k selection per query token (plan + attention "
                          "on every rank)")
@@ -74,6 +87,10 @@ def parse():
                     help="every rank writes its (o_r, lse_r) as bf16 records (+ fp32 lse) in head-owner order -- "
                          "the head-return all-to-all send buffer -- and one dcp_merge_heads over all owners' rows "
                          "folds the N ranks' records")
+    ap.add_argument("--o-fp32", action="store_true",
+                    help="every rank writes o_r in float32 and dcp_lse_merge merges them; by default o_r is bf16 "
+                         "(the float32 result rounded once, lse_r float32: the partial payload of page 'MLA 的 DCP' "
+                         "section 5) and dcp_lse_merge_bf16 merges them")
     ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
                     help="2: the per-rank calls alternate between two streams, each with its own workspace, so "
                          "one rank's launch starts on the compute units the previous one leaves idle at its end "
@@ -95,6 +112,15 @@ def parse():
     args = ap.parse_args()
     # timing protocol: 20 timed steps for the long-running shapes, 100 for the
     # short ones (whose step is a few hundred microseconds)
+    if args.streams > 1 and args.multi:
+        print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
+        sys.exit(2)
+    # per-rank calls on two streams and per-rank selection plans only exist in the per-rank form
+    if args.streams > 1 or args.topk > 0:
+        args.per_rank = True
+    args.multi = not args.per_rank
+    # o_r in bf16 unless asked for float32 (records carry their own bf16 form)
+    args.o_bf16 = not (args.o_fp32 or args.records)
     short = args.op == "step" and args.workload not in ("k3", "long")
     if args.steps is None:
         args.steps = 100 if short else 20
@@ -103,7 +129,9 @@ def parse():
     return args
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md")
+# counter records of HBM traffic: one per step form (the per-rank call, the one launch of all stripes)
+TRAFFIC_RECORDS = [os.path.join(ROOT, "profiles", "stripe_attn_k3_hbm_bytes.md"),
+                   os.path.join(ROOT, "profiles", "stripe_attn_k3_one_launch_hbm_bytes.md")]
 
 
 def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1, out_row_bytes: int = (512 + 1) * 4):
@@ -118,24 +146,30 @@ def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1, out_row_bytes:
     return local_rows.sum(axis=0) * ROW_BYTES + q_bytes + out_bytes
 
 
-def measured_traffic(workload: str):
-    """HBM bytes of one dcp_stripe_attn call from the committed counter record,
-    or None when there is none for this workload or the kernel sources changed
-    since the counters were taken."""
+def measured_traffic(workload: str, form: str = "per-rank", outputs: str = "o_r bf16, lse_r fp32"):
+    """HBM bytes of the dominant launch from a committed counter record: one
+    dcp_stripe_attn call (form "per-rank": the attention kernel and its chunk
+    combine) or one dcp_stripe_attn_multi launch of all stripes (form
+    "one-launch"), with the given output type.  None when no record covers
+    this workload, form and output type or the kernel sources changed since the
+    counters were taken."""
     import hashlib
-    try:
-        with open(TRAFFIC_RECORD) as f:
-            line = next(l for l in f if l.strip().startswith("traffic-record "))
-    except (OSError, StopIteration):
-        return None
-    rec = json.loads(line.strip()[len("traffic-record "):])
-    if rec.get("workload") != workload:
-        return None
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    return int(rec["bytes_per_call"]) if h.hexdigest() == rec["sha256"] else None
+    for path in TRAFFIC_RECORDS:
+        try:
+            with open(path) as f:
+                lines = [l.strip() for l in f if l.strip().startswith("traffic-record ")]
+        except OSError:
+            continue
+        for line in lines:
+            rec = json.loads(line[len("traffic-record "):])
+            if rec.get("workload") != workload or rec.get("form") != form or rec.get("outputs") != outputs:
+                continue
+            h = hashlib.sha256()
+            for src in rec["sources"]:
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    h.update(f.read())
+            return int(rec["bytes_per_call"]) if h.hexdigest() == rec["sha256"] else None
+    return None
 
 
 def main():
@@ -144,9 +178,6 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the per-rank stripe kernels of all N stripes and the merge run on a "
               f"single MI355X; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
-        sys.exit(2)
-    if args.streams > 1 and args.multi:
-        print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
         sys.exit(2)
     if args.records and args.parts:
         print("--records writes each rank's merged o_r as records; it does not take --parts", file=sys.stderr)
@@ -214,7 +245,8 @@ def main():
         recs = torch.empty((N, N, w.B * w.q_len, w.H // N, 516), dtype=torch.int16, device=dev)
         o_parts = lse_parts = None
     else:
-        o_parts = torch.empty((N * K, w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
+        o_parts = torch.empty((N * K, w.B, w.q_len, w.H, 512), dtype=torch.bfloat16 if args.o_bf16 else torch.float32,
+                              device=dev)
         lse_parts = torch.empty((N * K, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
@@ -229,6 +261,7 @@ def main():
                            args.parts if args.parts > 0 else args.splits, None, None, None, None,
                            partials=1 if args.parts > 0 else 0)
         a.out_records = 1 if args.records else 0
+        a.o_bf16 = 1 if args.o_bf16 else 0
         need = ctypes.c_size_t(0)
         assert L.dcp_stripe_attn_workspace(ctypes.byref(a), ctypes.byref(need)) == 0
         ws_bytes = max(ws_bytes, need.value)
@@ -286,25 +319,34 @@ def main():
         if args.records:
             rc = L.dcp_merge_heads(N, rows, 512, recs.data_ptr(), base, o.data_ptr(), lse.data_ptr(), sh_m)
         else:
-            rc = L.dcp_lse_merge(N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(),
+            fn = L.dcp_lse_merge_bf16 if args.o_bf16 else L.dcp_lse_merge
+            rc = fn(N * K, rows, 512, o_parts.data_ptr(), lse_parts.data_ptr(), base, o.data_ptr(),
                                  lse.data_ptr(), sh_m)
         if rc != 0:
             raise RuntimeError(f"merge: {dcp.strerror(rc)}")
 
+    def one_launch_step(events=None, sh=sh):
+        # events (3): before the launch, after it, after the merge -- nothing
+        # else is recorded inside the step (each event costs GPU time)
+        if events is not None:
+            events[0].record(stream)
+        rc = L.dcp_stripe_attn_multi(multi_arr, N, sh)
+        if rc != 0:
+            raise RuntimeError(f"dcp_stripe_attn_multi: {dcp.strerror(rc)}")
+        if events is not None:
+            events[1].record(stream)
+        merge(sh)
+        if events is not None:
+            events[2].record(stream)
+
     def step(events=None, sh=sh):
         if multi_arr is not None:
-            if events is not None:
-                events[0].record(stream)
-            rc = L.dcp_stripe_attn_multi(multi_arr, N, sh)
-            if rc != 0:
-                raise RuntimeError(f"dcp_stripe_attn_multi: {dcp.strerror(rc)}")
-            if events is not None:
-                for r in range(1, N + 1):
-                    events[r].record(stream)
-            merge(sh)
-            if events is not None:
-                events[N + 1].record(stream)
+            one_launch_step(events, sh)
             return
+        per_rank_step(events, sh)
+
+    def per_rank_step(events=None, sh=sh):
+        # events (N + 2): before each rank's call, after the last call, after the merge
         two = len(streams) > 1
         if two:
             if events is not None:
@@ -359,7 +401,10 @@ def main():
     if flush_mib < 0:
         flush_mib = 1024 if float(lens.sum()) * ROW_BYTES < (1 << 30) else 0
     scratch = torch.empty((flush_mib << 20) // 4, dtype=torch.float32, device=dev) if flush_mib > 0 else None
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 2)] for _ in range(args.steps)]
+    # event slots: the step's start, the end of its attention launches, the end of the merge
+    e_att = 1 if args.multi else N
+    e_end = e_att + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(e_end + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -368,8 +413,8 @@ def main():
         if graph is not None:
             evs[k][0].record(stream)
             graph.replay()
-            evs[k][N].record(stream)
-            evs[k][N + 1].record(stream)
+            evs[k][e_att].record(stream)
+            evs[k][e_end].record(stream)
         else:
             step(evs[k])
     torch.cuda.synchronize()
@@ -416,6 +461,34 @@ def main():
                       "launch_us": round(float(la2.mean()) * 1e3, 1), "ms": float(st2.mean())}
         del ws2
 
+    # ---- secondary form of a one-launch step: the per-rank form, N
+    # dcp_stripe_attn calls (the launch each rank runs on its own GPU, with
+    # its chunk combine) then the same merge, timed with an event per call
+    per_rank = None
+    if args.multi and not (args.no_secondary or args.graph):
+        for _ in range(max(2, args.warmup // 2)):
+            per_rank_step()
+        ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            if scratch is not None:
+                scratch.fill_(float(k))
+            per_rank_step(ev3[k])
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError(f"device status {int(status.item())} after the per-rank step")
+        st3 = np.array([ev3[k][0].elapsed_time(ev3[k][N + 1]) for k in range(args.steps)])
+        calls3 = np.array([[ev3[k][r].elapsed_time(ev3[k][r + 1]) for r in range(N)] for k in range(args.steps)])
+        mg3 = np.array([ev3[k][N].elapsed_time(ev3[k][N + 1]) for k in range(args.steps)])
+        per_rank = {"what": "the same step as N per-rank dcp_stripe_attn calls (each rank's launch and its chunk "
+                            "combine, the shape one rank runs on its own GPU) on one stream, then the same merge "
+                            "(HIP-event step times, one event per call)",
+                    "us_per_step": round(float(st3.mean()) * 1e3, 1),
+                    "us_per_step_median": round(float(np.median(st3)) * 1e3, 1),
+                    "per_call_us": [round(float(x) * 1e3, 1) for x in calls3.mean(axis=0)],
+                    "merge_us": round(float(mg3.mean()) * 1e3, 1),
+                    "ms": float(st3.mean()), "call_ms": calls3.mean(axis=0)}
+
     power = None
     if args.power_seconds > 0:
         def loop_step():
@@ -438,15 +511,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.streams > 1 or args.graph:
+    if args.multi:
+        # one launch of all stripes (with --graph: the whole graph's span, merge included)
+        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][1])] for k in range(args.steps)])
+    elif args.streams > 1 or args.graph:
         # overlapping calls, or one graph, have no per-launch span: the stripe part of the step over N
-        # (one launch of all stripes: the whole span is that launch's)
-        div = 1 if args.multi else N
-        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / div] * N for k in range(args.steps)])
+        per_stripe_ms = np.array([[evs[k][0].elapsed_time(evs[k][N]) / N] * N for k in range(args.steps)])
     else:
         per_stripe_ms = np.array([[evs[k][r].elapsed_time(evs[k][r + 1]) for r in range(N)] for k in range(args.steps)])
-    merge_ms = np.array([evs[k][N].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
-    step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][N + 1]) for k in range(args.steps)])
+    merge_ms = np.array([evs[k][e_att].elapsed_time(evs[k][e_end]) for k in range(args.steps)])
+    step_ev_ms = np.array([evs[k][0].elapsed_time(evs[k][e_end]) for k in range(args.steps)])
     ms_per_step = wall_s * 1e3 / args.steps
     if scratch is not None:
         ms_per_step = float(step_ev_ms.mean())        # the flushes between steps are not step time
@@ -461,13 +535,15 @@ def main():
         first = np.clip(lens - w.q_len + 1 - args.window, 0, None)
         local = local - dcp.dcp_local_count(lay, torch.from_numpy(first.astype(np.int64)).to(dev)).cpu().numpy()
     kv_bytes = float(local.sum()) * ROW_BYTES
-    if one_launch is not None:
-        ms2 = one_launch.pop("ms")
-        one_launch["value"] = round(kv_bytes / (ms2 * 1e-3) / 1e9, 2)
-        one_launch["unit"] = "GB/s"
-        one_launch["hbm_frac"] = round(kv_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    for sec in (one_launch, per_rank):
+        if sec is not None:
+            ms2 = sec.pop("ms")
+            sec["value"] = round(kv_bytes / (ms2 * 1e-3) / 1e9, 2)
+            sec["unit"] = "GB/s"
+            sec["hbm_frac"] = round(kv_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     q_bytes = w.B * M * ROW_BYTES
-    out_row_bytes = 1032 if args.records else (512 + 1) * 4            # per (row, head): bf16 record or fp32
+    # per (row, head): a bf16 record, bf16 o + fp32 lse, or fp32 o + fp32 lse
+    out_row_bytes = 1032 if args.records else (512 * 2 + 4 if args.o_bf16 else (512 + 1) * 4)
     part_bytes = K * w.B * M * out_row_bytes                           # one stripe's (o_r, lse_r), or its K parts
     vis = np.zeros(w.B)
     for t in range(w.q_len):
@@ -489,6 +565,19 @@ def main():
         achieved = float(stripe_bytes.sum() / (launch_ms[0] * 1e-3)) / 1e9
     else:
         achieved = float(np.mean(stripe_bytes / (launch_ms * 1e-3))) / 1e9
+    # a variant: no committed counter record applies (records are kept per
+    # step form and output type)
+    outputs = "bf16 records" if args.records else ("o_r bf16, lse_r fp32" if args.o_bf16 else "fp32")
+    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
+                     or args.streams > 1 or args.graph or args.records)
+    if per_rank is not None:
+        call_ms = per_rank.pop("call_ms")
+        call_gbs = float(np.mean(stripe_bytes / (call_ms * 1e-3))) / 1e9
+        per_rank["call"] = {"what": "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine",
+                            "achieved": round(call_gbs, 1), "unit": "GB/s",
+                            "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+                            "bytes_per_call": int(stripe_bytes.mean()),
+                            "traffic": measured_traffic(w.name, "per-rank", outputs) if not secondary else None}
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     # the same launch's matrix rate: each rank's share of the step's FLOPs
     # (in proportion to its latent rows) over its duration
@@ -500,8 +589,6 @@ def main():
         achieved_tf = float(np.mean(stripe_flops / (launch_ms * 1e-3))) / 1e12
     mfma_bound = flops / max(kv_bytes, 1.0) > MFMA_BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3)
 
-    secondary = bool(args.window or args.softcap or args.sinks or args.parts or args.splits or I != 1 or args.topk
-                     or args.multi or args.streams > 1 or args.graph or args.records)
     # ---- measured HBM read peak: the streaming-read probe over the same pools,
     # one launch per stripe's pool, in the step's back-to-back pattern
     probe = None
@@ -520,7 +607,7 @@ def main():
         if args.records:
             host_out = records_to_host(recs, o, lse, w)
         else:
-            host_out = (o.cpu().numpy(), lse.cpu().numpy(), o_parts.cpu().numpy(), lse_parts.cpu().numpy())
+            host_out = (o.cpu().numpy(), lse.cpu().numpy(), o_parts.cpu().float().numpy(), lse_parts.cpu().numpy())
         slot_bad = slot_map_mismatches(lay, lens[:len(sample)], sp.tables, N, I, P, dev)
         cpu, parity = cpu_oracle_leg(args, w, sample, N, I, host_out)
         parity["slot_map_mismatches"] = slot_bad
@@ -554,7 +641,8 @@ def main():
                    **({"outputs": "bf16 records + fp32 lse in head-owner order, merged by dcp_merge_heads"}
                       if args.records else {}),
                    **({"topk": args.topk, "plan_in_step": True} if args.topk > 0 else {}),
-                   **({"one_launch_for_all_stripes": True} if args.multi else {}),
+                   "form": ("one launch of all N stripes (dcp_stripe_attn_multi), then the merge" if args.multi
+                            else "N per-rank dcp_stripe_attn calls, then the merge"),
                    **({"streams": args.streams} if args.streams > 1 else {}),
                    **({"hip_graph": True} if args.graph else {})},
         "per_stripe_us": [round(float(x) * 1e3, 1) for x in launch_ms],
@@ -565,13 +653,15 @@ def main():
         "flush_mib_between_steps": flush_mib,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if secondary else measured_traffic(w.name),
+                     "traffic": None if secondary else measured_traffic(w.name, "one-launch" if args.multi
+                                                                       else "per-rank", outputs),
                      "kernel": ("one dcp_stripe_attn_multi launch: all stripes"
                                 + (" (in one HIP graph with the merge: the step's time)" if args.graph else "")
                                 if args.multi else
                                 (f"one dcp_stripe_attn call: stripe_attn_kernel writing {K} unmerged parts"
                                  if args.parts > 0 else "one dcp_stripe_attn call: stripe_attn_kernel + its chunk combine")
                                 + (" (bf16 record outputs)" if args.records else "")
+                                + (" (o_r in bf16)" if args.o_bf16 else "")
                                 + (" (two streams: the step's stripe time over N, calls overlapping)"
                                    if args.streams > 1 else "")
                                 + (" (one HIP graph per step: the step's time, merge included, over N)"
@@ -580,10 +670,11 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "step_algorithmic_bytes": int(kv_bytes + N * q_bytes + 2 * N * part_bytes + w.B * M * (512 + 1) * 4),
-        "outputs": "bf16 records" if args.records else "fp32",
+        "outputs": outputs,
         "device": device_ids(dev),
         "power": power,
         "one_launch_for_all_stripes": one_launch,
+        "per_rank_form": per_rank,
         "setup_s": round(setup_s, 1),
     }
     if probe is not None:
@@ -691,8 +782,10 @@ def sample_power(loop_step, seconds: float, sync=None):
         return {"skipped": "no amd-smi sample inside the loop"}
     pw = np.array([x[1] for x in use])
     clk = np.array([np.mean(x[2]) for x in use])
+    per_xcd = np.array([x[2] for x in use if len(x[2]) == len(use[0][2])])
     return {"tool": "amd-smi metric --power --clock", "loop_seconds": round(t_end - t0, 2), "steps": k,
             "samples": len(use), "socket_w_mean": round(float(pw.mean()), 1), "socket_w_max": round(float(pw.max()), 1),
+            "gfx_mhz_per_xcd": [round(float(v), 1) for v in per_xcd.mean(axis=0)],
             "gfx_mhz_mean": round(float(clk.mean()), 1), "gfx_mhz_min": round(float(clk.min()), 1),
             "xcds": len(use[-1][2])}
 

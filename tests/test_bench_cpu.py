@@ -43,10 +43,16 @@ def test_hbm_traffic_record_matches_the_kernel_sources():
     # a fresh pair of FETCH_SIZE / WRITE_SIZE passes and a new record
     sys.path.insert(0, ROOT)
     import bench
-    got = bench.measured_traffic("k3")
+    bf16 = "o_r bf16, lse_r fp32"
+    got = bench.measured_traffic("k3", "per-rank", bf16)
     assert got is not None, "profiles/stripe_attn_k3_hbm_bytes.md does not match the current kernel sources"
     assert 1.0e9 < got < 1.5e9                     # one K3 stripe call: 1.21 GB of KV plus partials
-    assert bench.measured_traffic("dsv3") is None  # the record covers the workload it was taken on only
+    one = bench.measured_traffic("k3", "one-launch", bf16)
+    assert one is not None, "profiles/stripe_attn_k3_one_launch_hbm_bytes.md does not match the kernel sources"
+    assert 9.6e9 < one < 9.9e9                     # all 8 stripes: 9.66 GB of KV, queries and bf16 outputs
+    # a record covers the workload, step form and output type it was taken on only
+    assert bench.measured_traffic("dsv3", "one-launch", bf16) is None
+    assert bench.measured_traffic("k3", "one-launch", "fp32") is None
 
 
 def test_k3_call_bytes_from_the_oracle_counts():
