@@ -1,28 +1,26 @@
 """Decode-step benchmark of DCP stripe attention + LSE merge on one MI355X.
 
-One step = the stripe attention of all N ranks, each at its real per-rank
-shape (all H query heads against that rank's stripe of every request), plus
-one merge of the N partials, on one stream with the inputs already resident
-in HBM.  By default the N stripe attentions run as one dcp_stripe_attn_multi
-launch -- on one GPU the ranks' attentions are independent work -- each rank
-writing o_r in bf16 (rounded once from the float32 result) and lse_r in
-float32, the partial payload the pages size at (512 + 4) x 2 bytes per (row,
-head); dcp_lse_merge_bf16 merges them into float32 (o, lse).  The per-rank
-form (N dcp_stripe_attn calls, the launch one rank runs on its own GPU, then
-the same merge) is timed beside it.  Default workload: the Kimi-K3-shaped
-decode batch (B=64 requests x 131072 tokens, H=96, N=8 stripes, page 64,
-base-2 LSE).
+One step = the N per-rank dcp_stripe_attn calls, each at its real per-rank
+shape (all H query heads against that rank's stripe of every request) with
+its chunk combine, plus one dcp_lse_merge of the N partials, all on one
+stream with the inputs already resident in HBM.  Default workload: the
+Kimi-K3-shaped decode batch (B=64 requests x 131072 tokens, H=96, N=8
+stripes, page 64, base-2 LSE).
 
 Prints one JSON line: KV GB/s as `value`, microseconds per step, the roofline
-of the dominant launch (timed with HIP events on its stream) and the float64
-CPU oracle timed on a bounded sample of the same workload on this host's
-cores, with the parity of the step's outputs against it.
+of the dominant launch (timed with HIP events on its stream), the float64 CPU
+oracle timed on a bounded sample of the same workload on this host's cores
+with the parity of the step's outputs against it, and the same step with the
+N stripe attentions in one dcp_stripe_attn_multi launch (on one GPU the
+ranks' attentions are independent work), timed beside it.
 
-Other modes (not the headline): --per-rank times the per-rank form as the
-step; --o-fp32 keeps o_r in float32; --softcap / --window / --sinks time the
-step with a mergeable variant switched on; --op relayout / head-return /
-stream / mfma time the relayout, the head-return exchange and the two probes
-behind the measured peaks.
+Other modes (not the headline): --one-launch times that form as the step
+(the per-rank form beside it); --o-bf16 writes o_r in bf16 (the float32
+result rounded once, lse_r float32: the partial payload the pages size at
+(512 + 4) x 2 bytes per (row, head)) and merges with dcp_lse_merge_bf16;
+--softcap / --window / --sinks time the step with a mergeable variant
+switched on; --op relayout / head-return / stream / mfma time the relayout,
+the head-return exchange and the two probes behind the measured peaks.
 """
 
 from __future__ import annotations
@@ -44,6 +42,63 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROW_BYTES = 576 * 2             # one latent row (key = whole row, value = first 512 dims)
 FLOP_PER_ROW_QUERY = 2 * 576 + 2 * 512   # QK^T + PV per (query row, visible token)
+
+
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: its record
+    writes the timestamp without the system-scope release (L2 write-back and
+    invalidation) a default event performs, which the HIP documentation names
+    for events used only to measure time.  Between two kernels of one stream a
+    default event's fence costs GPU time of its own (several microseconds);
+    the steps here are read only after a device-wide synchronize, which orders
+    everything.  Same record / elapsed_time interface as torch.cuda.Event."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        self.ev = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self.hip().hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, other) -> float:
+        ms = ctypes.c_float(0.0)
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, other.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.ev and FenceFreeEvent._hip is not None:
+            FenceFreeEvent._hip.hipEventDestroy(self.ev)
+            self.ev = ctypes.c_void_p()
+
+
+EVENT_KIND = "nofence"
+
+
+def timing_event():
+    """An event for the timed steps: fence-free (default) or torch's default one."""
+    if EVENT_KIND == "torch":
+        import torch
+        return torch.cuda.Event(enable_timing=True)
+    return FenceFreeEvent()
 
 
 def parse():
@@ -72,12 +127,11 @@ def parse():
                     help="MiB of scratch written between timed steps so the KV is not served from the memory-side "
                          "cache (-1: 1024 when the workload's KV is under 1 GiB, else 0); with a flush the step time "
                          "is the mean of the HIP-event step times")
-    ap.add_argument("--per-rank", action="store_true",
-                    help="time the per-rank form as the step: N dcp_stripe_attn calls (the launch one rank runs on "
-                         "its own GPU) then the merge; the default step runs the same N stripe attentions as one "
-                         "dcp_stripe_attn_multi launch (then the merge)")
-    ap.add_argument("--multi", action="store_true",
-                    help="the one-launch form (the default; kept for older command lines)")
+    ap.add_argument("--one-launch", "--multi", dest="multi", action="store_true",
+                    help="time the one-launch form as the step: the N stripe attentions as one "
+                         "dcp_stripe_attn_multi launch (then the merge); the default step is the per-rank form, N "
+                         "dcp_stripe_attn calls (the launch one rank runs on its own GPU) then the merge, and the "
+                         "one-launch form is timed beside it")
     ap.add_argument("--topk", type=int, default=0,
                     help="k > 0: sparse attention over a global top-k selection per query token (plan + attention "
                          "on every rank)")
@@ -87,10 +141,10 @@ def parse():
                     help="every rank writes its (o_r, lse_r) as bf16 records (+ fp32 lse) in head-owner order -- "
                          "the head-return all-to-all send buffer -- and one dcp_merge_heads over all owners' rows "
                          "folds the N ranks' records")
-    ap.add_argument("--o-fp32", action="store_true",
-                    help="every rank writes o_r in float32 and dcp_lse_merge merges them; by default o_r is bf16 "
-                         "(the float32 result rounded once, lse_r float32: the partial payload of page 'MLA 的 DCP' "
-                         "section 5) and dcp_lse_merge_bf16 merges them")
+    ap.add_argument("--o-bf16", action="store_true",
+                    help="every rank writes o_r in bf16 (the float32 result rounded once; lse_r stays float32), the "
+                         "partial payload of page 'MLA 的 DCP' section 5, and dcp_lse_merge_bf16 merges them; by "
+                         "default o_r is float32 and dcp_lse_merge merges them")
     ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
                     help="2: the per-rank calls alternate between two streams, each with its own workspace, so "
                          "one rank's launch starts on the compute units the previous one leaves idle at its end "
@@ -100,6 +154,9 @@ def parse():
                          "then has no per-launch split)")
     ap.add_argument("--cpu-sample-requests", type=int, default=64,
                     help="requests of the workload the CPU oracle is timed on (bounded sample)")
+    ap.add_argument("--events", default="nofence", choices=["nofence", "torch"],
+                    help="timing events inside the timed steps: nofence (hipEventDisableSystemFence, the default) or "
+                         "torch's default events, whose record also writes back and invalidates the caches")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary measurement: the same step with all N stripes in one "
                          "dcp_stripe_attn_multi launch")
@@ -115,12 +172,12 @@ def parse():
     if args.streams > 1 and args.multi:
         print("--streams 2 splits the per-rank calls over two streams; --multi makes one launch", file=sys.stderr)
         sys.exit(2)
-    # per-rank calls on two streams and per-rank selection plans only exist in the per-rank form
-    if args.streams > 1 or args.topk > 0:
-        args.per_rank = True
-    args.multi = not args.per_rank
-    # o_r in bf16 unless asked for float32 (records carry their own bf16 form)
-    args.o_bf16 = not (args.o_fp32 or args.records)
+    if args.topk > 0 and args.multi:
+        print("--topk plans and times each rank's selection with its call: per-rank form only", file=sys.stderr)
+        sys.exit(2)
+    if args.records and args.o_bf16:
+        print("--records already writes bf16 outputs; --o-bf16 is the plain-layout form", file=sys.stderr)
+        sys.exit(2)
     short = args.op == "step" and args.workload not in ("k3", "long")
     if args.steps is None:
         args.steps = 100 if short else 20
@@ -146,7 +203,7 @@ def stripe_call_bytes(local_rows, B: int, M: int, parts: int = 1, out_row_bytes:
     return local_rows.sum(axis=0) * ROW_BYTES + q_bytes + out_bytes
 
 
-def measured_traffic(workload: str, form: str = "per-rank", outputs: str = "o_r bf16, lse_r fp32"):
+def measured_traffic(workload: str, form: str = "per-rank", outputs: str = "fp32"):
     """HBM bytes of the dominant launch from a committed counter record: one
     dcp_stripe_attn call (form "per-rank": the attention kernel and its chunk
     combine) or one dcp_stripe_attn_multi launch of all stripes (form
@@ -173,7 +230,9 @@ def measured_traffic(workload: str, form: str = "per-rank", outputs: str = "o_r 
 
 
 def main():
+    global EVENT_KIND
     args = parse()
+    EVENT_KIND = args.events
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the per-rank stripe kernels of all N stripes and the merge run on a "
@@ -404,7 +463,7 @@ def main():
     # event slots: the step's start, the end of its attention launches, the end of the merge
     e_att = 1 if args.multi else N
     e_end = e_att + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(e_end + 1)] for _ in range(args.steps)]
+    evs = [[timing_event() for _ in range(e_end + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -443,7 +502,7 @@ def main():
                 ev[2].record(stream)
         for _ in range(max(2, args.warmup // 2)):
             step2()
-        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        ev2 = [[timing_event() for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for k in range(args.steps):
             if scratch is not None:
@@ -468,7 +527,7 @@ def main():
     if args.multi and not (args.no_secondary or args.graph):
         for _ in range(max(2, args.warmup // 2)):
             per_rank_step()
-        ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 2)] for _ in range(args.steps)]
+        ev3 = [[timing_event() for _ in range(N + 2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for k in range(args.steps):
             if scratch is not None:
@@ -820,7 +879,7 @@ def probe_pools(args, pools, N, stream, dev):
     for _ in range(args.warmup):
         for r in range(N):
             PR.stream(pools[r], per, mode, grid, sink, sh)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+    evs = [[timing_event() for _ in range(N + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     got = 0
     for k in range(args.steps):
@@ -946,7 +1005,7 @@ def run_stream(args):
         for _ in range(args.warmup):
             for r in range(N):
                 PR.stream(buf[r], per, mode, grid, sink, sh)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+        evs = [[timing_event() for _ in range(N + 1)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         got = 0
         for k in range(args.steps):
@@ -997,7 +1056,7 @@ def mfma_probe_steps(N, steps, warmup, stream, dev):
     for _ in range(warmup):
         for _ in range(N):
             PR.mfma(cus, MFMA_PROBE_ITERS, sink, sh)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(steps)]
+    evs = [[timing_event() for _ in range(N + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     flops = 0
     for k in range(steps):
@@ -1083,7 +1142,7 @@ def run_head_return(args):
 
     for _ in range(args.warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[timing_event() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         evs[k][0].record(stream)
@@ -1181,7 +1240,7 @@ def run_relayout(args):
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N + 1)] for _ in range(args.steps)]
+    evs = [[timing_event() for _ in range(N + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for k in range(args.steps):

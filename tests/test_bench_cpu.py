@@ -44,9 +44,11 @@ def test_hbm_traffic_record_matches_the_kernel_sources():
     sys.path.insert(0, ROOT)
     import bench
     bf16 = "o_r bf16, lse_r fp32"
-    got = bench.measured_traffic("k3", "per-rank", bf16)
+    got = bench.measured_traffic("k3")             # the headline: a per-rank call with fp32 o_r
     assert got is not None, "profiles/stripe_attn_k3_hbm_bytes.md does not match the current kernel sources"
     assert 1.0e9 < got < 1.5e9                     # one K3 stripe call: 1.21 GB of KV plus partials
+    got16 = bench.measured_traffic("k3", "per-rank", bf16)
+    assert got16 is not None and got16 < got       # bf16 o_r writes half the output bytes
     one = bench.measured_traffic("k3", "one-launch", bf16)
     assert one is not None, "profiles/stripe_attn_k3_one_launch_hbm_bytes.md does not match the kernel sources"
     assert 9.6e9 < one < 9.9e9                     # all 8 stripes: 9.66 GB of KV, queries and bf16 outputs

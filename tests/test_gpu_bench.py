@@ -19,8 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_long_verify_roofline_is_mfma_bound(form):
     cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", "long", "--steps", "1",
            "--warmup", "1", "--no-cpu-baseline", "--no-probe", "--no-secondary", "--power-seconds", "0"]
-    if form == "per-rank":
-        cmd.append("--per-rank")
+    if form == "one-launch":
+        cmd.append("--one-launch")
     print("bench:", " ".join(cmd[2:]), flush=True)
     r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=110)
     assert r.returncode == 0, r.stderr[-2000:]
