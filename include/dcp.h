@@ -343,7 +343,7 @@ int dcp_merge_heads(int32_t n_stripes, int64_t rows, int32_t v_dim, const void* 
  * dcp_stripe_attn argument block for its rank (own pool, block_table, o, lse,
  * sinks, sparse selection); everything else -- layout, shapes, q, seq_len,
  * scale, base, num_splits, window, softcap, bias_slopes, partials,
- * out_records and whether a selection is given -- must be the same in all n
+ * out_records, o_bf16 and whether a selection is given -- must be the same in all n
  * (else DCP_EINVAL).  The
  * workspace of args[0] serves the launch; size it with
  * dcp_stripe_attn_multi_workspace.  Results equal n dcp_stripe_attn calls.

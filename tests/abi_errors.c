@@ -210,6 +210,11 @@ static void stripe_attn_arguments(void) {
   CHECK(dcp_stripe_attn_multi(NULL, 2, NULL), DCP_EINVAL);
   arr[1].batch = 3;
   CHECK(dcp_stripe_attn_multi(arr, 2, NULL), DCP_EINVAL);
+  /* every rank of one launch writes the same output form */
+  arr[1] = base_args();
+  arr[1].rank = 1;
+  arr[1].o_bf16 = 1;
+  CHECK(dcp_stripe_attn_multi(arr, 2, NULL), DCP_EINVAL);
 }
 
 /* Workspace queries over a grid of shapes, extreme values included: the plan's
