@@ -651,7 +651,8 @@ def main():
     # ---- measured HBM read peak: the streaming-read probe over the same pools,
     # one launch per stripe's pool, in the step's back-to-back pattern
     probe = None
-    if not args.no_probe:
+    # pools of a few MB (Tiny) stream in a launch's latency: no peak to measure there
+    if not args.no_probe and kv_bytes >= (64 << 20):
         probe = probe_pools(args, sp.pools, N, stream, dev)
     mfma_peak = None
     if not args.no_probe and mfma_bound:
