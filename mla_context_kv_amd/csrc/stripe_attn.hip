@@ -390,6 +390,80 @@ __device__ __forceinline__ WorkItem find_work(const Params& p, int32_t c, bool w
   return w;
 }
 
+// The one-round plan of a launch with fewer requests than its round of
+// workgroups and at most 256 of them (one rank's call on a decode batch of up
+// to 256 requests), from registers: each lane holds the shapes of requests
+// lane, lane + 64, ..., read from the request table once, and every step of
+// the search (the total, the chunk counts of each candidate length, the scan,
+// the request of chunk c and its shape) runs on them -- the same chunk length
+// and numbering as find_work, with no further LDS round trips.
+constexpr int kSmallPerLane = 4;
+__device__ __forceinline__ WorkItem find_work_small(const Params& p, int32_t c, bool write_table, const int4* tab) {
+  const int lane = threadIdx.x & 63;
+  const int32_t Bv = p.nr * p.B;
+  int4 e[kSmallPerLane];
+  int32_t tsum = 0;
+#pragma unroll
+  for (int k = 0; k < kSmallPerLane; ++k) {
+    const int32_t v = 64 * k + lane;
+    e[k] = v < Bv ? tab[v] : make_int4(0, 0, 0, 0);
+    tsum += e[k].x;
+  }
+  const int32_t total = wave_sum_i(tsum);
+  const int32_t target = p.target_chunks;
+  auto chunks_for = [&](int32_t len) -> int32_t {
+    int32_t nc = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallPerLane; ++k)
+      nc += 64 * k + lane < Bv ? max(cdiv(e[k].x, len), 1) : 0;
+    return wave_sum_i(nc);
+  };
+  // the shortest chunk length whose chunks fit the round (find_work's rule)
+  int32_t C = max(cdiv(total, target), 1);
+  if (chunks_for(C) > target) {
+    int32_t hi = max(cdiv(total, target - Bv), 1);
+    ++C;
+    while (C < hi) {
+      const int32_t mid = C + (hi - C) / 2;
+      if (chunks_for(mid) <= target) hi = mid;
+      else C = mid + 1;
+    }
+  }
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, false};
+  int32_t carry = 0;
+#pragma unroll
+  for (int k = 0; k < kSmallPerLane; ++k) {
+    if (64 * k >= Bv) break;
+    const int32_t v = 64 * k + lane;
+    const int32_t t = e[k].x;
+    const int32_t nb = v < Bv ? max(cdiv(t, C), 1) : 0;
+    const int32_t incl = carry + wave_scan_i(nb), excl = incl - nb;
+    if (write_table && v < Bv) {
+      // entries cut to the workspace's slots, as in find_work
+      const int32_t fit = incl <= p.slots ? nb : max(p.slots - excl, 0);
+      if (fit != nb) flag_range(p.status);
+      p.table[v] = fit;
+      p.table[Bv + v] = excl;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(v < Bv && excl <= c && c < incl);
+    if (hit != 0 && !w.live) {
+      const int l = __builtin_ctzll(hit);
+      w.live = true;
+      w.b = 64 * k + l;
+      w.k = c - __builtin_amdgcn_readlane(excl, l);
+      w.n = __builtin_amdgcn_readlane(nb, l);
+      w.rows = __builtin_amdgcn_readlane(e[k].y, l);
+      w.ft = __builtin_amdgcn_readlane(e[k].z, l);
+      w.S = __builtin_amdgcn_readlane(e[k].w, l);
+      const int32_t tl = __builtin_amdgcn_readlane(t, l);
+      w.cs = tl > 0 ? cdiv(tl, w.n) : 0;
+      if (!write_table) break;
+    }
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return w;
+}
+
 // Chunk classes of the many-request plan: chunks of about 2^(30 - key)
 // tiles, key 31 for an empty request.  The plan numbers chunks class by
 // class, longest first (and request by request inside a class), so the
@@ -671,6 +745,8 @@ stripe_attn_kernel(Params p) {
         if (tot > p.slots) flag_range(p.status);
       }
     }
+  } else if (table != nullptr && p.forced_splits == 0 && p.target_chunks > Bv && Bv <= 64 * kSmallPerLane) {
+    wi = find_work_small(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0, table);
   } else {
     wi = find_work(p, chunk, p.table != nullptr && chunk == 0 && mg == 0 && wave == 0, table);
   }

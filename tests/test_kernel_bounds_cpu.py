@@ -327,6 +327,75 @@ def test_block_find_is_the_class_order():
     assert any(x != order[c] for c, x in enumerate(bad))
 
 
+SMALL_PER_LANE = 4          # requests per lane of the register lookup
+
+
+def register_find(tiles, target, c, plant=None):
+    """The one-round lookup from registers (fewer requests than workgroups,
+    at most 64 x SMALL_PER_LANE of them): lane l of the wave holds requests
+    l, l + 64, ...; the chunk length is found by the same bisection over wave
+    sums, then each block of 64 requests is scanned with the previous
+    blocks' total carried in, and the first lane whose range holds c wins.
+    Returns (b, k, n, cs) or None past the last chunk."""
+    B = len(tiles)
+    lanes = [[tiles[64 * k + l] if 64 * k + l < B else None for k in range(SMALL_PER_LANE)] for l in range(64)]
+    total = sum(t for lane in lanes for t in lane if t is not None)
+
+    def chunks_for(L):
+        return sum(max(cdiv(t, L), 1) for lane in lanes for t in lane if t is not None)
+
+    C = max(cdiv(total, target), 1)
+    if chunks_for(C) > target:
+        lo, hi = C + 1, max(cdiv(total, target - B), 1)
+        while lo < hi:
+            mid = lo + (hi - lo) // 2
+            if chunks_for(mid) <= target:
+                hi = mid
+            else:
+                lo = mid + 1
+        C = lo
+    carry = 0
+    for k in range(SMALL_PER_LANE):
+        if 64 * k >= B:
+            break
+        nb = [max(cdiv(lanes[l][k], C), 1) if lanes[l][k] is not None else 0 for l in range(64)]
+        incl = list(np.cumsum(nb) + carry)
+        for l in range(64):
+            excl = incl[l] - nb[l]
+            lo = excl + (1 if plant == "off_by_one" else 0)
+            if lanes[l][k] is not None and lo <= c < incl[l]:
+                t = lanes[l][k]
+                return (64 * k + l, c - excl, nb[l], cdiv(t, nb[l]) if t > 0 else 0)
+        carry = incl[63] if plant != "no_carry" else 0
+    return None
+
+
+def test_register_find_is_the_work_list():
+    """Over random one-round batches of 1 to 255 requests (empty, short and
+    long ones, every block count of the lanes' registers) the register lookup
+    finds for every chunk the request and chunk the work list numbers there,
+    and nothing past the end; a dropped carry between blocks and an off-by-one
+    in the range test are caught.  The kernel takes this path only below the
+    lanes' capacity, which is the constant mirrored here."""
+    k = kernel_constants()
+    assert k["kSmallPerLane"] == SMALL_PER_LANE
+    src = open(KERNEL_SRC).read()
+    assert "Bv <= 64 * kSmallPerLane" in src and "p.target_chunks > Bv" in src
+    rng = np.random.default_rng(23)
+    for trial in range(40):
+        B = int(rng.integers(1, 256)) if trial > 3 else [1, 64, 65, 255][trial]
+        tiles = [int(x) for x in np.rint(np.exp(rng.uniform(0, np.log(rng.choice([4, 400, 9000])), B)))]
+        tiles[: min(3, B)] = [0, 1, 0][: min(3, B)]
+        wl = work_list(tiles, 0, 256)
+        for c in range(len(wl)):
+            assert register_find(tiles, 256, c) == wl[c]
+        assert register_find(tiles, 256, len(wl)) is None
+    tiles = [int(x) for x in rng.integers(1, 50, 200)]
+    wl = work_list(tiles, 0, 256)
+    for plant in ("off_by_one", "no_carry"):
+        assert any(register_find(tiles, 256, c, plant=plant) != wl[c] for c in range(len(wl)))
+
+
 def chunk_table(tiles, forced, target, slots, mgroups=1, plant=None):
     """The chunk table the combine reads in the many-request plan: each
     request's first chunk, if it has a workgroup (chunk index < slots), writes
