@@ -444,3 +444,45 @@ def test_one_launch_many_requests_every_element(B, H_, N, P, smax, seed):
     assert int(s.status.item()) == 0
     for b in range(B):
         H.check_request(s, mo, ml, o, lse, b)
+
+
+ONE_ROUND = [
+    # B, H, N, P, max length, seed: fewer requests than workgroups per round and at most 256 of them,
+    # so every workgroup finds its chunk from registers; lanes hold requests l, l + 64, ..., so these
+    # batches fill one to four blocks of lanes, the last one partly
+    (65, 32, 4, 64, 4000, 11),     # a second block with one request
+    (130, 32, 8, 64, 3000, 12),    # three blocks
+    (255, 16, 4, 16, 600, 13),     # four blocks, one request short of the round
+    (100, 128, 8, 64, 2000, 14),   # two row groups: 128 workgroups per round, two blocks
+]
+
+
+@pytest.mark.parametrize("B,H_,N,P,smax,seed", ONE_ROUND)
+def test_one_round_lookup_blocks_every_element(B, H_, N, P, smax, seed):
+    rng = np.random.default_rng(seed)
+    lens = np.exp(rng.uniform(0, np.log(smax), B)).astype(np.int64).clip(1, smax)
+    lens[:5] = [1, 2, 3, 4, 5]
+    lens[-1] = smax                                      # the longest request last: its chunks end the list
+    w, lens = custom(B, H_, 1, N, P, lens.tolist(), "2")
+    print(f"one-round lookup B={B} H={H_} N={N} lens[:8]={lens[:8].tolist()}", flush=True)
+    s = H.make_setup(w, 1, lens=lens)
+    check_all(s)
+
+
+def test_one_launch_one_round_lookup_every_element():
+    # 4 ranks x 48 requests = 192 request-stripes in one launch: the register lookup over the
+    # requests of all ranks (request v is request v mod B of rank slot v / B)
+    rng = np.random.default_rng(21)
+    lens = np.exp(rng.uniform(0, np.log(5000), 48)).astype(np.int64).clip(1, 5000)
+    lens[:3] = [1, 2, 3]
+    w, lens = custom(48, 32, 1, 4, 64, lens.tolist(), "e")
+    print("one launch, one-round lookup B=48 N=4", flush=True)
+    s = H.make_setup(w, 1, lens=lens)
+    N = s.lay.n_stripes
+    mo, ml = dcp.dcp_stripe_attn_multi(s.lay, list(range(N)), s.q, s.sp.pools, s.sp.tables, s.sp.seq_len,
+                                       workloads.SCALE, s.base_flag, status=s.status)
+    o, lse = dcp.dcp_lse_merge(mo, ml, s.base_flag)
+    torch.cuda.synchronize()
+    assert int(s.status.item()) == 0
+    for b in range(w.B):
+        H.check_request(s, mo, ml, o, lse, b)
