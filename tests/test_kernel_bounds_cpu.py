@@ -592,3 +592,28 @@ def test_plan_matches_library_workspace():
         part = slots * q_len * H_ * (512 * 2 + 4)       # bf16 o and float32 lse per chunk partial row
         want = 0 if forced == 1 else cdiv(part, 256) * 256 + 2 * B * 4
         assert n.value == want
+
+
+def part_slot(c, slots, group=CHUNK_GROUP):
+    """Workspace slot of chunk c's partial: chunk c mod group of every group of
+    consecutive chunks goes to region c mod group, at c / group within it."""
+    return (c % group) * (slots // group) + c // group
+
+
+def test_partial_slots_are_a_bijection_inside_the_workspace():
+    """The kernel writes chunk c's partial to slot part_slot(c) and the
+    combine reads a request's chunks c0..c0+n-1 through the same map: for
+    every slot count the plan can make (a multiple of 8 x kChunkGroup) the map
+    is a permutation of the slots, so no two chunks share a slot and no read
+    leaves the workspace; the uniform 4-chunk plan lands on the unmerged
+    parts' layout (part k of request b at k x B + b).  A map that drops the
+    region offset is caught."""
+    src = open(KERNEL_SRC).read()
+    assert "return (c % kChunkGroup) * (p.slots / kChunkGroup) + c / kChunkGroup;" in src
+    for slots in range(8 * CHUNK_GROUP, 8 * CHUNK_GROUP * 40, 8 * CHUNK_GROUP):
+        m = [part_slot(c, slots) for c in range(slots)]
+        assert sorted(m) == list(range(slots))
+    B = 64
+    assert all(part_slot(4 * b + k, 4 * B) == k * B + b for b in range(B) for k in range(4))
+    bad = [(c % CHUNK_GROUP) + c // CHUNK_GROUP for c in range(256)]
+    assert sorted(bad) != list(range(256))
